@@ -1,0 +1,139 @@
+/*
+ * libsigattn — bidirectional sigmoid attention on padded variable-length
+ * batches, for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  For every sequence b and head h, on the valid rows
+ * 0..n_b-1 (right padding):
+ *
+ *     X = Q K^T / sqrt(d) + b_b          scores, n_b x n_b
+ *     P = sigma(X),  sigma(x) = 1/(1 + e^-x)   elementwise, no row normalisation
+ *     O = P V
+ *
+ * ("Better Models, Faster Training: Sigmoid Attention for single-cell
+ * Foundation Models", technical summary §2A: the SigmoidAttn formula and the
+ * bias b = -log(n).)  There is no causal mask: the paper's models are
+ * bidirectional (its abstract).  The backward follows from the diagonal
+ * Jacobian of §2B: with dP = dO V^T and dX = dP * P * (1 - P),
+ *
+ *     dQ = dX K / sqrt(d),   dK = dX^T Q / sqrt(d),   dV = P^T dO.
+ *
+ * As in §2C of the same summary, the forward is one fused pass and the
+ * backward is split in two calls — one for dQ, one for dK and dV — so that no
+ * output row has more than one writer and no atomics are needed; P is
+ * recomputed, never stored.  Tiles that lie entirely in padding (query side or
+ * key side) are never computed.
+ *
+ * Readings taken where the pages are silent: n in -log(n) is the sequence's
+ * own valid length (other conventions selectable through bias_mode); log is
+ * the natural log; d is the head dimension; padded output rows are written as
+ * zero; a sequence with n_b = 0 produces all-zero outputs.
+ *
+ * Tensors.  Q, K, V, dO, O, dQ, dK, dV are device pointers to contiguous
+ * bf16 arrays of shape [B, H, Lmax, d] (row-major: d fastest), 16-byte
+ * aligned.  The caller owns every buffer; the library allocates no device or
+ * pinned memory and keeps no state between calls.  Rows n_b..Lmax-1 of the
+ * inputs may hold any bit pattern (including NaN/Inf): they are never read.
+ *
+ * Streams and errors.  Every call validates all arguments on the host before
+ * it enqueues anything, so a call that returns an error has no side effect.
+ * On success the work is enqueued on args->stream (NULL: the default stream)
+ * and the call returns; results are valid once the stream has reached that
+ * point.  The dQ call and the dK/dV call are independent of each other and may
+ * run on different streams.  Every output is fully overwritten.  The library
+ * never prints and never aborts.
+ */
+#ifndef SIGATTN_H
+#define SIGATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sigattn_status {
+  SIGATTN_OK = 0,
+  SIGATTN_ERR_NULL = 1,      /* args, a tensor pointer or seqlens is NULL               */
+  SIGATTN_ERR_SHAPE = 2,     /* B, H or Lmax < 1, d not 64 or 128, or sizes overflow    */
+  SIGATTN_ERR_SEQLEN = 3,    /* some seqlens[b] outside [0, Lmax]                       */
+  SIGATTN_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned                 */
+  SIGATTN_ERR_ALIAS = 5,     /* an output overlaps an input or another output           */
+  SIGATTN_ERR_BIAS = 6,      /* unknown bias_mode, non-finite bias_arg, or bias_arg <= 0
+                                with SIGATTN_BIAS_NEG_LOG_N                             */
+  SIGATTN_ERR_PRECISION = 7, /* unknown precision                                       */
+  SIGATTN_ERR_HIP = 8,       /* the HIP runtime rejected a kernel launch                */
+  SIGATTN_ERR_PASS = 9       /* unknown pass id (sigattn_plan_stats only)               */
+} sigattn_status;
+
+/* The bias b_b of the SigmoidAttn formula (summary §2A, b = -log(n)). */
+typedef enum sigattn_bias_mode {
+  SIGATTN_BIAS_NEG_LOG_SEQLEN = 0, /* b_b = -ln(n_b), n_b = valid length (default)  */
+  SIGATTN_BIAS_NEG_LOG_N = 1,      /* b = -ln(bias_arg), a fixed n (e.g. Lmax)      */
+  SIGATTN_BIAS_CONST = 2           /* b = bias_arg                                  */
+} sigattn_bias_mode;
+
+/* How P (forward, dV) and dX (dQ, dK) enter the second bf16 matrix product. */
+typedef enum sigattn_precision {
+  SIGATTN_PREC_FAST = 0,  /* rounded once to bf16 (round-to-nearest-even)          */
+  SIGATTN_PREC_SPLIT = 1  /* as a pair hi = bf16(x), lo = bf16(x - hi): two products,
+                             ~16 significant bits; needed when scores saturate
+                             the sigmoid (|x| >> 10) and many small weights sum   */
+} sigattn_precision;
+
+/* Which pass sigattn_plan_stats describes. */
+typedef enum sigattn_pass {
+  SIGATTN_PASS_FWD = 0,
+  SIGATTN_PASS_BWD_DQ = 1,
+  SIGATTN_PASS_BWD_DKDV = 2
+} sigattn_pass;
+
+typedef struct sigattn_args {
+  int32_t B, H, Lmax, d;    /* batch, heads, padded length, head dim (64 or 128)    */
+  const int32_t *seqlens;   /* HOST pointer to B valid lengths, 0 <= n_b <= Lmax;
+                               read during the call only                            */
+  int32_t bias_mode;        /* sigattn_bias_mode                                    */
+  float bias_arg;           /* see sigattn_bias_mode; ignored for mode 0            */
+  int32_t precision;        /* sigattn_precision                                    */
+  void *stream;             /* hipStream_t to enqueue on; NULL = default stream     */
+} sigattn_args;
+
+/* Forward: O = sigma(Q K^T / sqrt(d) + b) V on valid rows; padded rows of O = 0.
+ * One fused kernel per launch chunk (summary §2C: fused forward). */
+sigattn_status sigattn_fwd(const sigattn_args *args, const void *q, const void *k,
+                           const void *v, void *o);
+
+/* Backward, query side: dQ = (dO V^T * P * (1 - P)) K / sqrt(d); padded rows
+ * of dQ = 0; padded rows of dO are ignored.  P is recomputed (§2B diagonal
+ * Jacobian, §2C backward split into a dQ kernel and a dK/dV kernel). */
+sigattn_status sigattn_bwd_dq(const sigattn_args *args, const void *q, const void *k,
+                              const void *v, const void *dout, void *dq);
+
+/* Backward, key side: dV = P^T dO and dK = (dO V^T * P * (1 - P))^T Q / sqrt(d);
+ * padded rows of dK and dV = 0.  Each output row has a single writer: no
+ * atomics (§2C). */
+sigattn_status sigattn_bwd_dkdv(const sigattn_args *args, const void *q, const void *k,
+                                const void *v, const void *dout, void *dk, void *dv);
+
+/* Static description of a status code; never NULL. */
+const char *sigattn_status_str(sigattn_status status);
+
+/* Host-only description of the tile schedule a call would run, without
+ * touching the GPU.  For pass p it reports the work items (one output tile
+ * each), the (outer tile, inner tile) pairs those items visit — fully padded
+ * tiles are not counted because they are never computed — and the number of
+ * kernel launches.  Any of the output pointers may be NULL.  Validates
+ * args (shape, seqlens, bias, precision) as the compute calls do. */
+sigattn_status sigattn_plan_stats(const sigattn_args *args, int32_t pass, int64_t *work_items,
+                                  int64_t *tile_pairs, int32_t *launches);
+
+/* Rows per output tile and per inner tile for pass p and head dim d
+ * (written to *outer_rows, *inner_rows); SIGATTN_ERR_PASS / _SHAPE on a bad
+ * pass or d. */
+sigattn_status sigattn_tile_shape(int32_t pass, int32_t d, int32_t *outer_rows,
+                                  int32_t *inner_rows);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SIGATTN_H */

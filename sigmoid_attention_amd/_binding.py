@@ -1,0 +1,188 @@
+"""ctypes binding of libsigattn (include/sigattn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  PyTorch provides device memory and the current
+stream.  There is no fallback: if the library is missing, loading fails with
+an error that says how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsigattn.so")
+_lib = None
+
+BIAS_MODES = {"seqlen": 0, "fixed_n": 1, "const": 2}
+PRECISIONS = {"fast": 0, "split": 1}
+PASSES = {"fwd": 0, "bwd_dq": 1, "bwd_dkdv": 2}
+
+STATUS_NAMES = {
+    0: "SIGATTN_OK", 1: "SIGATTN_ERR_NULL", 2: "SIGATTN_ERR_SHAPE", 3: "SIGATTN_ERR_SEQLEN",
+    4: "SIGATTN_ERR_ALIGN", 5: "SIGATTN_ERR_ALIAS", 6: "SIGATTN_ERR_BIAS", 7: "SIGATTN_ERR_PRECISION",
+    8: "SIGATTN_ERR_HIP", 9: "SIGATTN_ERR_PASS",
+}
+
+EXPORTED = ("sigattn_fwd", "sigattn_bwd_dq", "sigattn_bwd_dkdv", "sigattn_status_str",
+            "sigattn_plan_stats", "sigattn_tile_shape")
+
+
+class SigattnArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Lmax", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("seqlens", ctypes.POINTER(ctypes.c_int32)),
+        ("bias_mode", ctypes.c_int32), ("bias_arg", ctypes.c_float),
+        ("precision", ctypes.c_int32),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+class SigattnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS_NAMES.get(code, code)} ({status_str(code)})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libsigattn.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python -m sigmoid_attention_amd.build` "
+            "(or __graft_entry__.build()) first. There is no fallback implementation.")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, ap = ctypes.c_void_p, ctypes.POINTER(SigattnArgs)
+    lib.sigattn_fwd.argtypes = [ap, vp, vp, vp, vp]
+    lib.sigattn_bwd_dq.argtypes = [ap, vp, vp, vp, vp, vp]
+    lib.sigattn_bwd_dkdv.argtypes = [ap, vp, vp, vp, vp, vp, vp]
+    for f in (lib.sigattn_fwd, lib.sigattn_bwd_dq, lib.sigattn_bwd_dkdv):
+        f.restype = ctypes.c_int
+    lib.sigattn_status_str.argtypes = [ctypes.c_int]
+    lib.sigattn_status_str.restype = ctypes.c_char_p
+    lib.sigattn_plan_stats.argtypes = [ap, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]
+    lib.sigattn_plan_stats.restype = ctypes.c_int
+    lib.sigattn_tile_shape.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.POINTER(ctypes.c_int32)]
+    lib.sigattn_tile_shape.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_str(code: int) -> str:
+    return load().sigattn_status_str(int(code)).decode()
+
+
+def make_args(B, H, Lmax, d, seqlens, bias_mode="seqlen", bias_arg=0.0, precision="fast", stream=0):
+    """Build a sigattn_args struct.  Returns (args, keepalive) — keep the second
+    object alive for as long as the struct is used (it owns the lengths)."""
+    lens = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    a = SigattnArgs()
+    a.B, a.H, a.Lmax, a.d = int(B), int(H), int(Lmax), int(d)
+    a.seqlens = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if lens.size else None
+    a.bias_mode = BIAS_MODES[bias_mode] if isinstance(bias_mode, str) else int(bias_mode)
+    a.bias_arg = float(bias_arg)
+    a.precision = PRECISIONS[precision] if isinstance(precision, str) else int(precision)
+    a.stream = int(stream) if stream else None
+    return a, lens
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise SigattnError(code, where)
+
+
+def _tensor_args(ts, seqlens, bias_mode, bias_arg, precision, stream):
+    import torch
+
+    q = ts[0]
+    for t in ts:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("expected torch tensors")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"expected bfloat16 tensors, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, Lmax, d]")
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError("all tensors must share shape and device")
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, Lmax, d] tensors")
+    B, H, L, d = q.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    return make_args(B, H, L, d, seqlens, bias_mode, bias_arg, precision, stream)
+
+
+def fwd(q, k, v, seqlens: Sequence[int], o=None, bias_mode="seqlen", bias_arg=0.0, precision="fast",
+        stream: Optional[int] = None):
+    """O = sigma(Q K^T / sqrt(d) + b) V, padded rows of O zero.  Enqueued on the
+    current stream (or `stream`); returns O."""
+    import torch
+
+    if o is None:
+        o = torch.empty_like(q)
+    args, keep = _tensor_args((q, k, v, o), seqlens, bias_mode, bias_arg, precision, stream)
+    with torch.cuda.device(q.device):
+        _check(load().sigattn_fwd(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()),
+               "sigattn_fwd")
+    del keep
+    return o
+
+
+def bwd_dq(q, k, v, dout, seqlens, dq=None, bias_mode="seqlen", bias_arg=0.0, precision="fast", stream=None):
+    """dQ of sum(O * dO); padded rows zero.  Returns dQ."""
+    import torch
+
+    if dq is None:
+        dq = torch.empty_like(q)
+    args, keep = _tensor_args((q, k, v, dout, dq), seqlens, bias_mode, bias_arg, precision, stream)
+    with torch.cuda.device(q.device):
+        _check(load().sigattn_bwd_dq(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     dout.data_ptr(), dq.data_ptr()), "sigattn_bwd_dq")
+    del keep
+    return dq
+
+
+def bwd_dkdv(q, k, v, dout, seqlens, dk=None, dv=None, bias_mode="seqlen", bias_arg=0.0, precision="fast",
+             stream=None):
+    """dK and dV of sum(O * dO); padded rows zero.  Returns (dK, dV)."""
+    import torch
+
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    args, keep = _tensor_args((q, k, v, dout, dk, dv), seqlens, bias_mode, bias_arg, precision, stream)
+    with torch.cuda.device(q.device):
+        _check(load().sigattn_bwd_dkdv(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                       dout.data_ptr(), dk.data_ptr(), dv.data_ptr()), "sigattn_bwd_dkdv")
+    del keep
+    return dk, dv
+
+
+def plan_stats(B, H, Lmax, d, seqlens, pass_="fwd", bias_mode="seqlen", bias_arg=0.0, precision="fast"):
+    """Host-only: (work_items, tile_pairs, launches) the pass would run."""
+    args, keep = make_args(B, H, Lmax, d, seqlens, bias_mode, bias_arg, precision)
+    items, pairs, launches = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    _check(load().sigattn_plan_stats(ctypes.byref(args), PASSES[pass_], ctypes.byref(items), ctypes.byref(pairs),
+                                     ctypes.byref(launches)), "sigattn_plan_stats")
+    del keep
+    return items.value, pairs.value, launches.value
+
+
+def tile_shape(pass_: str, d: int):
+    """(outer_rows, inner_rows) of the tiles the pass uses at head dim d."""
+    o, i = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().sigattn_tile_shape(PASSES[pass_], int(d), ctypes.byref(o), ctypes.byref(i)), "sigattn_tile_shape")
+    return o.value, i.value

@@ -1,0 +1,143 @@
+// Host-side tile schedule: which output tiles exist, how they are grouped into
+// pieces, and which XCD list each piece goes to.  Pure C++; no HIP calls.
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+namespace sigattn {
+
+namespace {
+
+struct Piece {
+  int32_t b, h0, nh, t0, nt;
+  int32_t n;
+  int64_t item_cost;   // inner tiles per item
+  int64_t cost() const { return (int64_t)nh * nt * item_cost; }
+};
+
+int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+double bias_value(int32_t n, int32_t mode, float arg) {
+  // Summary §2A: b = -log(n).  Mode 0 reads n as the sequence's valid length.
+  if (mode == 0) return -std::log((double)n);
+  if (mode == 1) return -std::log((double)arg);
+  return (double)arg;
+}
+
+std::vector<Launch> build_plan(const PlanInput& in, PlanStats* stats) {
+  const double log2e = 1.4426950408889634;
+  std::vector<Piece> pieces;
+  int64_t total_cost = 0, total_items = 0;
+  for (int32_t b = 0; b < in.B; ++b) {
+    const int32_t n = in.seqlens[b];
+    if (n <= 0) continue;
+    const int64_t items = ceil_div(n, in.outer_rows);
+    const int64_t inner = ceil_div(n, in.inner_rows);
+    total_items += items * in.H;
+    total_cost += items * inner * in.H;
+  }
+  if (stats) {
+    stats->items = total_items;
+    stats->pairs = total_cost;
+  }
+  if (total_items == 0) return {};
+
+  // Cut work so that no piece is larger than about 1/64 of the total (1/8 of
+  // one XCD's share): longest-first assignment then evens out the 8 XCD lists
+  // to within a few percent on ragged batches.
+  const int64_t target = std::max<int64_t>(1, (total_cost + 8 * kXcds - 1) / (8 * kXcds));
+  for (int32_t b = 0; b < in.B; ++b) {
+    const int32_t n = in.seqlens[b];
+    if (n <= 0) continue;
+    const int32_t items = ceil_div(n, in.outer_rows);
+    const int64_t inner = ceil_div(n, in.inner_rows);
+    const int64_t head_cost = items * inner;
+    if (head_cost * in.H <= target) {
+      pieces.push_back({b, 0, in.H, 0, items, n, inner});
+    } else if (head_cost <= target) {
+      const int32_t k = (int32_t)std::max<int64_t>(1, target / head_cost);
+      for (int32_t h = 0; h < in.H; h += k)
+        pieces.push_back({b, h, std::min(k, in.H - h), 0, items, n, inner});
+    } else {
+      const int32_t m = (int32_t)std::max<int64_t>(1, target / inner);
+      for (int32_t h = 0; h < in.H; ++h)
+        for (int32_t t = 0; t < items; t += m)
+          pieces.push_back({b, h, 1, t, std::min(m, items - t), n, inner});
+    }
+  }
+  // Longest first (ties: lower sequence, head, tile first, so plans are deterministic).
+  std::stable_sort(pieces.begin(), pieces.end(), [](const Piece& a, const Piece& b) {
+    return a.cost() > b.cost();
+  });
+
+  std::vector<Launch> launches;
+  for (size_t p0 = 0; p0 < pieces.size(); p0 += kMaxPieces) {
+    const size_t p1 = std::min(pieces.size(), p0 + kMaxPieces);
+    // Longest-processing-time-first over the 8 XCD lists.
+    std::vector<std::vector<Piece>> lists(kXcds);
+    int64_t load[kXcds] = {0};
+    for (size_t p = p0; p < p1; ++p) {
+      int best = 0;
+      for (int x = 1; x < kXcds; ++x)
+        if (load[x] < load[best]) best = x;
+      lists[best].push_back(pieces[p]);
+      load[best] += pieces[p].cost();
+    }
+    Launch L;
+    std::memset(&L.sched, 0, sizeof(L.sched));
+    L.sched.H = in.H;
+    L.sched.Lmax = in.Lmax;
+    L.sched.c1 = (float)(-log2e / std::sqrt((double)in.d));
+    L.sched.out_scale = (float)(1.0 / std::sqrt((double)in.d));
+    int32_t g = 0, max_items = 0;
+    for (int x = 0; x < kXcds; ++x) {
+      // Within a list, items with the most inner tiles start first.
+      std::stable_sort(lists[x].begin(), lists[x].end(), [](const Piece& a, const Piece& b) {
+        return a.item_cost > b.item_cost;
+      });
+      L.sched.xcd_begin[x] = g;
+      int32_t item = 0;
+      for (const Piece& pc : lists[x]) {
+        L.sched.bh0[g] = pc.b * in.H + pc.h0;
+        L.sched.n[g] = pc.n;
+        L.sched.item0[g] = item;
+        L.sched.t0[g] = pc.t0;
+        L.sched.nt[g] = pc.nt;
+        L.sched.c2[g] = (float)(-bias_value(pc.n, in.bias_mode, in.bias_arg) * log2e);
+        item += pc.nh * pc.nt;
+        ++g;
+      }
+      L.sched.xcd_items[x] = item;
+      max_items = std::max(max_items, item);
+    }
+    L.sched.xcd_begin[kXcds] = g;
+    L.blocks = kXcds * max_items;
+    launches.push_back(L);
+  }
+  return launches;
+}
+
+std::vector<ZeroSched> build_zero_plan(int32_t B, int32_t H, int32_t Lmax, const int32_t* seqlens) {
+  std::vector<ZeroSched> out;
+  for (int32_t b0 = 0; b0 < B; b0 += kZeroMaxSeqs) {
+    ZeroSched z;
+    std::memset(&z, 0, sizeof(z));
+    z.H = H;
+    z.Lmax = Lmax;
+    z.b0 = b0;
+    z.nseq = std::min(kZeroMaxSeqs, B - b0);
+    bool any = false;
+    for (int32_t i = 0; i < z.nseq; ++i) {
+      z.n[i] = seqlens[b0 + i];
+      any |= z.n[i] < Lmax;
+    }
+    if (any) out.push_back(z);
+  }
+  return out;
+}
+
+}  // namespace sigattn

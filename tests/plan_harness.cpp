@@ -1,0 +1,83 @@
+// Host-only check of the tile schedule: builds the plan for the lengths given
+// on the command line and walks every workgroup of every launch through the
+// same decode_item() the kernels use.  Verifies that each non-padded output
+// tile is visited exactly once and that no fully padded tile appears; prints
+// a one-line JSON summary.
+//
+// usage: plan_harness B H Lmax d outer_rows inner_rows n_0 ... n_{B-1}
+#include <cstdio>
+#include <cstdlib>
+#include <map>
+#include <utility>
+#include <vector>
+
+#include "plan.h"
+
+int main(int argc, char** argv) {
+  if (argc < 7) return 2;
+  sigattn::PlanInput in;
+  in.B = atoi(argv[1]);
+  in.H = atoi(argv[2]);
+  in.Lmax = atoi(argv[3]);
+  in.d = atoi(argv[4]);
+  in.outer_rows = atoi(argv[5]);
+  in.inner_rows = atoi(argv[6]);
+  in.bias_mode = 0;
+  in.bias_arg = 0.0f;
+  if (argc != 7 + in.B) return 2;
+  std::vector<int32_t> lens(in.B);
+  for (int b = 0; b < in.B; ++b) lens[b] = atoi(argv[7 + b]);
+  in.seqlens = lens.data();
+
+  sigattn::PlanStats st;
+  const std::vector<sigattn::Launch> plan = sigattn::build_plan(in, &st);
+  std::map<std::pair<int, int>, int> seen;
+  long long blocks = 0, idle = 0, bad = 0, pairs = 0;
+  double worst_imbalance = 0.0;
+  for (const auto& L : plan) {
+    if (L.blocks % sigattn::kXcds) ++bad;
+    long long xload[sigattn::kXcds] = {0};
+    for (int32_t i = 0; i < L.blocks; ++i) {
+      sigattn::Item it;
+      ++blocks;
+      if (!sigattn::decode_item(L.sched, i % sigattn::kXcds, i / sigattn::kXcds, it)) {
+        ++idle;
+        continue;
+      }
+      const int b = it.bh / in.H;
+      const int ntiles = (lens[b] + in.outer_rows - 1) / in.outer_rows;
+      if (b < 0 || b >= in.B || it.n != lens[b] || it.tile < 0 || it.tile >= ntiles) ++bad;
+      seen[{it.bh, it.tile}]++;
+      const long long inner = (lens[b] + in.inner_rows - 1) / in.inner_rows;
+      pairs += inner;
+      xload[i % sigattn::kXcds] += inner;
+    }
+    long long mx = 0, sum = 0;
+    for (int x = 0; x < sigattn::kXcds; ++x) {
+      mx = xload[x] > mx ? xload[x] : mx;
+      sum += xload[x];
+    }
+    if (sum > 0) {
+      const double imb = (double)mx * sigattn::kXcds / (double)sum - 1.0;
+      worst_imbalance = imb > worst_imbalance ? imb : worst_imbalance;
+    }
+  }
+  long long expect = 0, dup = 0, missing = 0;
+  for (int b = 0; b < in.B; ++b) {
+    const int ntiles = (lens[b] + in.outer_rows - 1) / in.outer_rows;
+    for (int h = 0; h < in.H; ++h)
+      for (int t = 0; t < ntiles; ++t) {
+        ++expect;
+        auto itr = seen.find({b * in.H + h, t});
+        if (itr == seen.end()) ++missing;
+        else if (itr->second != 1) ++dup;
+      }
+  }
+  const long long extra = (long long)seen.size() - (expect - missing);
+  printf("{\"launches\": %zu, \"blocks\": %lld, \"idle\": %lld, \"items\": %lld, \"expect\": %lld, "
+         "\"missing\": %lld, \"dup\": %lld, \"extra\": %lld, \"bad\": %lld, \"pairs\": %lld, "
+         "\"stats_items\": %lld, \"stats_pairs\": %lld, \"xcd_imbalance\": %.4f}\n",
+         plan.size(), blocks, idle, blocks - idle, expect, missing, dup, extra, bad, pairs, (long long)st.items,
+         (long long)st.pairs, worst_imbalance);
+  return 0;
+}

@@ -1,0 +1,189 @@
+"""C-ABI of libsigattn on the CPU: the library loads, exports every function
+include/sigattn.h declares, and rejects bad arguments before touching the GPU.
+
+No call here reaches a kernel launch: every argument set is invalid in at
+least one way, and the library validates everything before it enqueues.
+Pointers are fake, 16-byte aligned addresses far apart; they are never
+dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sigmoid_attention_amd as sa
+from sigmoid_attention_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sigattn.h")
+
+OK, NULL, SHAPE, SEQLEN, ALIGN, ALIAS, BIAS, PREC, HIP, PASS = range(10)
+BIG = 1 << 40  # spacing between fake buffers: larger than any test tensor
+P = [0x100000000000 + i * BIG for i in range(8)]  # fake device addresses
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(sigattn_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = sa.load()
+    names = declared_functions()
+    assert set(names) == set(_binding.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(10):
+        s = sa.status_str(code)
+        assert isinstance(s, str) and s
+    assert sa.status_str(0) == "ok"
+    assert sa.status_str(1234) == "unknown status"
+
+
+def fwd(args, q=P[0], k=P[1], v=P[2], o=P[3]):
+    return sa.load().sigattn_fwd(ctypes.byref(args) if args is not None else None, q, k, v, o)
+
+
+def dq(args, q=P[0], k=P[1], v=P[2], g=P[3], d=P[4]):
+    return sa.load().sigattn_bwd_dq(ctypes.byref(args), q, k, v, g, d)
+
+
+def dkdv(args, q=P[0], k=P[1], v=P[2], g=P[3], dk=P[4], dv=P[5]):
+    return sa.load().sigattn_bwd_dkdv(ctypes.byref(args), q, k, v, g, dk, dv)
+
+
+def args(B=2, H=2, L=128, d=64, lens=(128, 77), **kw):
+    return sa.make_args(B, H, L, d, lens, **kw)
+
+
+def test_null_pointers():
+    assert fwd(None) == NULL
+    a, keep = args()
+    assert fwd(a, q=None) == NULL
+    assert fwd(a, o=None) == NULL
+    assert dq(a, g=None) == NULL
+    assert dkdv(a, dv=None) == NULL
+    a.seqlens = None
+    assert fwd(a) == NULL
+
+
+@pytest.mark.parametrize("shape", [(0, 2, 128, 64), (2, 0, 128, 64), (2, 2, 0, 64), (2, 2, 128, 32),
+                                   (2, 2, 128, 96), (2, 2, 128, 256), (-1, 2, 128, 64)])
+def test_bad_shapes(shape):
+    B, H, L, d = shape
+    a, keep = sa.make_args(B, H, L, d, [1] * max(B, 1))
+    for f in (fwd, dq, dkdv):
+        assert f(a) == SHAPE
+
+
+def test_size_overflow_rejected():
+    a, keep = sa.make_args(1 << 20, 1 << 20, 1 << 20, 128, [0] * 1)  # 2^67 elements
+    a.B = 1 << 20
+    # seqlens would be read after the shape check; the shape check fails first
+    assert fwd(a) == SHAPE
+
+
+@pytest.mark.parametrize("lens", [(129, 77), (-1, 77), (128, 1 << 30)])
+def test_bad_lengths(lens):
+    a, keep = args(lens=lens)
+    for f in (fwd, dq, dkdv):
+        assert f(a) == SEQLEN
+
+
+def test_misaligned_pointers():
+    a, keep = args()
+    assert fwd(a, q=P[0] + 8) == ALIGN
+    assert fwd(a, o=P[3] + 2) == ALIGN
+    assert dq(a, d=P[4] + 4) == ALIGN
+    assert dkdv(a, dk=P[4] + 8) == ALIGN
+
+
+def test_aliasing_outputs():
+    a, keep = args()
+    nbytes = 2 * 2 * 128 * 64 * 2
+    assert fwd(a, o=P[0]) == ALIAS                    # O is Q
+    assert fwd(a, o=P[1] + nbytes - 16) == ALIAS      # O overlaps the tail of K
+    assert dq(a, d=P[3]) == ALIAS                     # dQ is dO
+    assert dkdv(a, dk=P[4], dv=P[4] + 16) == ALIAS    # dK overlaps dV
+    assert dkdv(a, dv=P[2]) == ALIAS                  # dV is V
+
+
+def test_inputs_may_alias_each_other_but_output_checks_still_run():
+    a, keep = args()
+    # q == k == v is legal; the call still fails on the aliased output first.
+    assert fwd(a, q=P[0], k=P[0], v=P[0], o=P[0]) == ALIAS
+
+
+@pytest.mark.parametrize("mode,arg", [(3, 0.0), (-1, 0.0), (1, 0.0), (1, -5.0), (1, float("nan")),
+                                      (2, float("inf")), (2, float("nan"))])
+def test_bad_bias(mode, arg):
+    a, keep = args(bias_mode=mode, bias_arg=arg)
+    for f in (fwd, dq, dkdv):
+        assert f(a) == BIAS
+
+
+@pytest.mark.parametrize("prec", [2, -1, 99])
+def test_bad_precision(prec):
+    a, keep = args(precision=prec)
+    for f in (fwd, dq, dkdv):
+        assert f(a) == PREC
+
+
+def test_validation_order_no_side_effects():
+    """A bad length is reported even when pointers are also bad: all checks run
+    on the host before anything is enqueued."""
+    a, keep = args(lens=(500, 1))
+    assert fwd(a, q=P[0] + 1) == SEQLEN
+
+
+def expected_counts(H, lens, outer, inner):
+    lens = np.asarray(lens, dtype=np.int64)
+    return int((H * -(-lens // outer)).sum()), int((H * -(-lens // outer) * -(-lens // inner)).sum())
+
+
+@pytest.mark.parametrize("pass_", ["fwd", "bwd_dq", "bwd_dkdv"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_plan_stats_closed_forms(pass_, d):
+    lens = [1124, 2023, 1379, 743, 0, 545, 1602, 2048]
+    outer, inner = sa.tile_shape(pass_, d)
+    items, pairs, launches = sa.plan_stats(8, 16, 2048, d, lens, pass_)
+    assert (items, pairs) == expected_counts(16, lens, outer, inner)
+    assert launches == 2  # one compute launch + one zero-fill launch (there is padding)
+    items, pairs, launches = sa.plan_stats(2, 3, 256, d, [0, 0], pass_)
+    assert (items, pairs, launches) == (0, 0, 1)  # nothing to compute, all rows zero-filled
+    items, pairs, launches = sa.plan_stats(2, 3, 256, d, [256, 256], pass_)
+    assert launches == 1  # no padding: no zero-fill launch
+
+
+def test_plan_stats_errors():
+    with pytest.raises(sa.SigattnError) as e:
+        sa.plan_stats(2, 2, 128, 64, [128, 77], "fwd", bias_mode=7)
+    assert e.value.code == BIAS
+    lib = sa.load()
+    a, keep = args()
+    assert lib.sigattn_plan_stats(ctypes.byref(a), 5, None, None, None) == PASS
+    assert lib.sigattn_tile_shape(0, 48, None, None) == SHAPE
+    assert lib.sigattn_tile_shape(7, 64, None, None) == PASS
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(_binding, "_LIB_PATH", "/nonexistent/libsigattn.so")
+    monkeypatch.setattr(_binding, "_lib", None)
+    with pytest.raises(ImportError, match="not built"):
+        _binding.load()
+
+
+def test_no_oracle_in_product_path():
+    """The library package never imports the oracle (test infrastructure)."""
+    pkg = os.path.join(ROOT, "sigmoid_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), f
+                assert "oracle/" not in src, f
