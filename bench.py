@@ -1,0 +1,310 @@
+"""Benchmark: valid-token TFLOPS of sigmoid attention (forward + backward) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--precision fast|split|auto]
+                    [--sweep] [--no-cpu-baseline] [--cpu-seconds S]
+
+A step is one pass of the whole path over one batch already resident in HBM:
+sigattn_fwd, then sigattn_bwd_dq, then sigattn_bwd_dkdv (one launch each).
+W untimed steps, then exactly K timed steps bracketed by device syncs; HIP
+events recorded on the launch stream around every call give the per-kernel
+durations.  FLOPs are algorithmic and count valid (query, key) pairs only:
+forward 4 n^2 d and backward 10 n^2 d per (sequence, head) — the FlashAttention
+convention; recomputation inside the backward kernels is not counted.
+
+Prints ONE JSON line.  With --sweep it also times the three padding-sweep
+workloads (0 / 25 / 50 % padding) and adds their TFLOPS and the time ratio
+against the covered-tile and valid-pair ratios under "padding_sweep".
+
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "valid-token TFLOPS fwd/bwd, sigmoid attn d=64 L≤8K padded; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published (no sparsity)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "sigmoid_attention_amd", "csrc", "kernels.hip")
+# Algorithmic FLOP per valid (query, key) pair and head dim, per kernel:
+# forward: S = QK^T and PV (4); dK/dV kernel: S, dP, dV, dK (8); dQ kernel: dQ (2)
+# (its S and dP recompute what the dK/dV kernel already counts).  Sum: 14 = 4 + 10.
+KERNEL_FLOP_UNITS = {"fwd": 4, "bwd_dq": 2, "bwd_dkdv": 8}
+
+
+def pair_flops(seqlens, H, d):
+    n = np.asarray(seqlens, dtype=np.float64)
+    return float(H * d * (n * n).sum())
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        h = hashlib.sha256(f.read())
+    for extra in ("device_common.h", "plan.h", "plan.cpp"):
+        with open(os.path.join(ROOT, "sigmoid_attention_amd", "csrc", extra), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, precision: str):
+    """HBM bytes per launch measured with rocprofv3 counters for this exact
+    kernel source, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    entry = rec.get("kernels", {}).get(f"{kernel}/{workload}/{precision}")
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def time_workload(name, precision, steps, warmup, seed=0):
+    import torch
+
+    import sigmoid_attention_amd as sa
+    import workloads
+
+    case = workloads.make(name, seed=seed)
+    w = case["workload"]
+    n = case["seqlens"]
+    dev = torch.device("cuda:0")
+    q, k, v, do = (case[t].to(dev) for t in ("q", "k", "v", "do"))
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    kw = dict(precision=precision)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        sa.fwd(q, k, v, n, o=o, **kw)
+        if ev is not None:
+            ev[1].record()
+        sa.bwd_dq(q, k, v, do, n, dq=dq, **kw)
+        if ev is not None:
+            ev[2].record()
+        sa.bwd_dkdv(q, k, v, do, n, dk=dk, dv=dv, **kw)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - t0
+    per = {"fwd": [], "bwd_dq": [], "bwd_dkdv": []}
+    for ev in events:
+        per["fwd"].append(ev[0].elapsed_time(ev[1]))
+        per["bwd_dq"].append(ev[1].elapsed_time(ev[2]))
+        per["bwd_dkdv"].append(ev[2].elapsed_time(ev[3]))
+    step_ms = events[0][0].elapsed_time(events[-1][3]) / steps
+    base = pair_flops(n, w.H, w.d)
+    avg = {kname: float(np.mean(v_)) for kname, v_ in per.items()}
+    med = {kname: float(np.median(v_)) for kname, v_ in per.items()}
+    res = {
+        "workload": w, "seqlens": n, "step_ms": step_ms, "host_step_ms": host_s * 1e3 / steps,
+        "kernel_avg_ms": avg, "kernel_median_ms": med, "kernel_min_ms": {k_: float(np.min(v_)) for k_, v_ in per.items()},
+        "pair_flops": base,
+        "fwd_flops": 4 * base, "bwd_flops": 10 * base,
+        "outputs": (o, dq, dk, dv), "case": case,
+    }
+    return res
+
+
+def tflops(flops, ms):
+    return flops / (ms * 1e-3) / 1e12
+
+
+def cpu_baseline(case, outputs, budget_s):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same
+    workload: whole heads, cycling through the sequences longest first, until
+    about budget_s seconds of work.  Returns the record and the worst parity
+    ratio of the GPU outputs on those heads."""
+    import oracle
+    from workloads import as_f64
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = os.cpu_count()
+    w = case["workload"]
+    n = case["seqlens"]
+    order = [int(b) for b in np.argsort(-np.asarray(n), kind="stable") if n[b] > 0]
+    done, flops, secs, worst = [], 0.0, 0.0, 0.0
+    i = 0
+    while secs < budget_s and order and i < len(order) * w.H:
+        b = order[i % len(order)]
+        h = (i // len(order)) % w.H
+        i += 1
+        args = [as_f64(case[t][b, h]) for t in ("q", "k", "v", "do")]
+        t0 = time.perf_counter()
+        ref = oracle.head(*args, int(n[b]))
+        secs += time.perf_counter() - t0
+        flops += 14.0 * w.d * float(n[b]) ** 2
+        done.append((b, h, int(n[b])))
+        for got, r in zip(outputs, ref):
+            g = as_f64(got[b, h])
+            worst = max(worst, float(np.max(np.abs(g - r) / (2e-2 * (1.0 + np.abs(r))))))
+    rec = {
+        "value": flops / secs / 1e12 if secs > 0 else None,
+        "unit": "TFLOPS",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"fp64 oracle forward+backward on {len(done)} of {w.B * w.H} heads of {w.name} "
+                  f"(longest sequences first; lengths {sorted({x[2] for x in done}, reverse=True)}), "
+                  f"{secs:.1f} s, same algorithmic FLOP convention",
+        "seconds": secs,
+    }
+    return rec, worst
+
+
+def covered_pairs(seqlens, H, outer, inner):
+    n = np.asarray(seqlens, dtype=np.int64)
+    return int((H * -(-n // outer) * -(-n // inner)).sum())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--precision", default="auto", choices=["auto", "fast", "split"])
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB, 5 times (HBM counter calibration)")
+    a = ap.parse_args()
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {a.gpus}). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sigmoid_attention_amd as sa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sa.load()  # fail loudly if the library is not built
+
+    if a.copy_calibration:
+        x = torch.empty(1 << 29, dtype=torch.int16, device="cuda:0").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_copy": x.numel() * 2,
+                          "bytes_written_per_copy": y.numel() * 2, "copies": 5}))
+        return
+
+    name = a.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    precision = a.precision if a.precision != "auto" else ("split" if w.scale_qkv > 1.0 else "fast")
+    r = time_workload(name, precision, a.steps, a.warmup)
+    n = r["seqlens"]
+    total = r["fwd_flops"] + r["bwd_flops"]
+    value = tflops(total, r["step_ms"])
+    fwd_tf = tflops(r["fwd_flops"], r["kernel_avg_ms"]["fwd"])
+    bwd_tf = tflops(r["bwd_flops"], r["kernel_avg_ms"]["bwd_dq"] + r["kernel_avg_ms"]["bwd_dkdv"])
+
+    dominant = max(r["kernel_avg_ms"], key=r["kernel_avg_ms"].get)
+    dom_flops = KERNEL_FLOP_UNITS[dominant] * r["pair_flops"]
+    achieved = tflops(dom_flops, r["kernel_avg_ms"][dominant])
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": load_traffic(dominant, name, precision),
+        "kernel": dominant, "flop_per_launch": dom_flops,
+        "avg_launch_ms": round(r["kernel_avg_ms"][dominant], 5),
+        "per_kernel": {
+            kname: {"avg_ms": round(r["kernel_avg_ms"][kname], 5), "median_ms": round(r["kernel_median_ms"][kname], 5),
+                     "min_ms": round(r["kernel_min_ms"][kname], 5),
+                     "algorithmic_tflops": round(tflops(KERNEL_FLOP_UNITS[kname] * r["pair_flops"],
+                                                        r["kernel_avg_ms"][kname]), 2)}
+            for kname in KERNEL_FLOP_UNITS},
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": name, "B": w.B, "H": w.H, "d": w.d, "Lmax": w.Lmax, "seqlens": [int(x) for x in n],
+            "precision": precision, "bias": "-ln(n_b)",
+            "valid_token_frac": round(float(np.sum(n)) / (w.B * w.Lmax), 4),
+            "valid_pair_frac": round(float(np.sum(np.asarray(n, np.float64) ** 2)) / (w.B * w.Lmax ** 2), 4),
+        },
+        "fwd_tflops": round(fwd_tf, 2),
+        "bwd_tflops": round(bwd_tf, 2),
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_pct_bf16_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
+        "bwd_pct_bf16_peak": round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2),
+        "host_ms_per_step": round(r["host_step_ms"], 5),
+        "roofline": roofline,
+    }
+
+    if a.sweep:
+        sweep = {}
+        base_ms = None
+        for sw in ("sweep_b16h16d64_l4096_pad00", "sweep_b16h16d64_l4096_pad25", "sweep_b16h16d64_l4096_pad50"):
+            rs = time_workload(sw, "fast", max(5, a.steps // 2), 2)
+            ws = rs["workload"]
+            fwd_ms = rs["kernel_avg_ms"]["fwd"]
+            step_ms = rs["step_ms"]
+            if base_ms is None:
+                base_ms = (fwd_ms, step_ms)
+            dense_pairs = covered_pairs([ws.Lmax] * ws.B, ws.H, 128, 64)
+            sweep[sw] = {
+                "seqlens": [int(x) for x in rs["seqlens"]],
+                "padding": round(1 - float(np.sum(rs["seqlens"])) / (ws.B * ws.Lmax), 4),
+                "fwd_tflops": round(tflops(rs["fwd_flops"], fwd_ms), 2),
+                "fwd_bwd_tflops": round(tflops(rs["fwd_flops"] + rs["bwd_flops"], step_ms), 2),
+                "fwd_time_ratio": round(fwd_ms / base_ms[0], 4),
+                "step_time_ratio": round(step_ms / base_ms[1], 4),
+                "covered_tile_ratio": round(covered_pairs(rs["seqlens"], ws.H, 128, 64) / dense_pairs, 4),
+                "valid_pair_ratio": round(float(np.sum(np.asarray(rs["seqlens"], np.float64) ** 2))
+                                          / (ws.B * ws.Lmax ** 2), 4),
+            }
+            del rs
+            torch.cuda.empty_cache()
+        out["padding_sweep"] = sweep
+
+    if not a.no_cpu_baseline:
+        rec, worst = cpu_baseline(r["case"], r["outputs"], a.cpu_seconds)
+        out["cpu_baseline"] = {k_: v_ for k_, v_ in rec.items() if k_ != "seconds"}
+        out["parity_worst_ratio_on_cpu_sample"] = round(worst, 4)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

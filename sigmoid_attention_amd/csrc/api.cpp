@@ -95,13 +95,9 @@ sigattn::PlanInput plan_input(const sigattn_args* a, int32_t pass) {
 }
 
 template <class F>
-sigattn_status run(const sigattn_args* a, int32_t pass, void* z1, void* z2, F&& launch_one) {
-  const hipStream_t st = (hipStream_t)a->stream;
+sigattn_status run(const sigattn_args* a, int32_t pass, F&& launch_one) {
   const std::vector<Launch> plan = sigattn::build_plan(plan_input(a, pass), nullptr);
-  const std::vector<sigattn::ZeroSched> zero = sigattn::build_zero_plan(a->B, a->H, a->Lmax, a->seqlens);
   (void)hipGetLastError();  // start from a clean per-thread error state
-  for (const sigattn::ZeroSched& zs : zero)
-    if (sigattn::launch_zero(a->d, zs, z1, z2, st) != hipSuccess) return SIGATTN_ERR_HIP;
   for (const Launch& L : plan)
     if (launch_one(L) != hipSuccess) return SIGATTN_ERR_HIP;
   return SIGATTN_OK;
@@ -118,7 +114,7 @@ sigattn_status sigattn_fwd(const sigattn_args* a, const void* q, const void* k, 
   void* out[] = {o};
   if ((s = check_ptrs(a, in, 3, out, 1)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
-  return run(a, SIGATTN_PASS_FWD, o, nullptr, [&](const Launch& L) {
+  return run(a, SIGATTN_PASS_FWD, [&](const Launch& L) {
     return sigattn::launch_fwd(a->d, split, L, q, k, v, o, (hipStream_t)a->stream);
   });
 }
@@ -131,7 +127,7 @@ sigattn_status sigattn_bwd_dq(const sigattn_args* a, const void* q, const void* 
   void* out[] = {dq};
   if ((s = check_ptrs(a, in, 4, out, 1)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
-  return run(a, SIGATTN_PASS_BWD_DQ, dq, nullptr, [&](const Launch& L) {
+  return run(a, SIGATTN_PASS_BWD_DQ, [&](const Launch& L) {
     return sigattn::launch_bwd_dq(a->d, split, L, q, k, v, dout, dq, (hipStream_t)a->stream);
   });
 }
@@ -144,7 +140,7 @@ sigattn_status sigattn_bwd_dkdv(const sigattn_args* a, const void* q, const void
   void* out[] = {dk, dv};
   if ((s = check_ptrs(a, in, 4, out, 2)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
-  return run(a, SIGATTN_PASS_BWD_DKDV, dk, dv, [&](const Launch& L) {
+  return run(a, SIGATTN_PASS_BWD_DKDV, [&](const Launch& L) {
     return sigattn::launch_bwd_dkdv(a->d, split, L, q, k, v, dout, dk, dv, (hipStream_t)a->stream);
   });
 }
@@ -173,10 +169,9 @@ sigattn_status sigattn_plan_stats(const sigattn_args* a, int32_t pass, int64_t* 
   if (s != SIGATTN_OK) return s;
   sigattn::PlanStats st;
   const std::vector<Launch> plan = sigattn::build_plan(plan_input(a, pass), &st);
-  const size_t zl = sigattn::build_zero_plan(a->B, a->H, a->Lmax, a->seqlens).size();
   if (work_items) *work_items = st.items;
   if (tile_pairs) *tile_pairs = st.pairs;
-  if (launches) *launches = (int32_t)(plan.size() + zl);
+  if (launches) *launches = (int32_t)plan.size();
   return SIGATTN_OK;
 }
 

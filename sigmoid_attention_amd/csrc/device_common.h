@@ -131,6 +131,27 @@ struct TileRegs {
 // 16-byte LDS read of an A fragment.
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) { return as_bf16x8(*(const u32x4*)p); }
 
+// Trailing workgroups (blockIdx.x >= compute_blocks) write the padded rows
+// n_b..Lmax-1 of one or two outputs as 0 with 16-byte stores; the compute
+// workgroups store valid rows only, so no row has two writers.
+template <int D>
+__device__ __forceinline__ void zero_padded_rows(const Sched& S, uint16_t* __restrict__ o1,
+                                                 uint16_t* __restrict__ o2) {
+  const int zb = (int)blockIdx.x - S.compute_blocks;
+  const int bhl = zb / kZeroSplit, part = zb % kZeroSplit;
+  const int bl = bhl / S.H;
+  if (bl >= S.zero_nseq) return;
+  const int n = S.zero_n[bl];
+  const size_t head = (size_t)S.zero_b0 * S.H + bhl;
+  const size_t begin = (head * S.Lmax + n) * D;
+  const size_t chunks = (size_t)(S.Lmax - n) * (D / 8);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (size_t c = (size_t)part * blockDim.x + threadIdx.x; c < chunks; c += (size_t)kZeroSplit * blockDim.x) {
+    *(u32x4*)(o1 + begin + 8 * c) = z;
+    if (o2) *(u32x4*)(o2 + begin + 8 * c) = z;
+  }
+}
+
 // Work item of this workgroup (see plan.h); false for idle blocks.  The
 // result is uniform across the workgroup.
 __device__ __forceinline__ bool find_item(const Sched& S, Item& it) {

@@ -22,7 +22,9 @@
 //   applied to P: a zero K row gives a finite score and a zero V (or dO, Q)
 //   row contributes nothing;
 // * with no row normaliser (§2A), partial products need no running max or
-//   rescale, and the inner tiles may be visited in any order.
+//   rescale, and the inner tiles may be visited in any order;
+// * padded output rows are written as 0 by trailing workgroups of the same
+//   launch (dispatched last, they fill the tail), so each call is one launch.
 #include "device_common.h"
 #include "launch.h"
 #include "plan.h"
@@ -49,6 +51,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const uint16_t* __rest
   constexpr int KE = BK * KS, VE = D * VS, STAGE = KE + VE;
   __shared__ __align__(16) uint16_t lds[2 * STAGE];
 
+  if ((int)blockIdx.x >= S.compute_blocks) {
+    zero_padded_rows<D>(S, O, nullptr);
+    return;
+  }
   Item it;
   if (!find_item(S, it)) return;
   const int n = it.n;
@@ -148,6 +154,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dq_kernel(
   constexpr int KE = BK * RS, TE = D * TS, STAGE = 2 * KE + TE;
   __shared__ __align__(16) uint16_t lds[2 * STAGE];
 
+  if ((int)blockIdx.x >= S.compute_blocks) {
+    zero_padded_rows<D>(S, dQ, nullptr);
+    return;
+  }
   Item it;
   if (!find_item(S, it)) return;
   const int n = it.n;
@@ -262,6 +272,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(
   constexpr int RE = BQ * RS, TE = D * TS, STAGE = 2 * RE + 2 * TE;
   __shared__ __align__(16) uint16_t lds[2 * STAGE];
 
+  if ((int)blockIdx.x >= S.compute_blocks) {
+    zero_padded_rows<D>(S, dK, dV);
+    return;
+  }
   Item it;
   if (!find_item(S, it)) return;
   const int n = it.n;
@@ -375,28 +389,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Zero fill of padded rows n_b..Lmax-1 for one or two outputs.
-// Grid: (nseq * H, kZeroSplit); each block clears a share of one (b, h)'s
-// padded rows with 16-byte stores.
-// ---------------------------------------------------------------------------
-constexpr int kZeroSplit = 8;
-
-__global__ __launch_bounds__(kThreads) void zero_kernel(uint16_t* __restrict__ o1, uint16_t* __restrict__ o2,
-                                                        const ZeroSched z, int D) {
-  const int bhl = blockIdx.x;
-  const int bl = bhl / z.H;
-  const int n = z.n[bl];
-  const size_t head = (size_t)z.b0 * z.H + bhl;
-  const size_t begin = (head * z.Lmax + n) * D;
-  const size_t chunks = ((size_t)(z.Lmax - n) * D) / 8;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (size_t c = (size_t)blockIdx.y * kThreads + threadIdx.x; c < chunks; c += (size_t)gridDim.y * kThreads) {
-    *(u32x4*)(o1 + begin + 8 * c) = zero;
-    if (o2) *(u32x4*)(o2 + begin + 8 * c) = zero;
-  }
-}
-
 template <int D, bool SPLIT>
 hipError_t launch_fwd_t(const Launch& L, const void* q, const void* k, const void* v, void* o, hipStream_t st) {
   hipLaunchKernelGGL((fwd_kernel<D, SPLIT>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
@@ -443,12 +435,6 @@ hipError_t launch_bwd_dkdv(int d, bool split, const Launch& L, const void* q, co
                  : launch_dkdv_t<64, false>(L, q, k, v, g, dk, dv, st);
   return split ? launch_dkdv_t<128, true>(L, q, k, v, g, dk, dv, st)
                : launch_dkdv_t<128, false>(L, q, k, v, g, dk, dv, st);
-}
-
-hipError_t launch_zero(int d, const ZeroSched& z, void* o1, void* o2, hipStream_t st) {
-  hipLaunchKernelGGL(zero_kernel, dim3(z.nseq * z.H, kZeroSplit), dim3(kThreads), 0, st, (uint16_t*)o1,
-                     (uint16_t*)o2, z, d);
-  return hipGetLastError();
 }
 
 }  // namespace sigattn

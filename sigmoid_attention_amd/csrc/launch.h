@@ -14,6 +14,5 @@ hipError_t launch_bwd_dq(int d, bool split, const Launch& L, const void* q, cons
                          const void* g, void* dq, hipStream_t st);
 hipError_t launch_bwd_dkdv(int d, bool split, const Launch& L, const void* q, const void* k, const void* v,
                            const void* g, void* dk, void* dv, hipStream_t st);
-hipError_t launch_zero(int d, const ZeroSched& z, void* o1, void* o2, hipStream_t st);
 
 }  // namespace sigattn

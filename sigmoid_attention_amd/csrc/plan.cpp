@@ -19,6 +19,34 @@ struct Piece {
 
 int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
+// Pieces of at most about `target` tile pairs, cut evenly: whole sequences
+// (all heads) when small, else runs of heads, else runs of tiles of one head.
+std::vector<Piece> make_pieces(const PlanInput& in, int64_t target) {
+  std::vector<Piece> pieces;
+  for (int32_t b = 0; b < in.B; ++b) {
+    const int32_t n = in.seqlens[b];
+    if (n <= 0) continue;
+    const int32_t items = ceil_div(n, in.outer_rows);
+    const int64_t inner = ceil_div(n, in.inner_rows);
+    const int64_t head_cost = items * inner;
+    if (head_cost * in.H <= target) {
+      pieces.push_back({b, 0, in.H, 0, items, n, inner});
+    } else if (head_cost <= target) {
+      const int32_t parts = (int32_t)((head_cost * in.H + target - 1) / target);
+      const int32_t k = ceil_div(in.H, parts);
+      for (int32_t h = 0; h < in.H; h += k)
+        pieces.push_back({b, h, std::min(k, in.H - h), 0, items, n, inner});
+    } else {
+      const int32_t parts = (int32_t)std::min<int64_t>(items, (head_cost + target - 1) / target);
+      const int32_t m = ceil_div(items, parts);
+      for (int32_t h = 0; h < in.H; ++h)
+        for (int32_t t = 0; t < items; t += m)
+          pieces.push_back({b, h, 1, t, std::min(m, items - t), n, inner});
+    }
+  }
+  return pieces;
+}
+
 }  // namespace
 
 double bias_value(int32_t n, int32_t mode, float arg) {
@@ -44,38 +72,34 @@ std::vector<Launch> build_plan(const PlanInput& in, PlanStats* stats) {
     stats->items = total_items;
     stats->pairs = total_cost;
   }
-  if (total_items == 0) return {};
 
   // Cut work so that no piece is larger than about 1/64 of the total (1/8 of
   // one XCD's share): longest-first assignment then evens out the 8 XCD lists
-  // to within a few percent on ragged batches.
-  const int64_t target = std::max<int64_t>(1, (total_cost + 8 * kXcds - 1) / (8 * kXcds));
-  for (int32_t b = 0; b < in.B; ++b) {
-    const int32_t n = in.seqlens[b];
-    if (n <= 0) continue;
-    const int32_t items = ceil_div(n, in.outer_rows);
-    const int64_t inner = ceil_div(n, in.inner_rows);
-    const int64_t head_cost = items * inner;
-    if (head_cost * in.H <= target) {
-      pieces.push_back({b, 0, in.H, 0, items, n, inner});
-    } else if (head_cost <= target) {
-      const int32_t k = (int32_t)std::max<int64_t>(1, target / head_cost);
-      for (int32_t h = 0; h < in.H; h += k)
-        pieces.push_back({b, h, std::min(k, in.H - h), 0, items, n, inner});
-    } else {
-      const int32_t m = (int32_t)std::max<int64_t>(1, target / inner);
-      for (int32_t h = 0; h < in.H; ++h)
-        for (int32_t t = 0; t < items; t += m)
-          pieces.push_back({b, h, 1, t, std::min(m, items - t), n, inner});
-    }
+  // to within a few percent on ragged batches.  If that needs more pieces than
+  // one launch holds, cut coarser (1/32, 1/16, 1/8) before resorting to
+  // several launches.
+  for (int64_t parts_per_xcd = 8; parts_per_xcd >= 1; parts_per_xcd /= 2) {
+    pieces = make_pieces(in, std::max<int64_t>(1, (total_cost + parts_per_xcd * kXcds - 1) / (parts_per_xcd * kXcds)));
+    if (pieces.size() <= (size_t)kMaxPieces) break;
   }
   // Longest first (ties: lower sequence, head, tile first, so plans are deterministic).
   std::stable_sort(pieces.begin(), pieces.end(), [](const Piece& a, const Piece& b) {
     return a.cost() > b.cost();
   });
 
+  // Zero-fill chunks: sequences [256c, 256c + 256) that have padding.
+  std::vector<int32_t> zero_chunks;
+  for (int32_t b0 = 0; b0 < in.B; b0 += kZeroSeqs) {
+    bool any = false;
+    for (int32_t b = b0; b < std::min(in.B, b0 + kZeroSeqs); ++b) any |= in.seqlens[b] < in.Lmax;
+    if (any) zero_chunks.push_back(b0);
+  }
+  const size_t piece_chunks = (pieces.size() + kMaxPieces - 1) / kMaxPieces;
+  const size_t nlaunch = std::max(piece_chunks, zero_chunks.size());
+
   std::vector<Launch> launches;
-  for (size_t p0 = 0; p0 < pieces.size(); p0 += kMaxPieces) {
+  for (size_t li = 0; li < nlaunch; ++li) {
+    const size_t p0 = std::min(pieces.size(), li * kMaxPieces);
     const size_t p1 = std::min(pieces.size(), p0 + kMaxPieces);
     // Longest-processing-time-first over the 8 XCD lists.
     std::vector<std::vector<Piece>> lists(kXcds);
@@ -115,29 +139,18 @@ std::vector<Launch> build_plan(const PlanInput& in, PlanStats* stats) {
       max_items = std::max(max_items, item);
     }
     L.sched.xcd_begin[kXcds] = g;
-    L.blocks = kXcds * max_items;
+    L.sched.compute_blocks = kXcds * max_items;
+    L.blocks = L.sched.compute_blocks;
+    if (li < zero_chunks.size()) {
+      const int32_t b0 = zero_chunks[li];
+      L.sched.zero_b0 = b0;
+      L.sched.zero_nseq = std::min(kZeroSeqs, in.B - b0);
+      for (int32_t i = 0; i < L.sched.zero_nseq; ++i) L.sched.zero_n[i] = in.seqlens[b0 + i];
+      L.blocks += L.sched.zero_nseq * in.H * kZeroSplit;
+    }
     launches.push_back(L);
   }
   return launches;
-}
-
-std::vector<ZeroSched> build_zero_plan(int32_t B, int32_t H, int32_t Lmax, const int32_t* seqlens) {
-  std::vector<ZeroSched> out;
-  for (int32_t b0 = 0; b0 < B; b0 += kZeroMaxSeqs) {
-    ZeroSched z;
-    std::memset(&z, 0, sizeof(z));
-    z.H = H;
-    z.Lmax = Lmax;
-    z.b0 = b0;
-    z.nseq = std::min(kZeroMaxSeqs, B - b0);
-    bool any = false;
-    for (int32_t i = 0; i < z.nseq; ++i) {
-      z.n[i] = seqlens[b0 + i];
-      any |= z.n[i] < Lmax;
-    }
-    if (any) out.push_back(z);
-  }
-  return out;
 }
 
 }  // namespace sigattn

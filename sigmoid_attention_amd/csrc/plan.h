@@ -24,9 +24,13 @@
 namespace sigattn {
 
 constexpr int kXcds = 8;
-// Pieces per launch: six 4-byte arrays of this length plus a small header
-// keep the kernel-argument block near 3.2 KB, under the 4 KB limit.
-constexpr int kMaxPieces = 128;
+// Pieces per launch and sequences zero-filled per launch: six 4-byte arrays of
+// kMaxPieces, one of kZeroSeqs and a small header keep the kernel-argument
+// block near 3.4 KB, under the 4 KB limit.
+constexpr int kMaxPieces = 96;
+constexpr int kZeroSeqs = 256;
+// Workgroups that share the zero fill of one (sequence, head).
+constexpr int kZeroSplit = 4;
 
 // Kernel-argument block.  Plain data; copied by value into every launch.
 struct Sched {
@@ -44,6 +48,13 @@ struct Sched {
   int32_t t0[kMaxPieces];        // first outer tile of the piece
   int32_t nt[kMaxPieces];        // outer tiles per head in the piece
   float c2[kMaxPieces];          // -bias * log2(e)
+  // Padded rows n_b..Lmax-1 of the outputs are written as 0 by trailing
+  // workgroups: block compute_blocks + (bl * H + h) * kZeroSplit + part clears
+  // part `part` of those rows of sequence zero_b0 + bl, head h.
+  int32_t compute_blocks;        // 8 * max(xcd_items)
+  int32_t zero_b0;               // first sequence zero-filled by this launch
+  int32_t zero_nseq;             // sequences zero-filled by this launch (0: none)
+  int32_t zero_n[kZeroSeqs];     // their valid lengths
 };
 
 // Callable from kernels and from host-side checks of the schedule.
@@ -81,7 +92,7 @@ inline SIGATTN_HD bool decode_item(const Sched& S, int32_t x, int32_t j, Item& i
 
 struct Launch {
   Sched sched;
-  int32_t blocks;  // grid size = 8 * max(xcd_items)
+  int32_t blocks;  // grid size: compute blocks + zero-fill blocks
 };
 
 struct PlanInput {
@@ -98,23 +109,11 @@ struct PlanStats {
   int64_t pairs = 0;
 };
 
-// Builds the launches (possibly none, when every n_b is 0).
+// Builds the launches: the compute work (if any n_b > 0) and the zero fill of
+// padded rows (if any n_b < Lmax).  Empty when there is neither.
 std::vector<Launch> build_plan(const PlanInput& in, PlanStats* stats);
 
 // The bias b for a sequence of valid length n (n >= 1) in double precision.
 double bias_value(int32_t n, int32_t mode, float arg);
-
-// Zero-fill schedule: padded rows n_b..Lmax-1 of every (b, h) are written as 0
-// by a separate light kernel, so the compute kernels store only valid rows.
-constexpr int kZeroMaxSeqs = 512;
-struct ZeroSched {
-  int32_t H;
-  int32_t Lmax;
-  int32_t b0;                    // first sequence covered by this launch
-  int32_t nseq;                  // sequences covered
-  int32_t n[kZeroMaxSeqs];
-};
-
-std::vector<ZeroSched> build_zero_plan(int32_t B, int32_t H, int32_t Lmax, const int32_t* seqlens);
 
 }  // namespace sigattn

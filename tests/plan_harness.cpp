@@ -2,7 +2,8 @@
 // on the command line and walks every workgroup of every launch through the
 // same decode_item() the kernels use.  Verifies that each non-padded output
 // tile is visited exactly once and that no fully padded tile appears; prints
-// a one-line JSON summary.
+// a one-line JSON summary.  Also checks that every sequence with padding is
+// zero-filled by exactly one launch.
 //
 // usage: plan_harness B H Lmax d outer_rows inner_rows n_0 ... n_{B-1}
 #include <cstdio>
@@ -32,12 +33,19 @@ int main(int argc, char** argv) {
   sigattn::PlanStats st;
   const std::vector<sigattn::Launch> plan = sigattn::build_plan(in, &st);
   std::map<std::pair<int, int>, int> seen;
+  std::vector<int> zeroed(in.B, 0);
   long long blocks = 0, idle = 0, bad = 0, pairs = 0;
   double worst_imbalance = 0.0;
   for (const auto& L : plan) {
-    if (L.blocks % sigattn::kXcds) ++bad;
+    if (L.sched.compute_blocks % sigattn::kXcds) ++bad;
+    if (L.blocks != L.sched.compute_blocks + L.sched.zero_nseq * in.H * sigattn::kZeroSplit) ++bad;
+    for (int32_t i = 0; i < L.sched.zero_nseq; ++i) {
+      const int b = L.sched.zero_b0 + i;
+      if (b >= in.B || L.sched.zero_n[i] != lens[b]) ++bad;
+      else zeroed[b]++;
+    }
     long long xload[sigattn::kXcds] = {0};
-    for (int32_t i = 0; i < L.blocks; ++i) {
+    for (int32_t i = 0; i < L.sched.compute_blocks; ++i) {
       sigattn::Item it;
       ++blocks;
       if (!sigattn::decode_item(L.sched, i % sigattn::kXcds, i / sigattn::kXcds, it)) {
@@ -74,10 +82,13 @@ int main(int argc, char** argv) {
       }
   }
   const long long extra = (long long)seen.size() - (expect - missing);
+  long long zero_bad = 0;
+  for (int b = 0; b < in.B; ++b)
+    if (lens[b] < in.Lmax ? zeroed[b] != 1 : zeroed[b] > 1) ++zero_bad;
   printf("{\"launches\": %zu, \"blocks\": %lld, \"idle\": %lld, \"items\": %lld, \"expect\": %lld, "
          "\"missing\": %lld, \"dup\": %lld, \"extra\": %lld, \"bad\": %lld, \"pairs\": %lld, "
-         "\"stats_items\": %lld, \"stats_pairs\": %lld, \"xcd_imbalance\": %.4f}\n",
+         "\"stats_items\": %lld, \"stats_pairs\": %lld, \"xcd_imbalance\": %.4f, \"zero_bad\": %lld}\n",
          plan.size(), blocks, idle, blocks - idle, expect, missing, dup, extra, bad, pairs, (long long)st.items,
-         (long long)st.pairs, worst_imbalance);
+         (long long)st.pairs, worst_imbalance, zero_bad);
   return 0;
 }

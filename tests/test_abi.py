@@ -153,7 +153,7 @@ def test_plan_stats_closed_forms(pass_, d):
     outer, inner = sa.tile_shape(pass_, d)
     items, pairs, launches = sa.plan_stats(8, 16, 2048, d, lens, pass_)
     assert (items, pairs) == expected_counts(16, lens, outer, inner)
-    assert launches == 2  # one compute launch + one zero-fill launch (there is padding)
+    assert launches == 1  # one launch: compute workgroups plus trailing zero-fill workgroups
     items, pairs, launches = sa.plan_stats(2, 3, 256, d, [0, 0], pass_)
     assert (items, pairs, launches) == (0, 0, 1)  # nothing to compute, all rows zero-filled
     items, pairs, launches = sa.plan_stats(2, 3, 256, d, [256, 256], pass_)

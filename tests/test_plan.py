@@ -55,6 +55,7 @@ CASES = [
     ("single_head_long", 1, 1, 8192, [8192]),
     ("few_heads_long", 1, 4, 8192, [8192]),
     ("many_sequences", 300, 8, 512, list(np.random.default_rng(1).integers(0, 513, 300))),
+    ("many_full_sequences", 600, 2, 256, [256] * 599 + [255]),
 ]
 
 
@@ -66,9 +67,10 @@ def test_schedule_covers_every_tile_once(harness, case, pass_):
     r = run(harness, B, H, L, 64, lens, outer, inner)
     items, pairs = closed_forms(H, lens, outer, inner)
     assert r["missing"] == 0 and r["dup"] == 0 and r["extra"] == 0 and r["bad"] == 0, r
+    assert r["zero_bad"] == 0, r
     assert r["items"] == items == r["stats_items"], r
     assert r["pairs"] == pairs == r["stats_pairs"], r
-    if items == 0:
+    if items == 0 and all(n == L for n in lens):
         assert r["launches"] == 0
 
 
@@ -80,6 +82,7 @@ def test_schedule_on_workloads(harness, name):
         r = run(harness, w.B, w.H, w.Lmax, w.d, lens, outer, inner)
         items, pairs = closed_forms(w.H, lens, outer, inner)
         assert r["missing"] == 0 and r["dup"] == 0 and r["extra"] == 0 and r["bad"] == 0, r
+        assert r["zero_bad"] == 0, r
         assert (r["items"], r["pairs"]) == (items, pairs)
         # Longest-first over 8 XCD lists keeps the per-XCD tile-pair load even
         # (a batch with fewer items than XCD lists cannot be even).
