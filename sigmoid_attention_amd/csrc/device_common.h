@@ -9,15 +9,13 @@
 //                       8*(r/4) + 4*hf + (r%4)
 // Every product below is arranged so that the operand read from LDS is A and
 // the operand held in registers is B, and so that the C layout of the score
-// product S^T (keys x queries) feeds the B operand of the second product
+// product (e.g. S^T, keys x queries) feeds the B operand of the second product
 // directly: for a 16-wide K-chunk c the lane's eight C values
 // r = 8*(c%2) .. 8*(c%2)+7 of block c/2 are the rows
 //   16c + 4*hf + {0,1,2,3}  and  16c + 8 + 4*hf + {0,1,2,3}.
 // The contraction order inside a chunk does not matter as long as the A
-// operand uses the same order, so tiles that feed A along that index are
-// stored transposed in LDS with the rows of each 16-chunk permuted as
-//   [0-3, 8-11, 4-7, 12-15]  (quads 1 and 2 swapped)
-// which makes each lane's eight A values one contiguous 16-byte read.
+// operand uses the same order; the A operand of the second product is read
+// with transposing LDS reads (see TrFrag) in exactly that order.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -55,14 +53,6 @@ __device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) { return __builtin_convertv
 // Widen bf16 back to float exactly (bits << 16).
 __device__ __forceinline__ f32x8 to_f32x8(bf16x8 x) { return __builtin_convertvector(x, f32x8); }
 
-// Position of row r (0..63, or any multiple-of-16 range) inside a transposed
-// tile: quads 1 and 2 of every 16-row chunk trade places.
-__device__ __forceinline__ int perm_pos(int r) {
-  const int q4 = (r >> 2) & 3;
-  const int pq = ((q4 & 1) << 1) | (q4 >> 1);
-  return (r & ~15) | (pq << 2) | (r & 3);
-}
-
 // The eight values of C register block `blk` that form K-chunk `half` (0/1).
 __device__ __forceinline__ f32x8 chunk8(const f32x16& c, int half) {
   f32x8 r;
@@ -71,62 +61,143 @@ __device__ __forceinline__ f32x8 chunk8(const f32x16& c, int half) {
   return r;
 }
 
-// A global tile of ROWS x D bf16 rows (row stride D elements) staged through
-// registers.  Thread `tid` (0..255) owns NP row pairs (2kp, 2kp+1) of one
-// 8-column group each: pair index p = tid + 256*i, kp = p / (D/8),
-// col8 = p % (D/8).  Eight consecutive lanes read one full 2*D-byte row, so
-// global loads are coalesced 16-byte vectors.  Rows at or beyond `valid` are
-// zero-filled and never read from memory (so padding garbage, even NaN/Inf,
-// cannot reach the products).
-template <int ROWS, int D>
-struct TileRegs {
-  static constexpr int NP = ROWS * D / (16 * 256);
-  static_assert(NP >= 1 && ROWS * D == NP * 16 * 256, "tile must split evenly over 256 threads");
-  u32x4 r0[NP], r1[NP];
+// ---------------------------------------------------------------------------
+// LDS tile layout.  A tile holds ROWS rows of D bf16 values (keys or queries
+// by d).  Row r keeps its D/8 16-byte groups in order up to an XOR of the
+// group index by X(r):
+//     slot(r, g) = r * D/8 + (g ^ X(r))        (16-byte slots)
+//     D = 64:  X(r) = ((r >> 1) & 1) << 2 | ((r >> 2) & 3)
+//     D = 128: X(r) = (r & 3) << 2 | ((r >> 2) & 3)
+// The same copy serves both operand shapes the products need:
+// * 16-byte fragment reads (A operand, rows = tile rows, K-slots along d):
+//   the 16 lanes a 64-bank LDS serves per cycle read 16 consecutive rows at
+//   one group, and X is a bijection on those rows (within each row parity for
+//   D = 64), so all 64 banks are hit once;
+// * transposing reads (ds_read_b64_tr_b16; A operand, rows = d, K-slots along
+//   the tile rows): 32 lanes read 4 consecutive rows x 4 aligned groups, and X
+//   sends the 4 rows to disjoint group sets.
+// Both were measured conflict-free (SQ_LDS_BANK_CONFLICT = 0) on MI355X.
+// Each row's groups stay contiguous, so a tile is filled by direct
+// global -> LDS loads in which 8 consecutive lanes read one row.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int tile_xor(int r) {
+  if (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  return ((r & 3) << 2) | ((r >> 2) & 3);
+}
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int row0, int valid, int tid) {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int p = tid + 256 * i;
-      const int kp = p / (D / 8), col8 = p % (D / 8);
-      const int ra = row0 + 2 * kp, rb = ra + 1;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      r0[i] = ra < valid ? *(const u32x4*)(src + (size_t)ra * D + 8 * col8) : z;
-      r1[i] = rb < valid ? *(const u32x4*)(src + (size_t)rb * D + 8 * col8) : z;
-    }
-  }
+template <int D>
+__device__ __forceinline__ int tile_slot(int r, int g) {
+  return r * (D / 8) + (g ^ tile_xor<D>(r));
+}
 
-  // Row-major copy: lds[row * STRIDE + col].
-  template <int STRIDE>
-  __device__ __forceinline__ void store_rows(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int p = tid + 256 * i;
-      const int kp = p / (D / 8), col8 = p % (D / 8);
-      *(u32x4*)(lds + (2 * kp) * STRIDE + 8 * col8) = r0[i];
-      *(u32x4*)(lds + (2 * kp + 1) * STRIDE + 8 * col8) = r1[i];
-    }
-  }
-
-  // Transposed copy with permuted row order: lds[col * STRIDE + perm_pos(row)].
-  // Rows 2kp and 2kp+1 stay adjacent (quads are 4-aligned), so each column
-  // element pair is one 4-byte store.
-  template <int STRIDE>
-  __device__ __forceinline__ void store_cols(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int p = tid + 256 * i;
-      const int kp = p / (D / 8), col8 = p % (D / 8);
-      const int pos = perm_pos(2 * kp);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a = r0[i][e >> 1], b = r1[i][e >> 1];
-        const uint32_t word = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-        *(uint32_t*)(lds + (8 * col8 + e) * STRIDE + pos) = word;
-      }
-    }
+// Range-checked view of one (sequence, head) slice: rows 0..n-1 of D bf16
+// values.  Loads go through a raw buffer resource whose size is n * D * 2
+// bytes, so a load at or beyond row n returns zeros without touching memory:
+// padded rows are zero-filled by the hardware, with no VALU masking and no
+// branch, and garbage (even NaN/Inf) in padded rows cannot reach a product.
+// Offsets are 32-bit: the API bounds Lmax * d * 2 below 2^31.
+struct Slice {
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ Slice(const uint16_t* base, int n, int D)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc((void*)base, 0, n * D * 2, 0x00020000)) {}
+  // 16 bytes at element offset `elem` (a multiple of 8).
+  __device__ __forceinline__ u32x4 load16(int elem) const {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, elem * 2, 0, 0));
   }
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS loading of a ROWS x D tile (buffer_load_dwordx4 ... lds).
+// Each of the 4 waves issues NI instructions per tile; instruction i of wave w
+// fills the 1 KB block b = 4i + w of the tile, lane L writing slot 64b + L.
+// The per-lane source offset inverts the tile layout, so the 8 lanes of one
+// row read that row's 128 contiguous bytes (coalesced).  Completion is
+// tracked by vmcnt: wait (vm_drain) before the barrier that publishes a tile.
+template <int ROWS, int D>
+struct TileDma {
+  static constexpr int NI = ROWS * D * 2 / (4 * 1024);
+  static_assert(NI >= 1 && NI * 4 * 1024 == ROWS * D * 2, "tile must split into 1 KB blocks over 4 waves");
+  int src[NI];  // element offset within the tile's rows
+  int dst[NI];  // element offset of this wave's block within the tile (wave-uniform)
+  __device__ __forceinline__ TileDma(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int blk = 4 * i + wave;
+      const int t = 64 * blk + lane;  // 16-byte slot filled by this lane
+      const int r = t / (D / 8);
+      const int g = (t % (D / 8)) ^ tile_xor<D>(r);
+      src[i] = r * D + 8 * g;
+      dst[i] = 512 * blk;
+    }
+  }
+  // Tile rows row0 .. row0+ROWS-1 of `s` into `tile` (rows >= n read as zeros).
+  // The builtin is compiled in the device pass only: seen by the host pass,
+  // it makes clang drop the host stubs of the kernels that use it.
+  __device__ __forceinline__ void load(const Slice& s, int row0, uint16_t* tile) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rsrc, (lds_void*)(tile + dst[i]), 16, (src[i] + row0 * D) * 2, 0,
+                                               0, 0);
+#endif
+  }
+};
+
+// Wait until this wave's outstanding global loads (including LDS DMA) landed.
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0); }
+
+// B-operand fragments of one row of a slice (this lane's row), K-slots along
+// d: 16s + 8hf .. +7.  Rows >= n read as zero.
+template <int D>
+__device__ __forceinline__ void load_bfrag(bf16x8 (&f)[D / 16], const Slice& src, int row, int hf) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) f[s] = as_bf16x8(src.load16(row * D + 16 * s + 8 * hf));
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16).
+__device__ __forceinline__ bf16x4 lds_tr4(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// A fragment for rows = head-dim index d, K-slots = tile rows, read with
+// transposing reads.  For the MFMA of output block db (d = 32db .. 32db+31)
+// and K-chunk c (tile rows 16c .. 16c+15 in the order of the score registers):
+//   first read: rows 16c + 4*hf + {0..3}, second read: rows 16c + 8 + 4*hf + {0..3}.
+// Source lane j (of each 16) addresses row 16c + 4hf + j/4 (+8) at columns
+// 32db + 16gq + 4(j%4) .. +3; destination lane i then holds column
+// 32db + 16gq + i of those four rows.
+template <int D>
+struct TrFrag {
+  int row_lane;  // 4*hf + (j >> 2)
+  int chunk;     // this lane's 4-column chunk within a 32-column block: 4*gq + (j & 3)
+  __device__ __forceinline__ TrFrag(int lane) {
+    const int j = lane & 15, gq = (lane >> 4) & 1, hf = lane >> 5;
+    row_lane = 4 * hf + (j >> 2);
+    chunk = 4 * gq + (j & 3);
+  }
+  __device__ __forceinline__ int offset(int r, int db) const {
+    const int ch = 8 * db + chunk;  // 4-column chunk index
+    return 8 * tile_slot<D>(r, ch >> 1) + 4 * (ch & 1);
+  }
+  __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int db, int c) const {
+    const int r = 16 * c + row_lane;
+    const bf16x4 lo = lds_tr4(tile + offset(r, db));
+    const bf16x4 hi = lds_tr4(tile + offset(r + 8, db));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
+// A fragment (rows = tile rows 32mb .. 32mb+31, K-slots = head dim
+// 16s + 8hf .. +7) with a 16-byte read.
+template <int D>
+__device__ __forceinline__ bf16x8 frag_read(const uint16_t* tile, int mb, int s, int l32, int hf) {
+  return as_bf16x8(*(const u32x4*)(tile + 8 * tile_slot<D>(32 * mb + l32, 2 * s + hf)));
+}
 
 // 16-byte LDS read of an A fragment.
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) { return as_bf16x8(*(const u32x4*)p); }

@@ -1,5 +1,5 @@
 // Sigmoid attention kernels for gfx950: fused forward, backward-dQ,
-// backward-dK/dV, and the padded-row zero fill.
+// backward-dK/dV; padded output rows are zero-filled by the same launches.
 //
 // Method: "Better Models, Faster Training: Sigmoid Attention for single-cell
 // Foundation Models", technical summary §2A (O = sigma(Q K^T / sqrt(d) + b) V,
@@ -10,14 +10,16 @@
 // Design for MI355X (not a translation of the pages' Triton/H100 kernel):
 // * one 256-thread workgroup (4 waves of 64) per output tile; each wave owns
 //   32 output rows, so every product is a 32x32x16 bf16 MFMA;
-// * the streamed tile (K/V in the forward and dQ kernels, Q/dO in the dK/dV
-//   kernel) goes global -> registers -> LDS, double-buffered, with the next
-//   tile's global loads in flight while the current one is multiplied: one
-//   barrier per inner step;
-// * tiles feeding an MFMA A operand along the contraction index are written
-//   to LDS transposed (see device_common.h for the permuted row order), so
-//   the score product's output registers are directly the B operand of the
-//   second product: P never leaves registers and is never stored;
+// * the tile streamed by the inner loop (K/V in the forward and dQ kernels,
+//   Q/dO in the dK/dV kernel) is loaded straight from global memory into LDS
+//   (buffer_load ... lds), one step ahead, with hardware zero-fill past the
+//   sequence end; one LDS copy per tile serves both the 16-byte fragment
+//   reads and the transposing reads (see device_common.h): one barrier per
+//   inner step and no VALU work for staging;
+// * the score product's output registers are directly the B operand of the
+//   second product (see device_common.h): P and dS never leave registers and
+//   are never stored; the transposed A operand is read with ds_read_b64_tr_b16
+//   from a row-major tile, so nothing is transposed on the VALU;
 // * rows at or beyond n_b are zero-filled on load, never read, so no mask is
 //   applied to P: a zero K row gives a finite score and a zero V (or dO, Q)
 //   row contributes nothing;
@@ -31,25 +33,141 @@
 
 namespace sigattn {
 
-namespace {
+namespace kern {
 
 constexpr int kThreads = 256;
+constexpr int kInner = 64;  // rows per inner tile
+
+// Schedule per kernel and head dim: LA = compute the next tile's scores while
+// the VALU works on this tile (two tiles of scores live in registers), and
+// OCC = waves per SIMD the register budget is sized for.  Measured on MI355X:
+// a second resident workgroup per CU overlaps MFMA and VALU better than the
+// in-wave lookahead where both do not fit together.
+#ifndef SIGATTN_FWD64_LA
+#define SIGATTN_FWD64_LA 1
+#endif
+#ifndef SIGATTN_FWD64_OCC
+#define SIGATTN_FWD64_OCC 2
+#endif
+#ifndef SIGATTN_DQ64_LA
+#define SIGATTN_DQ64_LA 1
+#endif
+#ifndef SIGATTN_DQ64_OCC
+#define SIGATTN_DQ64_OCC 2
+#endif
+#ifndef SIGATTN_INTERLEAVE
+#define SIGATTN_INTERLEAVE 0
+#endif
+#ifndef SIGATTN_DKDV64_LA
+#define SIGATTN_DKDV64_LA 0
+#endif
+#ifndef SIGATTN_DKDV64_OCC
+#define SIGATTN_DKDV64_OCC 2
+#endif
+template <int D> struct FwdCfg { static constexpr bool LA = D == 64 ? SIGATTN_FWD64_LA : true; static constexpr int OCC = D == 64 ? SIGATTN_FWD64_OCC : 1; };
+template <int D> struct DqCfg { static constexpr bool LA = D == 64 ? SIGATTN_DQ64_LA : true; static constexpr int OCC = D == 64 ? SIGATTN_DQ64_OCC : 1; };
+template <int D> struct DkdvCfg { static constexpr bool LA = D == 64 ? SIGATTN_DKDV64_LA : false; static constexpr int OCC = D == 64 ? SIGATTN_DKDV64_OCC : 1; };
+
+// sigma of the eight score values of K-chunk c, rounded to bf16 (hi) and, in
+// split precision, the bf16 remainder (lo).
+template <bool SPLIT>
+__device__ __forceinline__ void sigmoid_chunk(const f32x16 (&sc)[2], int c, float c1, float c2, bf16x8& hi,
+                                              bf16x8& lo) {
+  f32x8 p = chunk8(sc[c >> 1], c & 1);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) p[t] = sigmoid2(p[t], c1, c2);
+  hi = to_bf16x8(p);
+  if (SPLIT) lo = to_bf16x8(p - to_f32x8(hi));
+}
+
+// dS = dP * sigma * (1 - sigma) for K-chunk c (and optionally sigma itself).
+template <bool SPLIT, bool WANT_P>
+__device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[2], const f32x16 (&dp)[2], int c, float c1,
+                                               float c2, bf16x8& dh, bf16x8& dl, bf16x8& ph, bf16x8& pl) {
+  const f32x8 sv = chunk8(sc[c >> 1], c & 1), gv = chunk8(dp[c >> 1], c & 1);
+  f32x8 p8, ds;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float p = sigmoid2(sv[t], c1, c2);
+    p8[t] = p;
+    ds[t] = gv[t] * __builtin_fmaf(-p, p, p);  // dP * p (1 - p)
+  }
+  dh = to_bf16x8(ds);
+  if (SPLIT) dl = to_bf16x8(ds - to_f32x8(dh));
+  if (WANT_P) {
+    ph = to_bf16x8(p8);
+    if (SPLIT) pl = to_bf16x8(p8 - to_f32x8(ph));
+  }
+}
+
+// Store 4 consecutive fp32 values of an output row as bf16 (8 bytes).
+__device__ __forceinline__ void store4(uint16_t* dst, const f32x16& acc, int i, float scale) {
+  f32x8 v8;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    v8[t] = scale * acc[4 * i + t];
+    v8[4 + t] = 0.0f;
+  }
+  const u32x4 packed = as_u32x4(to_bf16x8(v8));
+  *(uint2*)dst = (uint2){packed[0], packed[1]};
+}
+
+// Score-product helpers.  `tile` is an LDS tile; `bf` holds the B fragments
+// (this wave's 32 rows of the other operand).  Block mb covers tile rows
+// 32mb .. 32mb+31; K-steps s cover d = 16s .. 16s+15.
+template <int D>
+__device__ __forceinline__ void score_steps(f32x16 (&acc)[2], const uint16_t* tile, const bf16x8 (&bf)[D / 16],
+                                            int s0, int s1, int l32, int hf) {
+#pragma unroll
+  for (int s = s0; s < s1; ++s)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc[mb] = mfma(frag_read<D>(tile, mb, s, l32, hf), bf[s], acc[mb]);
+}
+
+template <int D>
+__device__ __forceinline__ void score_block(f32x16& acc, const uint16_t* tile, const bf16x8 (&bf)[D / 16], int mb,
+                                            int l32, int hf) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) acc = mfma(frag_read<D>(tile, mb, s, l32, hf), bf[s], acc);
+}
+
+// Second-product step for K-chunk c: acc[db] += A(tile rows d, K-chunk c) . B.
+template <int D, bool SPLIT>
+__device__ __forceinline__ void value_chunk(f32x16 (&acc)[D / 32], const TrFrag<D>& tr, const uint16_t* tile, int c,
+                                            const bf16x8& bh, const bf16x8& bl) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const bf16x8 a = tr.read(tile, db, c);
+    acc[db] = mfma(a, bh, acc[db]);
+    if (SPLIT) acc[db] = mfma(a, bl, acc[db]);
+  }
+}
+
+__device__ __forceinline__ void zero2(f32x16 (&a)[2]) {
+  a[0] = (f32x16){};
+  a[1] = (f32x16){};
+}
+
+// Rotating index over 3 LDS stages.
+__device__ __forceinline__ int next3(int i) { return i == 2 ? 0 : i + 1; }
 
 // ---------------------------------------------------------------------------
-// Forward.  Item = (b, h, 128-query tile).  Inner loop: 64-key tiles.
-// Per wave and key tile: S^T (64 keys x 32 queries) = K . Q^T, P = sigma,
-// O^T (d x 32 queries) += V^T . P^T.
+// Forward.  Item = (b, h, 128-query tile).  Inner loop: 64-key tiles j.
+// Per wave (32 queries): S^T_j (64 keys x 32 queries) = K_j . Q^T,
+// P_j = sigma(S^T_j), O^T (d x 32 queries) += V_j^T . P_j.
+// LDS: K in 3 stages (tile j+1 feeds the scores computed during step j while
+// the VALU evaluates sigma of tile j; tile j+2 is loading), V in 2 stages.
+// Tiles are loaded global -> LDS directly, one step ahead; loads past the
+// sequence return zeros, so the steady state has no branches (the few
+// products on such tiles are unused).
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const uint16_t* __restrict__ Q,
-                                                          const uint16_t* __restrict__ K,
-                                                          const uint16_t* __restrict__ V,
-                                                          uint16_t* __restrict__ O, const Sched S) {
-  constexpr int BQ = 128, BK = 64;
-  constexpr int KS = D + 8;   // K tile row stride (elements); +16 B keeps 16-B reads conflict-free
-  constexpr int VS = BK + 8;  // V^T tile row stride
-  constexpr int KE = BK * KS, VE = D * VS, STAGE = KE + VE;
-  __shared__ __align__(16) uint16_t lds[2 * STAGE];
+template <int D, bool SPLIT, bool LA = FwdCfg<D>::LA>
+__global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uint16_t* __restrict__ Q,
+                                                                        const uint16_t* __restrict__ K,
+                                                                        const uint16_t* __restrict__ V,
+                                                                        uint16_t* __restrict__ O, const Sched S) {
+  constexpr int BQ = 128, BK = kInner, TILE = BK * D;
+  __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
 
   if ((int)blockIdx.x >= S.compute_blocks) {
     zero_padded_rows<D>(S, O, nullptr);
@@ -59,100 +177,82 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const uint16_t* __rest
   if (!find_item(S, it)) return;
   const int n = it.n;
   const size_t base = (size_t)it.bh * S.Lmax * D;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c1 = S.c1, c2 = it.c2;
+  const TrFrag<D> tr(lane);
+  const TileDma<BK, D> dma(w, lane);
+  auto Kb = [&](int i) { return lds + i * TILE; };
+  auto Vb = [&](int i) { return lds + (3 + i) * TILE; };
+  const Slice qs(Q + base, n, D), ks(K + base, n, D), vs(V + base, n, D);
 
   const int qrow = it.tile * BQ + 32 * w + l32;
   bf16x8 qf[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    qf[s] = as_bf16x8(qrow < n ? *(const u32x4*)(Q + base + (size_t)qrow * D + 16 * s + 8 * hf) : z);
-  }
-
+  load_bfrag<D>(qf, qs, qrow, hf);
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
 
   const int nk = (n + BK - 1) / BK;
-  TileRegs<BK, D> kr, vr;
-  kr.load(K + base, 0, n, tid);
-  vr.load(V + base, 0, n, tid);
-  kr.template store_rows<KS>(lds, tid);
-  vr.template store_cols<VS>(lds + KE, tid);
+  dma.load(ks, 0, Kb(0));
+  dma.load(ks, BK, Kb(1));
+  dma.load(vs, 0, Vb(0));
+  vm_drain();
   __syncthreads();
+  f32x16 sA[2], sB[2];
+  zero2(sA);
+  score_steps<D>(sA, Kb(0), qf, 0, D / 16, l32, hf);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const uint16_t* Ks = lds + (kt & 1) * STAGE;
-    const uint16_t* Vt = Ks + KE;
-    if (kt + 1 < nk) {
-      kr.load(K + base, (kt + 1) * BK, n, tid);
-      vr.load(V + base, (kt + 1) * BK, n, tid);
-    }
-    f32x16 st[2] = {(f32x16){}, (f32x16){}};
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        st[mb] = mfma(lds_frag(Ks + (32 * mb + l32) * KS + 16 * s + 8 * hf), qf[s], st[mb]);
-    }
+  int kc = 0;  // K stage of tile j
+  auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    const int k1 = next3(kc), k2 = next3(k1);
+    dma.load(ks, (j + 2) * BK, Kb(k2));       // stage of tile j-1: free since the last barrier
+    dma.load(vs, (j + 1) * BK, Vb((j + 1) & 1));
+    const uint16_t* Kn = Kb(k1);
+    const uint16_t* Vc = Vb(j & 1);
+    zero2(nxt);
     bf16x8 ph[4], pl[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      f32x8 p = chunk8(st[c >> 1], c & 1);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) p[t] = sigmoid2(p[t], c1, c2);
-      ph[c] = to_bf16x8(p);
-      if (SPLIT) pl[c] = to_bf16x8(p - to_f32x8(ph[c]));
+      if (LA) score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), l32, hf);  // MFMA: tile j+1
+      sigmoid_chunk<SPLIT>(cur, c, c1, c2, ph[c], pl[c]);                              // VALU: tile j
+      if (c > 0) value_chunk<D, SPLIT>(acc, tr, Vc, c - 1, ph[c - 1], pl[c - 1]);
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 a = lds_frag(Vt + (32 * db + l32) * VS + 16 * c + 8 * hf);
-        acc[db] = mfma(a, ph[c], acc[db]);
-        if (SPLIT) acc[db] = mfma(a, pl[c], acc[db]);
-      }
-    }
-    if (kt + 1 < nk) {
-      uint16_t* nxt = lds + ((kt + 1) & 1) * STAGE;
-      kr.template store_rows<KS>(nxt, tid);
-      vr.template store_cols<VS>(nxt + KE, tid);
-    }
+    value_chunk<D, SPLIT>(acc, tr, Vc, 3, ph[3], pl[3]);
+    if (!LA) score_steps<D>(nxt, Kn, qf, 0, D / 16, l32, hf);
+    vm_drain();
     __syncthreads();
+    kc = k1;
+  };
+  int j = 0;
+  for (; j + 1 < nk; j += 2) {
+    step(j, sA, sB);
+    step(j + 1, sB, sA);
   }
+  if (j < nk) step(j, sA, sB);
 
   if (qrow < n) {
     uint16_t* dst = O + base + (size_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x8 v8;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) { v8[t] = acc[db][4 * i + t]; v8[4 + t] = 0.0f; }
-        const u32x4 packed = as_u32x4(to_bf16x8(v8));
-        uint2 out = {packed[0], packed[1]};
-        *(uint2*)(dst + 32 * db + 8 * i + 4 * hf) = out;
-      }
-    }
+      for (int i = 0; i < 4; ++i) store4(dst + 32 * db + 8 * i + 4 * hf, acc[db], i, 1.0f);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Backward, dQ.  Item = (b, h, 128-query tile).  Inner loop: 64-key tiles.
-// Per wave and key tile: S^T = K . Q^T, dP^T = V . dO^T, dS^T = dP^T * P(1-P),
-// dQ^T (d x 32 queries) += K^T . dS^T.  dQ = dQ^T^T / sqrt(d).
+// Backward, dQ.  Item = (b, h, 128-query tile).  Inner loop: 64-key tiles j.
+// Per wave (32 queries): S^T_j = K_j . Q^T, dP^T_j = V_j . dO^T,
+// dS^T_j = dP^T_j * P(1-P), dQ^T (d x 32 queries) += K_j^T . dS^T_j.
+// LDS: K in 3 stages (tile j: transposing reads for dQ; tile j+1: scores;
+// tile j+2: loading), V in 2 stages (tile j: dP; tile j+1: loading).
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT>
-__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dq_kernel(
+template <int D, bool SPLIT, bool LA = DqCfg<D>::LA>
+__global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, const Sched S) {
-  constexpr int BQ = 128, BK = 64;
-  constexpr int RS = D + 8;   // row-major K and V tiles
-  constexpr int TS = BK + 8;  // transposed K tile
-  constexpr int KE = BK * RS, TE = D * TS, STAGE = 2 * KE + TE;
-  __shared__ __align__(16) uint16_t lds[2 * STAGE];
+  constexpr int BQ = 128, BK = kInner, TILE = BK * D;
+  __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
 
   if ((int)blockIdx.x >= S.compute_blocks) {
     zero_padded_rows<D>(S, dQ, nullptr);
@@ -162,115 +262,94 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dq_kernel(
   if (!find_item(S, it)) return;
   const int n = it.n;
   const size_t base = (size_t)it.bh * S.Lmax * D;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c1 = S.c1, c2 = it.c2;
+  const TrFrag<D> tr(lane);
+  const TileDma<BK, D> dma(w, lane);
+  auto Kb = [&](int i) { return lds + i * TILE; };
+  auto Vb = [&](int i) { return lds + (3 + i) * TILE; };
+  const Slice qs(Q + base, n, D), ks(K + base, n, D), vs(V + base, n, D), gs(dO + base, n, D);
 
   const int qrow = it.tile * BQ + 32 * w + l32;
   bf16x8 qf[D / 16], gf[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const size_t off = base + (size_t)qrow * D + 16 * s + 8 * hf;
-    qf[s] = as_bf16x8(qrow < n ? *(const u32x4*)(Q + off) : z);
-    gf[s] = as_bf16x8(qrow < n ? *(const u32x4*)(dO + off) : z);
-  }
-
+  load_bfrag<D>(qf, qs, qrow, hf);
+  load_bfrag<D>(gf, gs, qrow, hf);
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
 
   const int nk = (n + BK - 1) / BK;
-  TileRegs<BK, D> kr, vr;
-  kr.load(K + base, 0, n, tid);
-  vr.load(V + base, 0, n, tid);
-  kr.template store_rows<RS>(lds, tid);
-  vr.template store_rows<RS>(lds + KE, tid);
-  kr.template store_cols<TS>(lds + 2 * KE, tid);
+  dma.load(ks, 0, Kb(0));
+  dma.load(ks, BK, Kb(1));
+  dma.load(vs, 0, Vb(0));
+  vm_drain();
   __syncthreads();
+  f32x16 sA[2], sB[2];
+  zero2(sA);
+  score_steps<D>(sA, Kb(0), qf, 0, D / 16, l32, hf);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const uint16_t* Ks = lds + (kt & 1) * STAGE;
-    const uint16_t* Vs = Ks + KE;
-    const uint16_t* Kt = Ks + 2 * KE;
-    if (kt + 1 < nk) {
-      kr.load(K + base, (kt + 1) * BK, n, tid);
-      vr.load(V + base, (kt + 1) * BK, n, tid);
-    }
-    f32x16 st[2] = {(f32x16){}, (f32x16){}}, dpt[2] = {(f32x16){}, (f32x16){}};
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        st[mb] = mfma(lds_frag(Ks + (32 * mb + l32) * RS + 16 * s + 8 * hf), qf[s], st[mb]);
-        dpt[mb] = mfma(lds_frag(Vs + (32 * mb + l32) * RS + 16 * s + 8 * hf), gf[s], dpt[mb]);
-      }
-    }
-    bf16x8 dh[4], dl[4];
+  int kc = 0;
+  auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    const int k1 = next3(kc), k2 = next3(k1);
+    dma.load(ks, (j + 2) * BK, Kb(k2));
+    dma.load(vs, (j + 1) * BK, Vb((j + 1) & 1));
+    const uint16_t* Kt = Kb(kc);
+    const uint16_t* Kn = Kb(k1);
+    const uint16_t* Vc = Vb(j & 1);
+    f32x16 dp[2];
+    zero2(dp);
+    zero2(nxt);
+    score_block<D>(dp[0], Vc, gf, 0, l32, hf);
+    score_block<D>(dp[1], Vc, gf, 1, l32, hf);
+    bf16x8 dh[4], dl[4], unused_h, unused_l;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const f32x8 sv = chunk8(st[c >> 1], c & 1), dv = chunk8(dpt[c >> 1], c & 1);
-      f32x8 ds;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float p = sigmoid2(sv[t], c1, c2);
-        ds[t] = dv[t] * __builtin_fmaf(-p, p, p);  // dP * p (1 - p)
-      }
-      dh[c] = to_bf16x8(ds);
-      if (SPLIT) dl[c] = to_bf16x8(ds - to_f32x8(dh[c]));
+      if (LA) score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), l32, hf);
+      dsigmoid_chunk<SPLIT, false>(cur, dp, c, c1, c2, dh[c], dl[c], unused_h, unused_l);
+      if (c > 0) value_chunk<D, SPLIT>(acc, tr, Kt, c - 1, dh[c - 1], dl[c - 1]);
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 a = lds_frag(Kt + (32 * db + l32) * TS + 16 * c + 8 * hf);
-        acc[db] = mfma(a, dh[c], acc[db]);
-        if (SPLIT) acc[db] = mfma(a, dl[c], acc[db]);
-      }
-    }
-    if (kt + 1 < nk) {
-      uint16_t* nxt = lds + ((kt + 1) & 1) * STAGE;
-      kr.template store_rows<RS>(nxt, tid);
-      vr.template store_rows<RS>(nxt + KE, tid);
-      kr.template store_cols<TS>(nxt + 2 * KE, tid);
-    }
+    value_chunk<D, SPLIT>(acc, tr, Kt, 3, dh[3], dl[3]);
+    if (!LA) score_steps<D>(nxt, Kn, qf, 0, D / 16, l32, hf);
+    vm_drain();
     __syncthreads();
+    kc = k1;
+  };
+  int j = 0;
+  for (; j + 1 < nk; j += 2) {
+    step(j, sA, sB);
+    step(j + 1, sB, sA);
   }
+  if (j < nk) step(j, sA, sB);
 
   if (qrow < n) {
-    const float sc = S.out_scale;
+    const float scale = S.out_scale;
     uint16_t* dst = dQ + base + (size_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x8 v8;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) { v8[t] = sc * acc[db][4 * i + t]; v8[4 + t] = 0.0f; }
-        const u32x4 packed = as_u32x4(to_bf16x8(v8));
-        uint2 out = {packed[0], packed[1]};
-        *(uint2*)(dst + 32 * db + 8 * i + 4 * hf) = out;
-      }
-    }
+      for (int i = 0; i < 4; ++i) store4(dst + 32 * db + 8 * i + 4 * hf, acc[db], i, scale);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Backward, dK/dV.  Item = (b, h, 128-key tile).  Inner loop: 64-query tiles.
-// Per wave (32 keys) and query tile: S = Q . K^T (64 queries x 32 keys),
-// dP = dO . V^T, P = sigma, dS = dP * P(1-P),
-// dV^T (d x 32 keys) += dO^T . P,  dK^T += Q^T . dS.  dK = dK^T^T / sqrt(d).
-// Each workgroup owns its rows of dK and dV: one writer per row, no atomics.
+// Backward, dK/dV.  Item = (b, h, 128-key tile).  Inner loop: 64-query tiles j.
+// Per wave (32 keys): S_j = Q_j . K^T (64 queries x 32 keys), dP_j = dO_j . V^T,
+// P_j = sigma, dS_j = dP_j * P(1-P), dV^T (d x 32 keys) += dO_j^T . P_j,
+// dK^T += Q_j^T . dS_j.  Each workgroup owns its rows of dK and dV: one
+// writer per row, no atomics.
+// LDS: Q and dO in 3 stages each (tile j: transposing reads for dK, dV;
+// tile j+1: scores; tile j+2: loading).  LOOKAHEAD: S and dP of tile j+1 are
+// computed while the VALU works on tile j (two tiles of scores live);
+// without it they follow tile j's products.
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT>
-__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(
+template <int D, bool SPLIT, bool LOOKAHEAD = DkdvCfg<D>::LA>
+__global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     const Sched S) {
-  constexpr int BKV = 128, BQ = 64;
-  constexpr int RS = D + 8;   // row-major Q and dO tiles
-  constexpr int TS = BQ + 8;  // transposed Q and dO tiles
-  constexpr int RE = BQ * RS, TE = D * TS, STAGE = 2 * RE + 2 * TE;
-  __shared__ __align__(16) uint16_t lds[2 * STAGE];
+  constexpr int BKV = 128, BQ = kInner, TILE = BQ * D;
+  __shared__ __align__(16) uint16_t lds[6 * TILE];  // Q0 Q1 Q2 G0 G1 G2
 
   if ((int)blockIdx.x >= S.compute_blocks) {
     zero_padded_rows<D>(S, dK, dV);
@@ -280,112 +359,91 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(
   if (!find_item(S, it)) return;
   const int n = it.n;
   const size_t base = (size_t)it.bh * S.Lmax * D;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c1 = S.c1, c2 = it.c2;
+  const TrFrag<D> tr(lane);
+  const TileDma<BQ, D> dma(w, lane);
+  auto Qb = [&](int i) { return lds + i * TILE; };
+  auto Gb = [&](int i) { return lds + (3 + i) * TILE; };
+  const Slice qs(Q + base, n, D), ks(K + base, n, D), vs(V + base, n, D), gs(dO + base, n, D);
 
   const int krow = it.tile * BKV + 32 * w + l32;
   bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const size_t off = base + (size_t)krow * D + 16 * s + 8 * hf;
-    kf[s] = as_bf16x8(krow < n ? *(const u32x4*)(K + off) : z);
-    vf[s] = as_bf16x8(krow < n ? *(const u32x4*)(V + off) : z);
-  }
-
+  load_bfrag<D>(kf, ks, krow, hf);
+  load_bfrag<D>(vf, vs, krow, hf);
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) { dk[i] = (f32x16){}; dv[i] = (f32x16){}; }
-
-  const int nq = (n + BQ - 1) / BQ;
-  TileRegs<BQ, D> qr, gr;
-  qr.load(Q + base, 0, n, tid);
-  gr.load(dO + base, 0, n, tid);
-  qr.template store_rows<RS>(lds, tid);
-  gr.template store_rows<RS>(lds + RE, tid);
-  qr.template store_cols<TS>(lds + 2 * RE, tid);
-  gr.template store_cols<TS>(lds + 2 * RE + TE, tid);
-  __syncthreads();
-
-  for (int qt = 0; qt < nq; ++qt) {
-    const uint16_t* Qs = lds + (qt & 1) * STAGE;
-    const uint16_t* Gs = Qs + RE;
-    const uint16_t* Qt = Qs + 2 * RE;
-    const uint16_t* Gt = Qt + TE;
-    if (qt + 1 < nq) {
-      qr.load(Q + base, (qt + 1) * BQ, n, tid);
-      gr.load(dO + base, (qt + 1) * BQ, n, tid);
-    }
-    f32x16 sc[2] = {(f32x16){}, (f32x16){}}, dp[2] = {(f32x16){}, (f32x16){}};
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        sc[mb] = mfma(lds_frag(Qs + (32 * mb + l32) * RS + 16 * s + 8 * hf), kf[s], sc[mb]);
-        dp[mb] = mfma(lds_frag(Gs + (32 * mb + l32) * RS + 16 * s + 8 * hf), vf[s], dp[mb]);
-      }
-    }
-    bf16x8 ph[4], pl[4], dh[4], dl[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const f32x8 sv = chunk8(sc[c >> 1], c & 1), gv = chunk8(dp[c >> 1], c & 1);
-      f32x8 p8, ds;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float p = sigmoid2(sv[t], c1, c2);
-        p8[t] = p;
-        ds[t] = gv[t] * __builtin_fmaf(-p, p, p);
-      }
-      ph[c] = to_bf16x8(p8);
-      dh[c] = to_bf16x8(ds);
-      if (SPLIT) {
-        pl[c] = to_bf16x8(p8 - to_f32x8(ph[c]));
-        dl[c] = to_bf16x8(ds - to_f32x8(dh[c]));
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 ag = lds_frag(Gt + (32 * db + l32) * TS + 16 * c + 8 * hf);
-        dv[db] = mfma(ag, ph[c], dv[db]);
-        if (SPLIT) dv[db] = mfma(ag, pl[c], dv[db]);
-        const bf16x8 aq = lds_frag(Qt + (32 * db + l32) * TS + 16 * c + 8 * hf);
-        dk[db] = mfma(aq, dh[c], dk[db]);
-        if (SPLIT) dk[db] = mfma(aq, dl[c], dk[db]);
-      }
-    }
-    if (qt + 1 < nq) {
-      uint16_t* nxt = lds + ((qt + 1) & 1) * STAGE;
-      qr.template store_rows<RS>(nxt, tid);
-      gr.template store_rows<RS>(nxt + RE, tid);
-      qr.template store_cols<TS>(nxt + 2 * RE, tid);
-      gr.template store_cols<TS>(nxt + 2 * RE + TE, tid);
-    }
-    __syncthreads();
+  for (int i = 0; i < D / 32; ++i) {
+    dk[i] = (f32x16){};
+    dv[i] = (f32x16){};
   }
 
+  const int nq = (n + BQ - 1) / BQ;
+  dma.load(qs, 0, Qb(0));
+  dma.load(gs, 0, Gb(0));
+  dma.load(qs, BQ, Qb(1));
+  dma.load(gs, BQ, Gb(1));
+  vm_drain();
+  __syncthreads();
+  f32x16 sA[2], dA[2], sB[2], dB[2];
+  zero2(sA);
+  zero2(dA);
+  score_steps<D>(sA, Qb(0), kf, 0, D / 16, l32, hf);
+  score_steps<D>(dA, Gb(0), vf, 0, D / 16, l32, hf);
+
+  int kc = 0;
+  auto step = [&](int j, f32x16 (&cs)[2], f32x16 (&cd)[2], f32x16 (&ns)[2], f32x16 (&nd)[2]) {
+    const int k1 = next3(kc), k2 = next3(k1);
+    dma.load(qs, (j + 2) * BQ, Qb(k2));
+    dma.load(gs, (j + 2) * BQ, Gb(k2));
+    const uint16_t* Qn = Qb(k1);
+    const uint16_t* Gn = Gb(k1);
+    const uint16_t* Qt = Qb(kc);
+    const uint16_t* Gt = Gb(kc);
+    zero2(ns);
+    zero2(nd);
+    bf16x8 dh[4], dl[4], ph[4], pl[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (LOOKAHEAD) {
+        score_steps<D>(ns, Qn, kf, c * (D / 64), (c + 1) * (D / 64), l32, hf);
+        score_steps<D>(nd, Gn, vf, c * (D / 64), (c + 1) * (D / 64), l32, hf);
+      }
+      dsigmoid_chunk<SPLIT, true>(cs, cd, c, c1, c2, dh[c], dl[c], ph[c], pl[c]);
+      if (c > 0) {
+        value_chunk<D, SPLIT>(dv, tr, Gt, c - 1, ph[c - 1], pl[c - 1]);
+        value_chunk<D, SPLIT>(dk, tr, Qt, c - 1, dh[c - 1], dl[c - 1]);
+      }
+    }
+    value_chunk<D, SPLIT>(dv, tr, Gt, 3, ph[3], pl[3]);
+    value_chunk<D, SPLIT>(dk, tr, Qt, 3, dh[3], dl[3]);
+    if (!LOOKAHEAD) {
+      score_steps<D>(ns, Qn, kf, 0, D / 16, l32, hf);
+      score_steps<D>(nd, Gn, vf, 0, D / 16, l32, hf);
+    }
+    vm_drain();
+    __syncthreads();
+    kc = k1;
+  };
+  int j = 0;
+  for (; j + 1 < nq; j += 2) {
+    step(j, sA, dA, sB, dB);
+    step(j + 1, sB, dB, sA, dA);
+  }
+  if (j < nq) step(j, sA, dA, sB, dB);
+
   if (krow < n) {
-    const float sc = S.out_scale;
+    const float scale = S.out_scale;
     uint16_t* dstk = dK + base + (size_t)krow * D;
     uint16_t* dstv = dV + base + (size_t)krow * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        f32x8 k8, v8;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          k8[t] = sc * dk[db][4 * i + t];
-          v8[t] = dv[db][4 * i + t];
-          k8[4 + t] = 0.0f;
-          v8[4 + t] = 0.0f;
-        }
-        const u32x4 pk = as_u32x4(to_bf16x8(k8)), pv = as_u32x4(to_bf16x8(v8));
-        *(uint2*)(dstk + 32 * db + 8 * i + 4 * hf) = (uint2){pk[0], pk[1]};
-        *(uint2*)(dstv + 32 * db + 8 * i + 4 * hf) = (uint2){pv[0], pv[1]};
+        store4(dstk + 32 * db + 8 * i + 4 * hf, dk[db], i, scale);
+        store4(dstv + 32 * db + 8 * i + 4 * hf, dv[db], i, 1.0f);
       }
-    }
   }
 }
 
@@ -413,7 +471,11 @@ hipError_t launch_dkdv_t(const Launch& L, const void* q, const void* k, const vo
   return hipGetLastError();
 }
 
-}  // namespace
+}  // namespace kern
+
+using kern::launch_fwd_t;
+using kern::launch_dq_t;
+using kern::launch_dkdv_t;
 
 hipError_t launch_fwd(int d, bool split, const Launch& L, const void* q, const void* k, const void* v, void* o,
                       hipStream_t st) {
