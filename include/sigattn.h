@@ -54,7 +54,8 @@ extern "C" {
 typedef enum sigattn_status {
   SIGATTN_OK = 0,
   SIGATTN_ERR_NULL = 1,      /* args, a tensor pointer or seqlens is NULL               */
-  SIGATTN_ERR_SHAPE = 2,     /* B, H or Lmax < 1, d not 64 or 128, or sizes overflow    */
+  SIGATTN_ERR_SHAPE = 2,     /* B, H or Lmax < 1, d not 64 or 128, sizes overflow, or
+                                (Lmax + 256) * d * 2 > 2^31 - 1 (32-bit slice offsets)  */
   SIGATTN_ERR_SEQLEN = 3,    /* some seqlens[b] outside [0, Lmax]                       */
   SIGATTN_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned                 */
   SIGATTN_ERR_ALIAS = 5,     /* an output overlaps an input or another output           */

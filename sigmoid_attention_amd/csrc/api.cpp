@@ -29,13 +29,18 @@ sigattn_status tile_rows(int32_t pass, int32_t* outer, int32_t* inner) {
 }
 
 // Shape, lengths, bias and precision (no pointers).
+constexpr int64_t kLmaxSlack = 256;  // rows a tile may reach past Lmax, with margin
+
 sigattn_status check_args(const sigattn_args* a) {
   if (!a) return SIGATTN_ERR_NULL;
   if (a->B < 1 || a->H < 1 || a->Lmax < 1 || (a->d != 64 && a->d != 128)) return SIGATTN_ERR_SHAPE;
   // Element count must fit comfortably in 62 bits; B * H must fit the
-  // schedule's 32-bit head index.
+  // schedule's 32-bit head index; byte offsets within one (sequence, head)
+  // slice, up to one tile past Lmax, must fit the kernels' 32-bit buffer
+  // offsets (Lmax <= 4,194,048 at d = 128, 8,388,352 at d = 64).
   const double elems = (double)a->B * a->H * a->Lmax * a->d;
   if (elems > 4.0e18 || (int64_t)a->B * a->H > INT32_MAX) return SIGATTN_ERR_SHAPE;
+  if (((int64_t)a->Lmax + kLmaxSlack) * a->d * 2 > INT32_MAX) return SIGATTN_ERR_SHAPE;
   if (!a->seqlens) return SIGATTN_ERR_NULL;
   for (int32_t b = 0; b < a->B; ++b)
     if (a->seqlens[b] < 0 || a->seqlens[b] > a->Lmax) return SIGATTN_ERR_SEQLEN;

@@ -38,35 +38,14 @@ namespace kern {
 constexpr int kThreads = 256;
 constexpr int kInner = 64;  // rows per inner tile
 
-// Schedule per kernel and head dim: LA = compute the next tile's scores while
-// the VALU works on this tile (two tiles of scores live in registers), and
-// OCC = waves per SIMD the register budget is sized for.  Measured on MI355X:
-// a second resident workgroup per CU overlaps MFMA and VALU better than the
-// in-wave lookahead where both do not fit together.
-#ifndef SIGATTN_FWD64_LA
-#define SIGATTN_FWD64_LA 1
-#endif
-#ifndef SIGATTN_FWD64_OCC
-#define SIGATTN_FWD64_OCC 2
-#endif
-#ifndef SIGATTN_DQ64_LA
-#define SIGATTN_DQ64_LA 1
-#endif
-#ifndef SIGATTN_DQ64_OCC
-#define SIGATTN_DQ64_OCC 2
-#endif
-#ifndef SIGATTN_INTERLEAVE
-#define SIGATTN_INTERLEAVE 0
-#endif
-#ifndef SIGATTN_DKDV64_LA
-#define SIGATTN_DKDV64_LA 0
-#endif
-#ifndef SIGATTN_DKDV64_OCC
-#define SIGATTN_DKDV64_OCC 2
-#endif
-template <int D> struct FwdCfg { static constexpr bool LA = D == 64 ? SIGATTN_FWD64_LA : true; static constexpr int OCC = D == 64 ? SIGATTN_FWD64_OCC : 1; };
-template <int D> struct DqCfg { static constexpr bool LA = D == 64 ? SIGATTN_DQ64_LA : true; static constexpr int OCC = D == 64 ? SIGATTN_DQ64_OCC : 1; };
-template <int D> struct DkdvCfg { static constexpr bool LA = D == 64 ? SIGATTN_DKDV64_LA : false; static constexpr int OCC = D == 64 ? SIGATTN_DKDV64_OCC : 1; };
+// Schedule per kernel and head dim (measured on MI355X, same-run A/B):
+// LA = compute the next tile's scores while the VALU works on this tile (two
+// tiles of scores live in registers); OCC = waves per SIMD the register
+// budget is sized for.  At d = 64 more resident waves beat in-wave lookahead
+// for the forward and dK/dV; dQ keeps the lookahead of its scores.
+template <int D> struct FwdCfg { static constexpr bool LA = D != 64; static constexpr int OCC = D == 64 ? 4 : 1; };
+template <int D> struct DqCfg { static constexpr bool LA = true; static constexpr int OCC = D == 64 ? 2 : 1; };
+template <int D> struct DkdvCfg { static constexpr int OCC = D == 64 ? 2 : 1; };
 
 // sigma of the eight score values of K-chunk c, rounded to bf16 (hi) and, in
 // split precision, the bf16 remainder (lo).
@@ -143,6 +122,52 @@ __device__ __forceinline__ void value_chunk(f32x16 (&acc)[D / 32], const TrFrag<
   }
 }
 
+// The same, with the A fragments read beforehand (see read_value_frags).
+template <int D, bool SPLIT>
+__device__ __forceinline__ void value_chunk_pre(f32x16 (&acc)[D / 32], const bf16x8 (&a)[D / 32], const bf16x8& bh,
+                                                const bf16x8& bl) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    acc[db] = mfma(a[db], bh, acc[db]);
+    if (SPLIT) acc[db] = mfma(a[db], bl, acc[db]);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void read_value_frags(bf16x8 (&a)[D / 32], const TrFrag<D>& tr, const uint16_t* tile,
+                                                 int c) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) a[db] = tr.read(tile, db, c);
+}
+
+// Keeps the compiler from moving instructions across this point, so LDS
+// reads issued before a block of VALU work stay there and their latency is
+// covered by that work.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Score product over all K-steps with the A fragments of step s+1 read while
+// step s multiplies (one step of read-ahead).
+template <int D>
+__device__ __forceinline__ void score_pipelined(f32x16 (&acc)[2], const uint16_t* tile, const bf16x8 (&bf)[D / 16],
+                                                int l32, int hf) {
+  bf16x8 a0[2], a1[2];
+  a0[0] = frag_read<D>(tile, 0, 0, l32, hf);
+  a0[1] = frag_read<D>(tile, 1, 0, l32, hf);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    if (s + 1 < D / 16) {
+      a1[0] = frag_read<D>(tile, 0, s + 1, l32, hf);
+      a1[1] = frag_read<D>(tile, 1, s + 1, l32, hf);
+    }
+    sched_fence();
+    acc[0] = mfma(a0[0], bf[s], acc[0]);
+    acc[1] = mfma(a0[1], bf[s], acc[1]);
+    sched_fence();
+    a0[0] = a1[0];
+    a0[1] = a1[1];
+  }
+}
+
 __device__ __forceinline__ void zero2(f32x16 (&a)[2]) {
   a[0] = (f32x16){};
   a[1] = (f32x16){};
@@ -212,14 +237,23 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
     const uint16_t* Vc = Vb(j & 1);
     zero2(nxt);
     bf16x8 ph[4], pl[4];
+    if (LA) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (LA) score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), l32, hf);  // MFMA: tile j+1
-      sigmoid_chunk<SPLIT>(cur, c, c1, c2, ph[c], pl[c]);                              // VALU: tile j
-      if (c > 0) value_chunk<D, SPLIT>(acc, tr, Vc, c - 1, ph[c - 1], pl[c - 1]);
+      for (int c = 0; c < 4; ++c) {
+        score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), l32, hf);  // MFMA: tile j+1
+        sigmoid_chunk<SPLIT>(cur, c, c1, c2, ph[c], pl[c]);                      // VALU: tile j
+        if (c > 0) value_chunk<D, SPLIT>(acc, tr, Vc, c - 1, ph[c - 1], pl[c - 1]);
+      }
+      value_chunk<D, SPLIT>(acc, tr, Vc, 3, ph[3], pl[3]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sigmoid_chunk<SPLIT>(cur, c, c1, c2, ph[c], pl[c]);
+        if (c > 0) value_chunk<D, SPLIT>(acc, tr, Vc, c - 1, ph[c - 1], pl[c - 1]);
+      }
+      value_chunk<D, SPLIT>(acc, tr, Vc, 3, ph[3], pl[3]);
+      score_steps<D>(nxt, Kn, qf, 0, D / 16, l32, hf);
     }
-    value_chunk<D, SPLIT>(acc, tr, Vc, 3, ph[3], pl[3]);
-    if (!LA) score_steps<D>(nxt, Kn, qf, 0, D / 16, l32, hf);
     vm_drain();
     __syncthreads();
     kc = k1;
@@ -247,7 +281,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
 // LDS: K in 3 stages (tile j: transposing reads for dQ; tile j+1: scores;
 // tile j+2: loading), V in 2 stages (tile j: dP; tile j+1: loading).
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT, bool LA = DqCfg<D>::LA>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, const Sched S) {
@@ -300,17 +334,15 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
     f32x16 dp[2];
     zero2(dp);
     zero2(nxt);
-    score_block<D>(dp[0], Vc, gf, 0, l32, hf);
-    score_block<D>(dp[1], Vc, gf, 1, l32, hf);
+    score_pipelined<D>(dp, Vc, gf, l32, hf);
     bf16x8 dh[4], dl[4], unused_h, unused_l;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      if (LA) score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), l32, hf);
+      score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), l32, hf);  // MFMA: tile j+1
       dsigmoid_chunk<SPLIT, false>(cur, dp, c, c1, c2, dh[c], dl[c], unused_h, unused_l);
       if (c > 0) value_chunk<D, SPLIT>(acc, tr, Kt, c - 1, dh[c - 1], dl[c - 1]);
     }
     value_chunk<D, SPLIT>(acc, tr, Kt, 3, dh[3], dl[3]);
-    if (!LA) score_steps<D>(nxt, Kn, qf, 0, D / 16, l32, hf);
     vm_drain();
     __syncthreads();
     kc = k1;
@@ -339,11 +371,12 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
 // dK^T += Q_j^T . dS_j.  Each workgroup owns its rows of dK and dV: one
 // writer per row, no atomics.
 // LDS: Q and dO in 3 stages each (tile j: transposing reads for dK, dV;
-// tile j+1: scores; tile j+2: loading).  LOOKAHEAD: S and dP of tile j+1 are
-// computed while the VALU works on tile j (two tiles of scores live);
-// without it they follow tile j's products.
+// tile j+1: scores; tile j+2: loading).  Per 16-row chunk the transposing
+// reads are issued before the VALU block that computes P and dS, so their
+// latency is covered; the next tile's S and dP follow, with the fragments of
+// each K-step read one step ahead.
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT, bool LOOKAHEAD = DkdvCfg<D>::LA>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
@@ -404,23 +437,22 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     zero2(ns);
     zero2(nd);
     bf16x8 dh[4], dl[4], ph[4], pl[4];
+    {
+      // Per chunk: issue the transposing reads of dO^T and Q^T, evaluate
+      // P and dS on the VALU while they land, then multiply.
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (LOOKAHEAD) {
-        score_steps<D>(ns, Qn, kf, c * (D / 64), (c + 1) * (D / 64), l32, hf);
-        score_steps<D>(nd, Gn, vf, c * (D / 64), (c + 1) * (D / 64), l32, hf);
+      for (int c = 0; c < 4; ++c) {
+        bf16x8 ag[D / 32], aq[D / 32];
+        read_value_frags<D>(ag, tr, Gt, c);
+        read_value_frags<D>(aq, tr, Qt, c);
+        sched_fence();
+        dsigmoid_chunk<SPLIT, true>(cs, cd, c, c1, c2, dh[c], dl[c], ph[c], pl[c]);
+        sched_fence();
+        value_chunk_pre<D, SPLIT>(dv, ag, ph[c], pl[c]);
+        value_chunk_pre<D, SPLIT>(dk, aq, dh[c], dl[c]);
       }
-      dsigmoid_chunk<SPLIT, true>(cs, cd, c, c1, c2, dh[c], dl[c], ph[c], pl[c]);
-      if (c > 0) {
-        value_chunk<D, SPLIT>(dv, tr, Gt, c - 1, ph[c - 1], pl[c - 1]);
-        value_chunk<D, SPLIT>(dk, tr, Qt, c - 1, dh[c - 1], dl[c - 1]);
-      }
-    }
-    value_chunk<D, SPLIT>(dv, tr, Gt, 3, ph[3], pl[3]);
-    value_chunk<D, SPLIT>(dk, tr, Qt, 3, dh[3], dl[3]);
-    if (!LOOKAHEAD) {
-      score_steps<D>(ns, Qn, kf, 0, D / 16, l32, hf);
-      score_steps<D>(nd, Gn, vf, 0, D / 16, l32, hf);
+      score_pipelined<D>(ns, Qn, kf, l32, hf);
+      score_pipelined<D>(nd, Gn, vf, l32, hf);
     }
     vm_drain();
     __syncthreads();

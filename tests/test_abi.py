@@ -88,6 +88,22 @@ def test_size_overflow_rejected():
     assert fwd(a) == SHAPE
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_lmax_bound_for_32bit_slice_offsets(d):
+    # largest accepted Lmax: (Lmax + 256) * d * 2 <= 2^31 - 1
+    top = (2**31 - 1) // (2 * d) - 256
+    a, keep = sa.make_args(1, 1, top + 1, d, [0])
+    for f in (fwd, dq, dkdv):
+        assert f(a) == SHAPE
+    with pytest.raises(sa.SigattnError) as e:
+        sa.plan_stats(1, 1, top + 1, d, [0])
+    assert e.value.code == SHAPE
+    assert sa.plan_stats(1, 1, top, d, [0])[0] == 0  # one empty sequence: no work
+    a, keep = sa.make_args(1, 1, top, d, [0])
+    # passes the shape check; the (fake) pointers then fail alignment
+    assert fwd(a, q=P[0] + 8) == ALIGN
+
+
 @pytest.mark.parametrize("lens", [(129, 77), (-1, 77), (128, 1 << 30)])
 def test_bad_lengths(lens):
     a, keep = args(lens=lens)
