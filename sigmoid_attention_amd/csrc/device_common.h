@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "plan.h"
 
 namespace sigattn {
@@ -43,6 +45,14 @@ __device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(
 // exponential (v_exp_f32) and reciprocal (v_rcp_f32), each about 1 ulp.  For
 // t -> +inf, 2^t = inf and the reciprocal gives 0; for t -> -inf it gives 1;
 // no NaN arises from finite scores.
+// The score scale c1 for head dim D, a compile-time literal (so the scale
+// and bias take one VOP2 fmamk instruction per score).
+template <int D>
+__device__ __forceinline__ constexpr float score_c1() {
+  static_assert(D == 64 || D == 128, "head dim");
+  return (float)(-1.4426950408889634074 / (D == 64 ? 8.0 : 11.313708498984760390));
+}
+
 __device__ __forceinline__ float sigmoid2(float score, float c1, float c2) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(score, c1, c2)));
 }
@@ -110,21 +120,21 @@ struct Slice {
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Direct global -> LDS loading of a ROWS x D tile (buffer_load_dwordx4 ... lds).
-// Each of the 4 waves issues NI instructions per tile; instruction i of wave w
-// fills the 1 KB block b = 4i + w of the tile, lane L writing slot 64b + L.
+// Each of the NW waves issues NI instructions per tile; instruction i of wave w
+// fills the 1 KB block b = NW*i + w of the tile, lane L writing slot 64b + L.
 // The per-lane source offset inverts the tile layout, so the 8 lanes of one
 // row read that row's 128 contiguous bytes (coalesced).  Completion is
 // tracked by vmcnt: wait (vm_drain) before the barrier that publishes a tile.
-template <int ROWS, int D>
+template <int ROWS, int D, int NW = 4>
 struct TileDma {
-  static constexpr int NI = ROWS * D * 2 / (4 * 1024);
-  static_assert(NI >= 1 && NI * 4 * 1024 == ROWS * D * 2, "tile must split into 1 KB blocks over 4 waves");
+  static constexpr int NI = ROWS * D * 2 / (NW * 1024);
+  static_assert(NI >= 1 && NI * NW * 1024 == ROWS * D * 2, "tile must split into 1 KB blocks over the waves");
   int src[NI];  // element offset within the tile's rows
   int dst[NI];  // element offset of this wave's block within the tile (wave-uniform)
   __device__ __forceinline__ TileDma(int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int blk = 4 * i + wave;
+      const int blk = NW * i + wave;
       const int t = 64 * blk + lane;  // 16-byte slot filled by this lane
       const int r = t / (D / 8);
       const int g = (t % (D / 8)) ^ tile_xor<D>(r);
@@ -171,36 +181,45 @@ __device__ __forceinline__ bf16x4 lds_tr4(const uint16_t* p) {
 // Source lane j (of each 16) addresses row 16c + 4hf + j/4 (+8) at columns
 // 32db + 16gq + 4(j%4) .. +3; destination lane i then holds column
 // 32db + 16gq + i of those four rows.
+// X(r) depends on bits 0..3 of r only, so the address of row 16c + x is that
+// of row x plus 16c full rows: the lane offsets are computed once (off) and
+// the chunk, tile and stage enter as compile-time immediates.
 template <int D>
 struct TrFrag {
-  int row_lane;  // 4*hf + (j >> 2)
-  int chunk;     // this lane's 4-column chunk within a 32-column block: 4*gq + (j & 3)
+  int off[D / 32][2];  // element offsets of rows 4hf + j/4 (+8) for block db
   __device__ __forceinline__ TrFrag(int lane) {
     const int j = lane & 15, gq = (lane >> 4) & 1, hf = lane >> 5;
-    row_lane = 4 * hf + (j >> 2);
-    chunk = 4 * gq + (j & 3);
-  }
-  __device__ __forceinline__ int offset(int r, int db) const {
-    const int ch = 8 * db + chunk;  // 4-column chunk index
-    return 8 * tile_slot<D>(r, ch >> 1) + 4 * (ch & 1);
+    const int row_lane = 4 * hf + (j >> 2);
+    const int chunk = 4 * gq + (j & 3);  // this lane's 4-column chunk within a 32-column block
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ch = 8 * db + chunk;
+        off[db][h] = 8 * tile_slot<D>(row_lane + 8 * h, ch >> 1) + 4 * (ch & 1);
+      }
   }
   __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int db, int c) const {
-    const int r = 16 * c + row_lane;
-    const bf16x4 lo = lds_tr4(tile + offset(r, db));
-    const bf16x4 hi = lds_tr4(tile + offset(r + 8, db));
+    const bf16x4 lo = lds_tr4(tile + 16 * c * D + off[db][0]);
+    const bf16x4 hi = lds_tr4(tile + 16 * c * D + off[db][1]);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 };
 
 // A fragment (rows = tile rows 32mb .. 32mb+31, K-slots = head dim
-// 16s + 8hf .. +7) with a 16-byte read.
+// 16s + 8hf .. +7) with a 16-byte read.  As above, the lane offsets of rows
+// l32 are computed once and the row block enters as an immediate.
 template <int D>
-__device__ __forceinline__ bf16x8 frag_read(const uint16_t* tile, int mb, int s, int l32, int hf) {
-  return as_bf16x8(*(const u32x4*)(tile + 8 * tile_slot<D>(32 * mb + l32, 2 * s + hf)));
-}
-
-// 16-byte LDS read of an A fragment.
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) { return as_bf16x8(*(const u32x4*)p); }
+struct FragAddr {
+  int off[D / 16];
+  __device__ __forceinline__ FragAddr(int l32, int hf) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) off[s] = 8 * tile_slot<D>(l32, 2 * s + hf);
+  }
+  __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int mb, int s) const {
+    return as_bf16x8(*(const u32x4*)(tile + 32 * mb * D + off[s]));
+  }
+};
 
 // Trailing workgroups (blockIdx.x >= compute_blocks) write the padded rows
 // n_b..Lmax-1 of one or two outputs as 0 with 16-byte stores; the compute

@@ -49,25 +49,24 @@ template <int D> struct DkdvCfg { static constexpr int OCC = D == 64 ? 2 : 1; };
 
 // sigma of the eight score values of K-chunk c, rounded to bf16 (hi) and, in
 // split precision, the bf16 remainder (lo).
-template <bool SPLIT>
-__device__ __forceinline__ void sigmoid_chunk(const f32x16 (&sc)[2], int c, float c1, float c2, bf16x8& hi,
-                                              bf16x8& lo) {
+template <int D, bool SPLIT>
+__device__ __forceinline__ void sigmoid_chunk(const f32x16 (&sc)[2], int c, float c2, bf16x8& hi, bf16x8& lo) {
   f32x8 p = chunk8(sc[c >> 1], c & 1);
 #pragma unroll
-  for (int t = 0; t < 8; ++t) p[t] = sigmoid2(p[t], c1, c2);
+  for (int t = 0; t < 8; ++t) p[t] = sigmoid2(p[t], score_c1<D>(), c2);
   hi = to_bf16x8(p);
   if (SPLIT) lo = to_bf16x8(p - to_f32x8(hi));
 }
 
 // dS = dP * sigma * (1 - sigma) for K-chunk c (and optionally sigma itself).
-template <bool SPLIT, bool WANT_P>
-__device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[2], const f32x16 (&dp)[2], int c, float c1,
-                                               float c2, bf16x8& dh, bf16x8& dl, bf16x8& ph, bf16x8& pl) {
+template <int D, bool SPLIT, bool WANT_P, int NB>
+__device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[NB], const f32x16 (&dp)[NB], int c, float c2,
+                                               bf16x8& dh, bf16x8& dl, bf16x8& ph, bf16x8& pl) {
   const f32x8 sv = chunk8(sc[c >> 1], c & 1), gv = chunk8(dp[c >> 1], c & 1);
   f32x8 p8, ds;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const float p = sigmoid2(sv[t], c1, c2);
+    const float p = sigmoid2(sv[t], score_c1<D>(), c2);
     p8[t] = p;
     ds[t] = gv[t] * __builtin_fmaf(-p, p, p);  // dP * p (1 - p)
   }
@@ -96,18 +95,18 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x16& acc, int i, 
 // 32mb .. 32mb+31; K-steps s cover d = 16s .. 16s+15.
 template <int D>
 __device__ __forceinline__ void score_steps(f32x16 (&acc)[2], const uint16_t* tile, const bf16x8 (&bf)[D / 16],
-                                            int s0, int s1, int l32, int hf) {
+                                            int s0, int s1, const FragAddr<D>& fa) {
 #pragma unroll
   for (int s = s0; s < s1; ++s)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) acc[mb] = mfma(frag_read<D>(tile, mb, s, l32, hf), bf[s], acc[mb]);
+    for (int mb = 0; mb < 2; ++mb) acc[mb] = mfma(fa.read(tile, mb, s), bf[s], acc[mb]);
 }
 
 template <int D>
 __device__ __forceinline__ void score_block(f32x16& acc, const uint16_t* tile, const bf16x8 (&bf)[D / 16], int mb,
-                                            int l32, int hf) {
+                                            const FragAddr<D>& fa) {
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) acc = mfma(frag_read<D>(tile, mb, s, l32, hf), bf[s], acc);
+  for (int s = 0; s < D / 16; ++s) acc = mfma(fa.read(tile, mb, s), bf[s], acc);
 }
 
 // Second-product step for K-chunk c: acc[db] += A(tile rows d, K-chunk c) . B.
@@ -149,15 +148,15 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // step s multiplies (one step of read-ahead).
 template <int D>
 __device__ __forceinline__ void score_pipelined(f32x16 (&acc)[2], const uint16_t* tile, const bf16x8 (&bf)[D / 16],
-                                                int l32, int hf) {
+                                                const FragAddr<D>& fa) {
   bf16x8 a0[2], a1[2];
-  a0[0] = frag_read<D>(tile, 0, 0, l32, hf);
-  a0[1] = frag_read<D>(tile, 1, 0, l32, hf);
+  a0[0] = fa.read(tile, 0, 0);
+  a0[1] = fa.read(tile, 1, 0);
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     if (s + 1 < D / 16) {
-      a1[0] = frag_read<D>(tile, 0, s + 1, l32, hf);
-      a1[1] = frag_read<D>(tile, 1, s + 1, l32, hf);
+      a1[0] = fa.read(tile, 0, s + 1);
+      a1[1] = fa.read(tile, 1, s + 1);
     }
     sched_fence();
     acc[0] = mfma(a0[0], bf[s], acc[0]);
@@ -173,8 +172,42 @@ __device__ __forceinline__ void zero2(f32x16 (&a)[2]) {
   a[1] = (f32x16){};
 }
 
-// Rotating index over 3 LDS stages.
-__device__ __forceinline__ int next3(int i) { return i == 2 ? 0 : i + 1; }
+// Inner loops are unrolled six times (the period of the 3-stage LDS ring and
+// of the 2-way register ping-pong), so every LDS address is a lane offset
+// plus a compile-time immediate.  Phase<P> is the step index modulo 6.
+template <int P>
+using Phase = std::integral_constant<int, P>;
+
+template <int P, class T>
+__device__ __forceinline__ T& pick(T& a, T& b) {
+  if constexpr (P % 2 == 0) return a;
+  else return b;
+}
+
+// Runs step(Phase<j % 6>, j) for j = 0 .. n-1 (n >= 1).
+template <class Step>
+__device__ __forceinline__ void run_steps(int n, Step&& step) {
+  for (int j = 0;;) {
+    step(Phase<0>{}, j);
+    if (++j == n) break;
+    sched_fence();
+    step(Phase<1>{}, j);
+    if (++j == n) break;
+    sched_fence();
+    step(Phase<2>{}, j);
+    if (++j == n) break;
+    sched_fence();
+    step(Phase<3>{}, j);
+    if (++j == n) break;
+    sched_fence();
+    step(Phase<4>{}, j);
+    if (++j == n) break;
+    sched_fence();
+    step(Phase<5>{}, j);
+    if (++j == n) break;
+    sched_fence();
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Forward.  Item = (b, h, 128-query tile).  Inner loop: 64-key tiles j.
@@ -204,8 +237,9 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
   const size_t base = (size_t)it.bh * S.Lmax * D;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const float c1 = S.c1, c2 = it.c2;
+  const float c2 = it.c2;
   const TrFrag<D> tr(lane);
+  const FragAddr<D> fa(l32, hf);
   const TileDma<BK, D> dma(w, lane);
   auto Kb = [&](int i) { return lds + i * TILE; };
   auto Vb = [&](int i) { return lds + (3 + i) * TILE; };
@@ -226,44 +260,40 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
   __syncthreads();
   f32x16 sA[2], sB[2];
   zero2(sA);
-  score_steps<D>(sA, Kb(0), qf, 0, D / 16, l32, hf);
+  score_steps<D>(sA, Kb(0), qf, 0, D / 16, fa);
 
-  int kc = 0;  // K stage of tile j
-  auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    const int k1 = next3(kc), k2 = next3(k1);
-    dma.load(ks, (j + 2) * BK, Kb(k2));       // stage of tile j-1: free since the last barrier
-    dma.load(vs, (j + 1) * BK, Vb((j + 1) & 1));
+  auto step = [&](auto phase, int j) {
+    constexpr int P = decltype(phase)::value;
+    constexpr int k1 = (P + 1) % 3, k2 = (P + 2) % 3;  // K stages of tiles j+1, j+2
+    f32x16(&cur)[2] = pick<P>(sA, sB);
+    f32x16(&nxt)[2] = pick<P + 1>(sA, sB);
+    dma.load(ks, (j + 2) * BK, Kb(k2));        // stage of tile j-1: free since the last barrier
+    dma.load(vs, (j + 1) * BK, Vb((P + 1) % 2));
     const uint16_t* Kn = Kb(k1);
-    const uint16_t* Vc = Vb(j & 1);
+    const uint16_t* Vc = Vb(P % 2);
     zero2(nxt);
     bf16x8 ph[4], pl[4];
     if (LA) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), l32, hf);  // MFMA: tile j+1
-        sigmoid_chunk<SPLIT>(cur, c, c1, c2, ph[c], pl[c]);                      // VALU: tile j
+        score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), fa);  // MFMA: tile j+1
+        sigmoid_chunk<D, SPLIT>(cur, c, c2, ph[c], pl[c]);                       // VALU: tile j
         if (c > 0) value_chunk<D, SPLIT>(acc, tr, Vc, c - 1, ph[c - 1], pl[c - 1]);
       }
       value_chunk<D, SPLIT>(acc, tr, Vc, 3, ph[3], pl[3]);
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        sigmoid_chunk<SPLIT>(cur, c, c1, c2, ph[c], pl[c]);
+        sigmoid_chunk<D, SPLIT>(cur, c, c2, ph[c], pl[c]);
         if (c > 0) value_chunk<D, SPLIT>(acc, tr, Vc, c - 1, ph[c - 1], pl[c - 1]);
       }
       value_chunk<D, SPLIT>(acc, tr, Vc, 3, ph[3], pl[3]);
-      score_steps<D>(nxt, Kn, qf, 0, D / 16, l32, hf);
+      score_steps<D>(nxt, Kn, qf, 0, D / 16, fa);
     }
     vm_drain();
     __syncthreads();
-    kc = k1;
   };
-  int j = 0;
-  for (; j + 1 < nk; j += 2) {
-    step(j, sA, sB);
-    step(j + 1, sB, sA);
-  }
-  if (j < nk) step(j, sA, sB);
+  run_steps(nk, step);
 
   if (qrow < n) {
     uint16_t* dst = O + base + (size_t)qrow * D;
@@ -298,8 +328,9 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
   const size_t base = (size_t)it.bh * S.Lmax * D;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const float c1 = S.c1, c2 = it.c2;
+  const float c2 = it.c2;
   const TrFrag<D> tr(lane);
+  const FragAddr<D> fa(l32, hf);
   const TileDma<BK, D> dma(w, lane);
   auto Kb = [&](int i) { return lds + i * TILE; };
   auto Vb = [&](int i) { return lds + (3 + i) * TILE; };
@@ -321,38 +352,34 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
   __syncthreads();
   f32x16 sA[2], sB[2];
   zero2(sA);
-  score_steps<D>(sA, Kb(0), qf, 0, D / 16, l32, hf);
+  score_steps<D>(sA, Kb(0), qf, 0, D / 16, fa);
 
-  int kc = 0;
-  auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    const int k1 = next3(kc), k2 = next3(k1);
+  auto step = [&](auto phase, int j) {
+    constexpr int P = decltype(phase)::value;
+    constexpr int kc = P % 3, k1 = (P + 1) % 3, k2 = (P + 2) % 3;
+    f32x16(&cur)[2] = pick<P>(sA, sB);
+    f32x16(&nxt)[2] = pick<P + 1>(sA, sB);
     dma.load(ks, (j + 2) * BK, Kb(k2));
-    dma.load(vs, (j + 1) * BK, Vb((j + 1) & 1));
+    dma.load(vs, (j + 1) * BK, Vb((P + 1) % 2));
     const uint16_t* Kt = Kb(kc);
     const uint16_t* Kn = Kb(k1);
-    const uint16_t* Vc = Vb(j & 1);
+    const uint16_t* Vc = Vb(P % 2);
     f32x16 dp[2];
     zero2(dp);
     zero2(nxt);
-    score_pipelined<D>(dp, Vc, gf, l32, hf);
+    score_pipelined<D>(dp, Vc, gf, fa);
     bf16x8 dh[4], dl[4], unused_h, unused_l;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), l32, hf);  // MFMA: tile j+1
-      dsigmoid_chunk<SPLIT, false>(cur, dp, c, c1, c2, dh[c], dl[c], unused_h, unused_l);
+      score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), fa);  // MFMA: tile j+1
+      dsigmoid_chunk<D, SPLIT, false>(cur, dp, c, c2, dh[c], dl[c], unused_h, unused_l);
       if (c > 0) value_chunk<D, SPLIT>(acc, tr, Kt, c - 1, dh[c - 1], dl[c - 1]);
     }
     value_chunk<D, SPLIT>(acc, tr, Kt, 3, dh[3], dl[3]);
     vm_drain();
     __syncthreads();
-    kc = k1;
   };
-  int j = 0;
-  for (; j + 1 < nk; j += 2) {
-    step(j, sA, sB);
-    step(j + 1, sB, sA);
-  }
-  if (j < nk) step(j, sA, sB);
+  run_steps(nk, step);
 
   if (qrow < n) {
     const float scale = S.out_scale;
@@ -394,8 +421,9 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   const size_t base = (size_t)it.bh * S.Lmax * D;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const float c1 = S.c1, c2 = it.c2;
+  const float c2 = it.c2;
   const TrFrag<D> tr(lane);
+  const FragAddr<D> fa(l32, hf);
   const TileDma<BQ, D> dma(w, lane);
   auto Qb = [&](int i) { return lds + i * TILE; };
   auto Gb = [&](int i) { return lds + (3 + i) * TILE; };
@@ -422,12 +450,16 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   f32x16 sA[2], dA[2], sB[2], dB[2];
   zero2(sA);
   zero2(dA);
-  score_steps<D>(sA, Qb(0), kf, 0, D / 16, l32, hf);
-  score_steps<D>(dA, Gb(0), vf, 0, D / 16, l32, hf);
+  score_steps<D>(sA, Qb(0), kf, 0, D / 16, fa);
+  score_steps<D>(dA, Gb(0), vf, 0, D / 16, fa);
 
-  int kc = 0;
-  auto step = [&](int j, f32x16 (&cs)[2], f32x16 (&cd)[2], f32x16 (&ns)[2], f32x16 (&nd)[2]) {
-    const int k1 = next3(kc), k2 = next3(k1);
+  auto step = [&](auto phase, int j) {
+    constexpr int P = decltype(phase)::value;
+    constexpr int kc = P % 3, k1 = (P + 1) % 3, k2 = (P + 2) % 3;
+    f32x16(&cs)[2] = pick<P>(sA, sB);
+    f32x16(&cd)[2] = pick<P>(dA, dB);
+    f32x16(&ns)[2] = pick<P + 1>(sA, sB);
+    f32x16(&nd)[2] = pick<P + 1>(dA, dB);
     dma.load(qs, (j + 2) * BQ, Qb(k2));
     dma.load(gs, (j + 2) * BQ, Gb(k2));
     const uint16_t* Qn = Qb(k1);
@@ -446,24 +478,18 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
         read_value_frags<D>(ag, tr, Gt, c);
         read_value_frags<D>(aq, tr, Qt, c);
         sched_fence();
-        dsigmoid_chunk<SPLIT, true>(cs, cd, c, c1, c2, dh[c], dl[c], ph[c], pl[c]);
+        dsigmoid_chunk<D, SPLIT, true>(cs, cd, c, c2, dh[c], dl[c], ph[c], pl[c]);
         sched_fence();
         value_chunk_pre<D, SPLIT>(dv, ag, ph[c], pl[c]);
         value_chunk_pre<D, SPLIT>(dk, aq, dh[c], dl[c]);
       }
-      score_pipelined<D>(ns, Qn, kf, l32, hf);
-      score_pipelined<D>(nd, Gn, vf, l32, hf);
+      score_pipelined<D>(ns, Qn, kf, fa);
+      score_pipelined<D>(nd, Gn, vf, fa);
     }
     vm_drain();
     __syncthreads();
-    kc = k1;
   };
-  int j = 0;
-  for (; j + 1 < nq; j += 2) {
-    step(j, sA, dA, sB, dB);
-    step(j + 1, sB, dB, sA, dA);
-  }
-  if (j < nq) step(j, sA, dA, sB, dB);
+  run_steps(nq, step);
 
   if (krow < n) {
     const float scale = S.out_scale;

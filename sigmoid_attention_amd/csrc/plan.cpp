@@ -115,7 +115,6 @@ std::vector<Launch> build_plan(const PlanInput& in, PlanStats* stats) {
     std::memset(&L.sched, 0, sizeof(L.sched));
     L.sched.H = in.H;
     L.sched.Lmax = in.Lmax;
-    L.sched.c1 = (float)(-log2e / std::sqrt((double)in.d));
     L.sched.out_scale = (float)(1.0 / std::sqrt((double)in.d));
     int32_t g = 0, max_items = 0;
     for (int x = 0; x < kXcds; ++x) {

@@ -36,7 +36,6 @@ constexpr int kZeroSplit = 4;
 struct Sched {
   int32_t H;
   int32_t Lmax;
-  float c1;                      // -log2(e) / sqrt(d): t = c1 * s + c2, sigma = 1 / (1 + 2^t)
   float out_scale;               // 1 / sqrt(d) (gradient epilogues)
   int32_t xcd_begin[kXcds + 1];  // piece range of each XCD list
   int32_t xcd_items[kXcds];      // work items in each XCD list
