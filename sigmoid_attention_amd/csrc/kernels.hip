@@ -45,7 +45,7 @@ constexpr int kInner = 64;  // rows per inner tile
 // for the forward and dK/dV; dQ keeps the lookahead of its scores.
 template <int D> struct FwdCfg { static constexpr bool LA = D != 64; static constexpr int OCC = D == 64 ? 4 : 1; };
 template <int D> struct DqCfg { static constexpr bool LA = true; static constexpr int OCC = D == 64 ? 2 : 1; };
-template <int D> struct DkdvCfg { static constexpr int OCC = D == 64 ? 2 : 1; };
+template <int D> struct DkdvCfg { static constexpr int BQ = 64; static constexpr int OCC = D == 64 ? 2 : 1; };
 
 // sigma of the eight score values of K-chunk c, rounded to bf16 (hi) and, in
 // split precision, the bf16 remainder (lo).
@@ -93,13 +93,13 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x16& acc, int i, 
 // Score-product helpers.  `tile` is an LDS tile; `bf` holds the B fragments
 // (this wave's 32 rows of the other operand).  Block mb covers tile rows
 // 32mb .. 32mb+31; K-steps s cover d = 16s .. 16s+15.
-template <int D>
-__device__ __forceinline__ void score_steps(f32x16 (&acc)[2], const uint16_t* tile, const bf16x8 (&bf)[D / 16],
+template <int D, int NB>
+__device__ __forceinline__ void score_steps(f32x16 (&acc)[NB], const uint16_t* tile, const bf16x8 (&bf)[D / 16],
                                             int s0, int s1, const FragAddr<D>& fa) {
 #pragma unroll
   for (int s = s0; s < s1; ++s)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) acc[mb] = mfma(fa.read(tile, mb, s), bf[s], acc[mb]);
+    for (int mb = 0; mb < NB; ++mb) acc[mb] = mfma(fa.read(tile, mb, s), bf[s], acc[mb]);
 }
 
 template <int D>
@@ -146,30 +146,42 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 
 // Score product over all K-steps with the A fragments of step s+1 read while
 // step s multiplies (one step of read-ahead).
-template <int D>
-__device__ __forceinline__ void score_pipelined(f32x16 (&acc)[2], const uint16_t* tile, const bf16x8 (&bf)[D / 16],
+template <int D, int NB>
+__device__ __forceinline__ void score_pipelined(f32x16 (&acc)[NB], const uint16_t* tile, const bf16x8 (&bf)[D / 16],
                                                 const FragAddr<D>& fa) {
-  bf16x8 a0[2], a1[2];
-  a0[0] = fa.read(tile, 0, 0);
-  a0[1] = fa.read(tile, 1, 0);
+  bf16x8 a0[NB], a1[NB];
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) a0[mb] = fa.read(tile, mb, 0);
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     if (s + 1 < D / 16) {
-      a1[0] = fa.read(tile, 0, s + 1);
-      a1[1] = fa.read(tile, 1, s + 1);
+#pragma unroll
+      for (int mb = 0; mb < NB; ++mb) a1[mb] = fa.read(tile, mb, s + 1);
     }
     sched_fence();
-    acc[0] = mfma(a0[0], bf[s], acc[0]);
-    acc[1] = mfma(a0[1], bf[s], acc[1]);
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) acc[mb] = mfma(a0[mb], bf[s], acc[mb]);
     sched_fence();
-    a0[0] = a1[0];
-    a0[1] = a1[1];
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) a0[mb] = a1[mb];
   }
 }
 
-__device__ __forceinline__ void zero2(f32x16 (&a)[2]) {
-  a[0] = (f32x16){};
-  a[1] = (f32x16){};
+// Scheduling hint: NM matrix products, each followed by NV vector ALU
+// instructions, so the MFMA unit works while the VALU evaluates sigma.
+template <int NM, int NV>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void zero2(f32x16 (&a)[NB]) {
+#pragma unroll
+  for (int i = 0; i < NB; ++i) a[i] = (f32x16){};
 }
 
 // Inner loops are unrolled six times (the period of the 3-stage LDS ring and
@@ -408,7 +420,7 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     const Sched S) {
-  constexpr int BKV = 128, BQ = kInner, TILE = BQ * D;
+  constexpr int BKV = 128, BQ = DkdvCfg<D>::BQ, TILE = BQ * D, NMB = BQ / 32, NC = BQ / 16;
   __shared__ __align__(16) uint16_t lds[6 * TILE];  // Q0 Q1 Q2 G0 G1 G2
 
   if ((int)blockIdx.x >= S.compute_blocks) {
@@ -447,7 +459,7 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   dma.load(gs, BQ, Gb(1));
   vm_drain();
   __syncthreads();
-  f32x16 sA[2], dA[2], sB[2], dB[2];
+  f32x16 sA[NMB], dA[NMB], sB[NMB], dB[NMB];
   zero2(sA);
   zero2(dA);
   score_steps<D>(sA, Qb(0), kf, 0, D / 16, fa);
@@ -456,10 +468,10 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   auto step = [&](auto phase, int j) {
     constexpr int P = decltype(phase)::value;
     constexpr int kc = P % 3, k1 = (P + 1) % 3, k2 = (P + 2) % 3;
-    f32x16(&cs)[2] = pick<P>(sA, sB);
-    f32x16(&cd)[2] = pick<P>(dA, dB);
-    f32x16(&ns)[2] = pick<P + 1>(sA, sB);
-    f32x16(&nd)[2] = pick<P + 1>(dA, dB);
+    f32x16(&cs)[NMB] = pick<P>(sA, sB);
+    f32x16(&cd)[NMB] = pick<P>(dA, dB);
+    f32x16(&ns)[NMB] = pick<P + 1>(sA, sB);
+    f32x16(&nd)[NMB] = pick<P + 1>(dA, dB);
     dma.load(qs, (j + 2) * BQ, Qb(k2));
     dma.load(gs, (j + 2) * BQ, Gb(k2));
     const uint16_t* Qn = Qb(k1);
@@ -468,21 +480,29 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     const uint16_t* Gt = Gb(kc);
     zero2(ns);
     zero2(nd);
-    bf16x8 dh[4], dl[4], ph[4], pl[4];
+    bf16x8 dh[NC], dl[NC], ph[NC], pl[NC];
     {
       // Per chunk: issue the transposing reads of dO^T and Q^T, evaluate
-      // P and dS on the VALU while they land, then multiply.
+      // P and dS on the VALU while they land, with the previous chunk's
+      // dV and dK products interleaved into that VALU work.
+      bf16x8 ag[2][D / 32], aq[2][D / 32];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        bf16x8 ag[D / 32], aq[D / 32];
-        read_value_frags<D>(ag, tr, Gt, c);
-        read_value_frags<D>(aq, tr, Qt, c);
+      for (int c = 0; c < NC; ++c) {
+        read_value_frags<D>(ag[c & 1], tr, Gt, c);
+        read_value_frags<D>(aq[c & 1], tr, Qt, c);
         sched_fence();
         dsigmoid_chunk<D, SPLIT, true>(cs, cd, c, c2, dh[c], dl[c], ph[c], pl[c]);
+        if (c > 0) {
+          value_chunk_pre<D, SPLIT>(dv, ag[(c - 1) & 1], ph[c - 1], pl[c - 1]);
+          value_chunk_pre<D, SPLIT>(dk, aq[(c - 1) & 1], dh[c - 1], dl[c - 1]);
+          // the previous chunk's products spread through this chunk's VALU work
+          constexpr int nm = 2 * (D / 32) * (SPLIT ? 2 : 1);
+          interleave<nm, 64 / nm>();
+        }
         sched_fence();
-        value_chunk_pre<D, SPLIT>(dv, ag, ph[c], pl[c]);
-        value_chunk_pre<D, SPLIT>(dk, aq, dh[c], dl[c]);
       }
+      value_chunk_pre<D, SPLIT>(dv, ag[(NC - 1) & 1], ph[NC - 1], pl[NC - 1]);
+      value_chunk_pre<D, SPLIT>(dk, aq[(NC - 1) & 1], dh[NC - 1], dl[NC - 1]);
       score_pipelined<D>(ns, Qn, kf, fa);
       score_pipelined<D>(nd, Gn, vf, fa);
     }
