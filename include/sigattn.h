@@ -28,11 +28,15 @@
  * the natural log; d is the head dimension; padded output rows are written as
  * zero; a sequence with n_b = 0 produces all-zero outputs.
  *
- * Tensors.  Q, K, V, dO, O, dQ, dK, dV are device pointers to contiguous
- * bf16 arrays of shape [B, H, Lmax, d] (row-major: d fastest), 16-byte
- * aligned.  The caller owns every buffer; the library allocates no device or
- * pinned memory and keeps no state between calls.  Rows n_b..Lmax-1 of the
- * inputs may hold any bit pattern (including NaN/Inf): they are never read.
+ * Tensors.  Q, K, V, dO, O, dQ, dK, dV are device pointers to bf16 arrays
+ * seen as [B, H, Lmax, d], 16-byte aligned.  By default each is contiguous
+ * (row-major: d fastest); with args->strides each tensor argument may be any
+ * strided view whose head dimension is contiguous (for example [B, Lmax, H, d]
+ * activations, or the q/k/v slices of a fused QKV projection), so a caller
+ * needs no transposes or copies.  The caller owns every buffer; the library
+ * allocates no device or pinned memory and keeps no state between calls.
+ * Rows n_b..Lmax-1 of the inputs may hold any bit pattern (including
+ * NaN/Inf): they are never read.
  *
  * Streams and errors.  Every call validates all arguments on the host before
  * it enqueues anything, so a call that returns an error has no side effect.
@@ -63,7 +67,11 @@ typedef enum sigattn_status {
                                 with SIGATTN_BIAS_NEG_LOG_N                             */
   SIGATTN_ERR_PRECISION = 7, /* unknown precision                                       */
   SIGATTN_ERR_HIP = 8,       /* the HIP runtime rejected a kernel launch                */
-  SIGATTN_ERR_PASS = 9       /* unknown pass id (sigattn_plan_stats only)               */
+  SIGATTN_ERR_PASS = 9,      /* unknown pass id (sigattn_plan_stats only)               */
+  SIGATTN_ERR_STRIDE = 10    /* a stride is negative or not a multiple of 8 elements, a
+                                row stride is below d or too large for 32-bit offsets
+                                ((Lmax + 256) * l * 2 > 2^31 - 1), or an output view
+                                maps two elements to one address                        */
 } sigattn_status;
 
 /* The bias b_b of the SigmoidAttn formula (summary §2A, b = -log(n)). */
@@ -88,6 +96,21 @@ typedef enum sigattn_pass {
   SIGATTN_PASS_BWD_DKDV = 2
 } sigattn_pass;
 
+/* Element strides of one tensor argument seen as [B, H, Lmax, d]: element
+ * (b, h, l, c) is at ptr[b * b_stride + h * h_stride + l * l_stride + c].  The
+ * head dimension is always contiguous.  Contiguous [B, H, Lmax, d] is
+ * {H*Lmax*d, Lmax*d, d}; [B, Lmax, H, d] is {Lmax*H*d, d, H*d}; the q slice of
+ * a fused [B, Lmax, 3, H, d] projection is {Lmax*3*H*d, d, 3*H*d}.  Every
+ * stride must be a non-negative multiple of 8 (16-byte rows) and l_stride >= d.
+ * Inputs may overlap one another and may broadcast (a zero stride); an output
+ * must map distinct elements to distinct addresses and may not overlap an
+ * input or another output (checked exactly for outputs that share strides,
+ * such as the dq/dk/dv slices of one fused buffer, and by address range
+ * otherwise). */
+typedef struct sigattn_strides {
+  int64_t b, h, l;
+} sigattn_strides;
+
 typedef struct sigattn_args {
   int32_t B, H, Lmax, d;    /* batch, heads, padded length, head dim (64 or 128)    */
   const int32_t *seqlens;   /* HOST pointer to B valid lengths, 0 <= n_b <= Lmax;
@@ -96,6 +119,11 @@ typedef struct sigattn_args {
   float bias_arg;           /* see sigattn_bias_mode; ignored for mode 0            */
   int32_t precision;        /* sigattn_precision                                    */
   void *stream;             /* hipStream_t to enqueue on; NULL = default stream     */
+  const sigattn_strides *strides; /* HOST pointer, NULL = every tensor contiguous
+                               [B, H, Lmax, d]; else one entry per tensor argument
+                               of the call, in argument order (fwd: q, k, v, o;
+                               dq: q, k, v, dout, dq; dkdv: q, k, v, dout, dk, dv);
+                               read during the call only                            */
 } sigattn_args;
 
 /* Forward: O = sigma(Q K^T / sqrt(d) + b) V on valid rows; padded rows of O = 0.
@@ -114,6 +142,14 @@ sigattn_status sigattn_bwd_dq(const sigattn_args *args, const void *q, const voi
  * atomics (§2C). */
 sigattn_status sigattn_bwd_dkdv(const sigattn_args *args, const void *q, const void *k,
                                 const void *v, const void *dout, void *dk, void *dv);
+
+/* Runs every check the compute call for pass p would run (shape, lengths,
+ * bias, precision, null pointers, alignment, strides, aliasing) on the
+ * call's tensor arguments, given in argument order (fwd: q, k, v, o; dq: q,
+ * k, v, dout, dq; dkdv: q, k, v, dout, dk, dv), and returns the status that
+ * call would return, without enqueuing anything and without dereferencing the
+ * tensor pointers.  For callers that want to vet a layout ahead of time. */
+sigattn_status sigattn_validate(const sigattn_args *args, int32_t pass, const void *const *tensors);
 
 /* Static description of a status code; never NULL. */
 const char *sigattn_status_str(sigattn_status status);

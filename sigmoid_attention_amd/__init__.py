@@ -6,13 +6,18 @@ Python face of the C-ABI library ``libsigattn`` (include/sigattn.h):
     dq      = bwd_dq(q, k, v, do, seqlens)
     dk, dv  = bwd_dkdv(q, k, v, do, seqlens)
 
-q, k, v, do: bf16 CUDA tensors [B, H, Lmax, d] (d = 64 or 128), contiguous;
-seqlens: B valid lengths (right padding).  Calls enqueue on the current
-stream.  All computation happens in the library's HIP kernels; this package
-only marshals arguments and fails loudly if the library is not built.
+q, k, v, do: bf16 CUDA tensors [B, H, Lmax, d] (d = 64 or 128), or
+[B, Lmax, H, d] with layout="blhd", head dimension contiguous (other strides
+are passed through); seqlens: B valid lengths (right padding).  Calls enqueue
+on the current stream.  ``sigmoid_attention`` and ``SigmoidAttention`` add
+autograd and an nn.Module on top.  All computation happens in the library's
+HIP kernels; this package only marshals arguments and fails loudly if the
+library is not built.
 """
-from ._binding import (BIAS_MODES, EXPORTED, PASSES, PRECISIONS, SigattnError, bwd_dkdv, bwd_dq, fwd, lib_path,
-                       load, make_args, plan_stats, status_str, tile_shape)
+from ._binding import (BIAS_MODES, EXPORTED, LAYOUTS, PASSES, PRECISIONS, SigattnError, bwd_dkdv, bwd_dq, fwd,
+                       lib_path, load, make_args, plan_stats, status_str, tile_shape, validate)
+from .function import SigmoidAttention, lengths_from_padding_mask, sigmoid_attention
 
-__all__ = ["BIAS_MODES", "EXPORTED", "PASSES", "PRECISIONS", "SigattnError", "bwd_dkdv", "bwd_dq", "fwd",
-           "lib_path", "load", "make_args", "plan_stats", "status_str", "tile_shape"]
+__all__ = ["BIAS_MODES", "EXPORTED", "LAYOUTS", "PASSES", "PRECISIONS", "SigattnError", "SigmoidAttention",
+           "bwd_dkdv", "bwd_dq", "fwd", "lengths_from_padding_mask", "lib_path", "load", "make_args",
+           "plan_stats", "sigmoid_attention", "status_str", "tile_shape", "validate"]

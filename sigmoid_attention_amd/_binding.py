@@ -23,11 +23,18 @@ PASSES = {"fwd": 0, "bwd_dq": 1, "bwd_dkdv": 2}
 STATUS_NAMES = {
     0: "SIGATTN_OK", 1: "SIGATTN_ERR_NULL", 2: "SIGATTN_ERR_SHAPE", 3: "SIGATTN_ERR_SEQLEN",
     4: "SIGATTN_ERR_ALIGN", 5: "SIGATTN_ERR_ALIAS", 6: "SIGATTN_ERR_BIAS", 7: "SIGATTN_ERR_PRECISION",
-    8: "SIGATTN_ERR_HIP", 9: "SIGATTN_ERR_PASS",
+    8: "SIGATTN_ERR_HIP", 9: "SIGATTN_ERR_PASS", 10: "SIGATTN_ERR_STRIDE",
 }
 
+# Index order of a 4-d tensor for each supported layout, as (b, h, l, d) positions.
+LAYOUTS = {"bhld": (0, 1, 2, 3), "blhd": (0, 2, 1, 3)}
+
 EXPORTED = ("sigattn_fwd", "sigattn_bwd_dq", "sigattn_bwd_dkdv", "sigattn_status_str",
-            "sigattn_plan_stats", "sigattn_tile_shape")
+            "sigattn_plan_stats", "sigattn_tile_shape", "sigattn_validate")
+
+
+class SigattnStrides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("l", ctypes.c_int64)]
 
 
 class SigattnArgs(ctypes.Structure):
@@ -37,6 +44,7 @@ class SigattnArgs(ctypes.Structure):
         ("bias_mode", ctypes.c_int32), ("bias_arg", ctypes.c_float),
         ("precision", ctypes.c_int32),
         ("stream", ctypes.c_void_p),
+        ("strides", ctypes.POINTER(SigattnStrides)),
     ]
 
 
@@ -74,6 +82,8 @@ def load() -> ctypes.CDLL:
     lib.sigattn_tile_shape.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                        ctypes.POINTER(ctypes.c_int32)]
     lib.sigattn_tile_shape.restype = ctypes.c_int
+    lib.sigattn_validate.argtypes = [ap, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+    lib.sigattn_validate.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -82,9 +92,13 @@ def status_str(code: int) -> str:
     return load().sigattn_status_str(int(code)).decode()
 
 
-def make_args(B, H, Lmax, d, seqlens, bias_mode="seqlen", bias_arg=0.0, precision="fast", stream=0):
-    """Build a sigattn_args struct.  Returns (args, keepalive) — keep the second
-    object alive for as long as the struct is used (it owns the lengths)."""
+def make_args(B, H, Lmax, d, seqlens, bias_mode="seqlen", bias_arg=0.0, precision="fast", stream=0,
+              strides=None):
+    """Build a sigattn_args struct.  `strides`: None (every tensor contiguous
+    [B, H, Lmax, d]) or one (b, h, l) element-stride triple per tensor
+    argument, in argument order.  Returns (args, keepalive) — keep the second
+    object alive for as long as the struct is used (it owns the lengths and
+    strides)."""
     lens = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
     a = SigattnArgs()
     a.B, a.H, a.Lmax, a.d = int(B), int(H), int(Lmax), int(d)
@@ -93,7 +107,11 @@ def make_args(B, H, Lmax, d, seqlens, bias_mode="seqlen", bias_arg=0.0, precisio
     a.bias_arg = float(bias_arg)
     a.precision = PRECISIONS[precision] if isinstance(precision, str) else int(precision)
     a.stream = int(stream) if stream else None
-    return a, lens
+    st = None
+    if strides is not None:
+        st = (SigattnStrides * len(strides))(*[SigattnStrides(int(b), int(h), int(l)) for b, h, l in strides])
+        a.strides = ctypes.cast(st, ctypes.POINTER(SigattnStrides))
+    return a, (lens, st)
 
 
 def _check(code: int, where: str):
@@ -101,9 +119,22 @@ def _check(code: int, where: str):
         raise SigattnError(code, where)
 
 
-def _tensor_args(ts, seqlens, bias_mode, bias_arg, precision, stream):
-    import torch
+def layout_strides(t, layout: str = "bhld"):
+    """(B, H, Lmax, d) and the (b, h, l) element strides of a 4-d tensor in
+    `layout` order."""
+    pos = LAYOUTS[layout]
+    return tuple(t.shape[i] for i in pos), (t.stride(pos[0]), t.stride(pos[1]), t.stride(pos[2]))
 
+
+def _tensor_args(ts, seqlens, bias_mode, bias_arg, precision, stream, layout="bhld"):
+    """Validate tensors and build the argument block.  Each tensor is 4-d in
+    `layout` order ("bhld": [B, H, Lmax, d]; "blhd": [B, Lmax, H, d]) with a
+    contiguous last dimension; any other strides (views of a fused projection,
+    a broadcast K/V head) go to the library, which checks them."""
+    import torch
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    pos = LAYOUTS[layout]
     q = ts[0]
     for t in ts:
         if not isinstance(t, torch.Tensor):
@@ -112,27 +143,38 @@ def _tensor_args(ts, seqlens, bias_mode, bias_arg, precision, stream):
             raise TypeError(f"expected bfloat16 tensors, got {t.dtype}")
         if not t.is_cuda:
             raise ValueError("tensors must live on the GPU")
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous [B, H, Lmax, d]")
+        if t.dim() != 4:
+            raise ValueError(f"expected 4-d tensors in {layout} order")
         if t.shape != q.shape or t.device != q.device:
             raise ValueError("all tensors must share shape and device")
-    if q.dim() != 4:
-        raise ValueError("expected [B, H, Lmax, d] tensors")
-    B, H, L, d = q.shape
+        if t.stride(3) != 1:
+            raise ValueError("the head dimension must be contiguous")
+    (B, H, L, d), _ = layout_strides(q, layout)
+    strides = [layout_strides(t, layout)[1] for t in ts]
+    contiguous = all(s == (H * L * d, L * d, d) for s in strides)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    return make_args(B, H, L, d, seqlens, bias_mode, bias_arg, precision, stream)
+    return make_args(B, H, L, d, seqlens, bias_mode, bias_arg, precision, stream,
+                     None if contiguous else strides)
+
+
+def _new_like(t):
+    """A fresh contiguous tensor of t's shape (t itself may be a strided view)."""
+    import torch
+
+    return torch.empty(t.shape, dtype=t.dtype, device=t.device)
 
 
 def fwd(q, k, v, seqlens: Sequence[int], o=None, bias_mode="seqlen", bias_arg=0.0, precision="fast",
-        stream: Optional[int] = None):
+        stream: Optional[int] = None, layout: str = "bhld"):
     """O = sigma(Q K^T / sqrt(d) + b) V, padded rows of O zero.  Enqueued on the
-    current stream (or `stream`); returns O."""
+    current stream (or `stream`); returns O (a new O is contiguous in `layout`
+    order)."""
     import torch
 
     if o is None:
-        o = torch.empty_like(q)
-    args, keep = _tensor_args((q, k, v, o), seqlens, bias_mode, bias_arg, precision, stream)
+        o = _new_like(q)
+    args, keep = _tensor_args((q, k, v, o), seqlens, bias_mode, bias_arg, precision, stream, layout)
     with torch.cuda.device(q.device):
         _check(load().sigattn_fwd(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()),
                "sigattn_fwd")
@@ -140,13 +182,14 @@ def fwd(q, k, v, seqlens: Sequence[int], o=None, bias_mode="seqlen", bias_arg=0.
     return o
 
 
-def bwd_dq(q, k, v, dout, seqlens, dq=None, bias_mode="seqlen", bias_arg=0.0, precision="fast", stream=None):
+def bwd_dq(q, k, v, dout, seqlens, dq=None, bias_mode="seqlen", bias_arg=0.0, precision="fast", stream=None,
+           layout: str = "bhld"):
     """dQ of sum(O * dO); padded rows zero.  Returns dQ."""
     import torch
 
     if dq is None:
-        dq = torch.empty_like(q)
-    args, keep = _tensor_args((q, k, v, dout, dq), seqlens, bias_mode, bias_arg, precision, stream)
+        dq = _new_like(q)
+    args, keep = _tensor_args((q, k, v, dout, dq), seqlens, bias_mode, bias_arg, precision, stream, layout)
     with torch.cuda.device(q.device):
         _check(load().sigattn_bwd_dq(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                      dout.data_ptr(), dq.data_ptr()), "sigattn_bwd_dq")
@@ -155,15 +198,15 @@ def bwd_dq(q, k, v, dout, seqlens, dq=None, bias_mode="seqlen", bias_arg=0.0, pr
 
 
 def bwd_dkdv(q, k, v, dout, seqlens, dk=None, dv=None, bias_mode="seqlen", bias_arg=0.0, precision="fast",
-             stream=None):
+             stream=None, layout: str = "bhld"):
     """dK and dV of sum(O * dO); padded rows zero.  Returns (dK, dV)."""
     import torch
 
     if dk is None:
-        dk = torch.empty_like(k)
+        dk = _new_like(k)
     if dv is None:
-        dv = torch.empty_like(v)
-    args, keep = _tensor_args((q, k, v, dout, dk, dv), seqlens, bias_mode, bias_arg, precision, stream)
+        dv = _new_like(v)
+    args, keep = _tensor_args((q, k, v, dout, dk, dv), seqlens, bias_mode, bias_arg, precision, stream, layout)
     with torch.cuda.device(q.device):
         _check(load().sigattn_bwd_dkdv(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                        dout.data_ptr(), dk.data_ptr(), dv.data_ptr()), "sigattn_bwd_dkdv")
@@ -179,6 +222,13 @@ def plan_stats(B, H, Lmax, d, seqlens, pass_="fwd", bias_mode="seqlen", bias_arg
                                      ctypes.byref(launches)), "sigattn_plan_stats")
     del keep
     return items.value, pairs.value, launches.value
+
+
+def validate(args, pass_: str, pointers) -> int:
+    """Status the compute call for `pass_` would return for these arguments
+    and tensor addresses (host-only, nothing enqueued or dereferenced)."""
+    arr = (ctypes.c_void_p * len(pointers))(*[int(p) for p in pointers])
+    return load().sigattn_validate(ctypes.byref(args), PASSES[pass_], arr)
 
 
 def tile_shape(pass_: str, d: int):

@@ -3,6 +3,7 @@
 // return has no side effect.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -58,14 +59,90 @@ sigattn_status check_args(const sigattn_args* a) {
   return SIGATTN_OK;
 }
 
-struct Span {
-  uintptr_t lo, hi;
+// One tensor argument: address and element strides of its [B, H, Lmax, d] view.
+struct View {
+  uintptr_t p;
+  int64_t sb, sh, sl;
 };
 
-bool overlaps(Span x, Span y) { return x.lo < y.hi && y.lo < x.hi; }
+// Contiguous [B, H, Lmax, d] unless args->strides says otherwise.
+std::vector<View> views(const sigattn_args* a, const void* const* t, int n) {
+  std::vector<View> v(n);
+  for (int i = 0; i < n; ++i) {
+    v[i].p = (uintptr_t)t[i];
+    if (a->strides) {
+      v[i].sb = a->strides[i].b;
+      v[i].sh = a->strides[i].h;
+      v[i].sl = a->strides[i].l;
+    } else {
+      v[i].sl = a->d;
+      v[i].sh = (int64_t)a->Lmax * a->d;
+      v[i].sb = (int64_t)a->H * a->Lmax * a->d;
+    }
+  }
+  return v;
+}
 
-// Null, alignment and aliasing checks.  Inputs may alias one another; an
-// output may overlap neither an input nor another output.
+// Dimensions (extent > 1) of a view, inner run of d elements included, sorted
+// by stride.
+struct Dim {
+  int64_t e, s;
+};
+
+std::vector<Dim> dims(const sigattn_args* a, const View& v) {
+  std::vector<Dim> d = {{a->d, 1}};
+  if (a->B > 1) d.push_back({a->B, v.sb});
+  if (a->H > 1) d.push_back({a->H, v.sh});
+  if (a->Lmax > 1) d.push_back({a->Lmax, v.sl});
+  std::sort(d.begin(), d.end(), [](const Dim& x, const Dim& y) { return x.s < y.s; });
+  return d;
+}
+
+// Distinct elements at distinct addresses: each stride at least the extent of
+// the dimensions below it (sufficient, and exact for the usual layouts).
+bool injective(const sigattn_args* a, const View& v) {
+  const std::vector<Dim> d = dims(a, v);
+  if (d[0].s < 1) return false;  // a broadcast (zero-stride) dimension
+  for (size_t k = 1; k < d.size(); ++k)
+    if (d[k].s < d[k - 1].s * d[k - 1].e) return false;
+  return true;
+}
+
+// Byte range [lo, hi) a view can touch.
+void span(const sigattn_args* a, const View& v, uintptr_t& lo, uintptr_t& hi) {
+  const int64_t last = (int64_t)(a->B - 1) * v.sb + (int64_t)(a->H - 1) * v.sh + (int64_t)(a->Lmax - 1) * v.sl;
+  lo = v.p;
+  hi = v.p + 2 * (uintptr_t)(last + a->d);
+}
+
+// Whether two views may share an address.  Disjoint address ranges never do.
+// Two injective views with the same strides whose footprint repeats with the
+// period of their first non-contiguous stride (all outer strides multiples of
+// it) occupy residue windows [0, R) and [delta, delta + R) modulo that period,
+// R being the contiguous run; they are disjoint when those windows are.
+bool may_overlap(const sigattn_args* a, const View& x, const View& y) {
+  uintptr_t xl, xh, yl, yh;
+  span(a, x, xl, xh);
+  span(a, y, yl, yh);
+  if (xh <= yl || yh <= xl) return false;
+  if (x.sb != y.sb || x.sh != y.sh || x.sl != y.sl || !injective(a, x)) return true;
+  std::vector<Dim> d = dims(a, x);
+  int64_t run = d[0].e;  // contiguous elements from the start of a run
+  size_t k = 1;
+  while (k < d.size() && d[k].s == run) run *= d[k++].e;
+  if (k == d.size()) return true;  // one contiguous block: ranges already overlap
+  const int64_t period = d[k].s;
+  for (size_t m = k + 1; m < d.size(); ++m)
+    if (d[m].s % period) return true;
+  const int64_t delta_bytes = (int64_t)(y.p - x.p);
+  if (delta_bytes % 2) return true;
+  int64_t r = (delta_bytes / 2) % period;
+  if (r < 0) r += period;
+  return !(r >= run && r <= period - run);
+}
+
+// Null, alignment, stride and aliasing checks.  Inputs may alias one another;
+// an output may overlap neither an input nor another output.
 sigattn_status check_ptrs(const sigattn_args* a, const void* const* in, int nin, void* const* out, int nout) {
   for (int i = 0; i < nin; ++i)
     if (!in[i]) return SIGATTN_ERR_NULL;
@@ -75,15 +152,30 @@ sigattn_status check_ptrs(const sigattn_args* a, const void* const* in, int nin,
     if ((uintptr_t)in[i] % 16) return SIGATTN_ERR_ALIGN;
   for (int i = 0; i < nout; ++i)
     if ((uintptr_t)out[i] % 16) return SIGATTN_ERR_ALIGN;
-  const uintptr_t bytes = (uintptr_t)a->B * a->H * a->Lmax * a->d * 2;
-  for (int i = 0; i < nout; ++i) {
-    const Span o = {(uintptr_t)out[i], (uintptr_t)out[i] + bytes};
-    for (int j = 0; j < nin; ++j)
-      if (overlaps(o, {(uintptr_t)in[j], (uintptr_t)in[j] + bytes})) return SIGATTN_ERR_ALIAS;
-    for (int j = i + 1; j < nout; ++j)
-      if (overlaps(o, {(uintptr_t)out[j], (uintptr_t)out[j] + bytes})) return SIGATTN_ERR_ALIAS;
+  std::vector<const void*> all(in, in + nin);
+  for (int i = 0; i < nout; ++i) all.push_back(out[i]);
+  const std::vector<View> v = views(a, all.data(), nin + nout);
+  for (int i = 0; i < nin + nout; ++i) {
+    const View& t = v[i];
+    if (t.sb < 0 || t.sh < 0 || t.sl < 0 || t.sb % 8 || t.sh % 8 || t.sl % 8 || t.sl < a->d)
+      return SIGATTN_ERR_STRIDE;
+    if (((int64_t)a->Lmax + kLmaxSlack) * t.sl * 2 > INT32_MAX) return SIGATTN_ERR_STRIDE;
+    if (i >= nin && !injective(a, t)) return SIGATTN_ERR_STRIDE;
   }
+  for (int i = nin; i < nin + nout; ++i)
+    for (int j = 0; j < i; ++j)
+      if (may_overlap(a, v[i], v[j])) return SIGATTN_ERR_ALIAS;
   return SIGATTN_OK;
+}
+
+// Strides of the call's tensor arguments, in argument order, into the schedule.
+void set_strides(const sigattn_args* a, const void* const* t, int n, Launch& L) {
+  const std::vector<View> v = views(a, t, n);
+  for (int i = 0; i < n; ++i) {
+    L.sched.sb[i] = v[i].sb;
+    L.sched.sh[i] = v[i].sh;
+    L.sched.sl[i] = (int32_t)v[i].sl;
+  }
 }
 
 sigattn::PlanInput plan_input(const sigattn_args* a, int32_t pass) {
@@ -100,11 +192,13 @@ sigattn::PlanInput plan_input(const sigattn_args* a, int32_t pass) {
 }
 
 template <class F>
-sigattn_status run(const sigattn_args* a, int32_t pass, F&& launch_one) {
-  const std::vector<Launch> plan = sigattn::build_plan(plan_input(a, pass), nullptr);
+sigattn_status run(const sigattn_args* a, int32_t pass, const void* const* t, int n, F&& launch_one) {
+  std::vector<Launch> plan = sigattn::build_plan(plan_input(a, pass), nullptr);
   (void)hipGetLastError();  // start from a clean per-thread error state
-  for (const Launch& L : plan)
+  for (Launch& L : plan) {
+    set_strides(a, t, n, L);
     if (launch_one(L) != hipSuccess) return SIGATTN_ERR_HIP;
+  }
   return SIGATTN_OK;
 }
 
@@ -119,7 +213,8 @@ sigattn_status sigattn_fwd(const sigattn_args* a, const void* q, const void* k, 
   void* out[] = {o};
   if ((s = check_ptrs(a, in, 3, out, 1)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
-  return run(a, SIGATTN_PASS_FWD, [&](const Launch& L) {
+  const void* t[] = {q, k, v, o};
+  return run(a, SIGATTN_PASS_FWD, t, 4, [&](const Launch& L) {
     return sigattn::launch_fwd(a->d, split, L, q, k, v, o, (hipStream_t)a->stream);
   });
 }
@@ -132,7 +227,8 @@ sigattn_status sigattn_bwd_dq(const sigattn_args* a, const void* q, const void* 
   void* out[] = {dq};
   if ((s = check_ptrs(a, in, 4, out, 1)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
-  return run(a, SIGATTN_PASS_BWD_DQ, [&](const Launch& L) {
+  const void* t[] = {q, k, v, dout, dq};
+  return run(a, SIGATTN_PASS_BWD_DQ, t, 5, [&](const Launch& L) {
     return sigattn::launch_bwd_dq(a->d, split, L, q, k, v, dout, dq, (hipStream_t)a->stream);
   });
 }
@@ -145,9 +241,22 @@ sigattn_status sigattn_bwd_dkdv(const sigattn_args* a, const void* q, const void
   void* out[] = {dk, dv};
   if ((s = check_ptrs(a, in, 4, out, 2)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
-  return run(a, SIGATTN_PASS_BWD_DKDV, [&](const Launch& L) {
+  const void* t[] = {q, k, v, dout, dk, dv};
+  return run(a, SIGATTN_PASS_BWD_DKDV, t, 6, [&](const Launch& L) {
     return sigattn::launch_bwd_dkdv(a->d, split, L, q, k, v, dout, dk, dv, (hipStream_t)a->stream);
   });
+}
+
+sigattn_status sigattn_validate(const sigattn_args* a, int32_t pass, const void* const* t) {
+  int32_t o, i;
+  if (tile_rows(pass, &o, &i) != SIGATTN_OK) return SIGATTN_ERR_PASS;
+  sigattn_status s = check_args(a);
+  if (s != SIGATTN_OK) return s;
+  if (!t) return SIGATTN_ERR_NULL;
+  const int nin = pass == SIGATTN_PASS_FWD ? 3 : 4;
+  const int nout = pass == SIGATTN_PASS_BWD_DKDV ? 2 : 1;
+  void* out[2] = {const_cast<void*>(t[nin]), nout == 2 ? const_cast<void*>(t[nin + 1]) : nullptr};
+  return check_ptrs(a, t, nin, out, nout);
 }
 
 const char* sigattn_status_str(sigattn_status s) {
@@ -162,6 +271,9 @@ const char* sigattn_status_str(sigattn_status s) {
     case SIGATTN_ERR_PRECISION: return "unknown precision mode";
     case SIGATTN_ERR_HIP: return "HIP kernel launch failed";
     case SIGATTN_ERR_PASS: return "unknown pass";
+    case SIGATTN_ERR_STRIDE:
+      return "bad strides: negative, not a multiple of 8, row stride below d or too large, or an output "
+             "that maps two elements to one address";
   }
   return "unknown status";
 }

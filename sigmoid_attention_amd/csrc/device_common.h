@@ -102,20 +102,37 @@ __device__ __forceinline__ int tile_slot(int r, int g) {
 }
 
 // Range-checked view of one (sequence, head) slice: rows 0..n-1 of D bf16
-// values.  Loads go through a raw buffer resource whose size is n * D * 2
-// bytes, so a load at or beyond row n returns zeros without touching memory:
-// padded rows are zero-filled by the hardware, with no VALU masking and no
-// branch, and garbage (even NaN/Inf) in padded rows cannot reach a product.
-// Offsets are 32-bit: the API bounds Lmax * d * 2 below 2^31.
+// values, row r at element r * rs.  Loads go through a raw buffer resource
+// whose size is n * rs * 2 bytes, so a load at or beyond row n returns zeros
+// without touching memory: padded rows are zero-filled by the hardware, with
+// no VALU masking and no branch, and garbage (even NaN/Inf) in padded rows
+// cannot reach a product.  Offsets are 32-bit: the API bounds
+// (Lmax + 256) * rs * 2 below 2^31.
 struct Slice {
   __amdgpu_buffer_rsrc_t rsrc;
-  __device__ __forceinline__ Slice(const uint16_t* base, int n, int D)
-      : rsrc(__builtin_amdgcn_make_buffer_rsrc((void*)base, 0, n * D * 2, 0x00020000)) {}
+  const uint16_t* base;
+  int n, rs;
+  __device__ __forceinline__ Slice(const uint16_t* base_, int n_, int row_stride)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc((void*)base_, 0, n_ * row_stride * 2, 0x00020000)),
+        base(base_), n(n_), rs(row_stride) {}
   // 16 bytes at element offset `elem` (a multiple of 8).
   __device__ __forceinline__ u32x4 load16(int elem) const {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, elem * 2, 0, 0));
   }
+  // The same range check for rows row0.. (row0 wave-uniform): a resource whose
+  // base is row row0, so per-lane offsets within a tile stay loop-invariant.
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t from_row(int row0) const {
+    const int rows = n > row0 ? n - row0 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)row0 * rs), 0, rows * rs * 2, 0x00020000);
+  }
 };
+
+// Start of the (sequence, head) slice of tensor argument t of a launch.
+template <class T>
+__device__ __forceinline__ T* slice_base(T* p, const Sched& S, int bh, int t) {
+  const int b = bh / S.H, h = bh - b * S.H;
+  return p + (size_t)b * S.sb[t] + (size_t)h * S.sh[t];
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -129,16 +146,16 @@ template <int ROWS, int D, int NW = 4>
 struct TileDma {
   static constexpr int NI = ROWS * D * 2 / (NW * 1024);
   static_assert(NI >= 1 && NI * NW * 1024 == ROWS * D * 2, "tile must split into 1 KB blocks over the waves");
-  int src[NI];  // element offset within the tile's rows
+  int src[NI];  // byte offset within the tile's rows (row stride row_stride)
   int dst[NI];  // element offset of this wave's block within the tile (wave-uniform)
-  __device__ __forceinline__ TileDma(int wave, int lane) {
+  __device__ __forceinline__ TileDma(int wave, int lane, int row_stride) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int blk = NW * i + wave;
       const int t = 64 * blk + lane;  // 16-byte slot filled by this lane
       const int r = t / (D / 8);
       const int g = (t % (D / 8)) ^ tile_xor<D>(r);
-      src[i] = r * D + 8 * g;
+      src[i] = 2 * (r * row_stride + 8 * g);
       dst[i] = 512 * blk;
     }
   }
@@ -147,10 +164,10 @@ struct TileDma {
   // it makes clang drop the host stubs of the kernels that use it.
   __device__ __forceinline__ void load(const Slice& s, int row0, uint16_t* tile) const {
 #if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t r = s.from_row(row0);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rsrc, (lds_void*)(tile + dst[i]), 16, (src[i] + row0 * D) * 2, 0,
-                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + dst[i]), 16, src[i], 0, 0, 0);
 #endif
   }
 };
@@ -163,7 +180,7 @@ __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0); }
 template <int D>
 __device__ __forceinline__ void load_bfrag(bf16x8 (&f)[D / 16], const Slice& src, int row, int hf) {
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) f[s] = as_bf16x8(src.load16(row * D + 16 * s + 8 * hf));
+  for (int s = 0; s < D / 16; ++s) f[s] = as_bf16x8(src.load16(row * src.rs + 16 * s + 8 * hf));
 }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -222,23 +239,27 @@ struct FragAddr {
 };
 
 // Trailing workgroups (blockIdx.x >= compute_blocks) write the padded rows
-// n_b..Lmax-1 of one or two outputs as 0 with 16-byte stores; the compute
-// workgroups store valid rows only, so no row has two writers.
+// n_b..Lmax-1 of one or two outputs (tensor arguments t1, t2) as 0 with
+// 16-byte stores; the compute workgroups store valid rows only, so no row has
+// two writers.
 template <int D>
-__device__ __forceinline__ void zero_padded_rows(const Sched& S, uint16_t* __restrict__ o1,
-                                                 uint16_t* __restrict__ o2) {
+__device__ __forceinline__ void zero_padded_rows(const Sched& S, uint16_t* __restrict__ o1, int t1,
+                                                 uint16_t* __restrict__ o2, int t2) {
   const int zb = (int)blockIdx.x - S.compute_blocks;
   const int bhl = zb / kZeroSplit, part = zb % kZeroSplit;
   const int bl = bhl / S.H;
   if (bl >= S.zero_nseq) return;
   const int n = S.zero_n[bl];
-  const size_t head = (size_t)S.zero_b0 * S.H + bhl;
-  const size_t begin = (head * S.Lmax + n) * D;
-  const size_t chunks = (size_t)(S.Lmax - n) * (D / 8);
+  const int bh = (S.zero_b0 + bl) * S.H + (bhl - bl * S.H);
+  uint16_t* p1 = slice_base(o1, S, bh, t1);
+  uint16_t* p2 = o2 ? slice_base(o2, S, bh, t2) : nullptr;
+  const int rs1 = S.sl[t1], rs2 = o2 ? S.sl[t2] : 0;
+  const int chunks = (S.Lmax - n) * (D / 8);
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (size_t c = (size_t)part * blockDim.x + threadIdx.x; c < chunks; c += (size_t)kZeroSplit * blockDim.x) {
-    *(u32x4*)(o1 + begin + 8 * c) = z;
-    if (o2) *(u32x4*)(o2 + begin + 8 * c) = z;
+  for (int c = part * (int)blockDim.x + (int)threadIdx.x; c < chunks; c += kZeroSplit * (int)blockDim.x) {
+    const int row = n + c / (D / 8), col = 8 * (c % (D / 8));
+    *(u32x4*)(p1 + (size_t)row * rs1 + col) = z;
+    if (o2) *(u32x4*)(p2 + (size_t)row * rs2 + col) = z;
   }
 }
 

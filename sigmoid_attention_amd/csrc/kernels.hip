@@ -240,22 +240,22 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
   __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
 
   if ((int)blockIdx.x >= S.compute_blocks) {
-    zero_padded_rows<D>(S, O, nullptr);
+    zero_padded_rows<D>(S, O, 3, nullptr, 0);
     return;
   }
   Item it;
   if (!find_item(S, it)) return;
   const int n = it.n;
-  const size_t base = (size_t)it.bh * S.Lmax * D;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c2 = it.c2;
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
-  const TileDma<BK, D> dma(w, lane);
+  const TileDma<BK, D> dma_k(w, lane, S.sl[1]), dma_v(w, lane, S.sl[2]);
   auto Kb = [&](int i) { return lds + i * TILE; };
   auto Vb = [&](int i) { return lds + (3 + i) * TILE; };
-  const Slice qs(Q + base, n, D), ks(K + base, n, D), vs(V + base, n, D);
+  const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
+      vs(slice_base(V, S, it.bh, 2), n, S.sl[2]);
 
   const int qrow = it.tile * BQ + 32 * w + l32;
   bf16x8 qf[D / 16];
@@ -265,9 +265,9 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
 
   const int nk = (n + BK - 1) / BK;
-  dma.load(ks, 0, Kb(0));
-  dma.load(ks, BK, Kb(1));
-  dma.load(vs, 0, Vb(0));
+  dma_k.load(ks, 0, Kb(0));
+  dma_k.load(ks, BK, Kb(1));
+  dma_v.load(vs, 0, Vb(0));
   vm_drain();
   __syncthreads();
   f32x16 sA[2], sB[2];
@@ -279,8 +279,8 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
     constexpr int k1 = (P + 1) % 3, k2 = (P + 2) % 3;  // K stages of tiles j+1, j+2
     f32x16(&cur)[2] = pick<P>(sA, sB);
     f32x16(&nxt)[2] = pick<P + 1>(sA, sB);
-    dma.load(ks, (j + 2) * BK, Kb(k2));        // stage of tile j-1: free since the last barrier
-    dma.load(vs, (j + 1) * BK, Vb((P + 1) % 2));
+    dma_k.load(ks, (j + 2) * BK, Kb(k2));        // stage of tile j-1: free since the last barrier
+    dma_v.load(vs, (j + 1) * BK, Vb((P + 1) % 2));
     const uint16_t* Kn = Kb(k1);
     const uint16_t* Vc = Vb(P % 2);
     zero2(nxt);
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
   run_steps(nk, step);
 
   if (qrow < n) {
-    uint16_t* dst = O + base + (size_t)qrow * D;
+    uint16_t* dst = slice_base(O, S, it.bh, 3) + (size_t)qrow * S.sl[3];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -331,22 +331,22 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
   __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
 
   if ((int)blockIdx.x >= S.compute_blocks) {
-    zero_padded_rows<D>(S, dQ, nullptr);
+    zero_padded_rows<D>(S, dQ, 4, nullptr, 0);
     return;
   }
   Item it;
   if (!find_item(S, it)) return;
   const int n = it.n;
-  const size_t base = (size_t)it.bh * S.Lmax * D;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c2 = it.c2;
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
-  const TileDma<BK, D> dma(w, lane);
+  const TileDma<BK, D> dma_k(w, lane, S.sl[1]), dma_v(w, lane, S.sl[2]);
   auto Kb = [&](int i) { return lds + i * TILE; };
   auto Vb = [&](int i) { return lds + (3 + i) * TILE; };
-  const Slice qs(Q + base, n, D), ks(K + base, n, D), vs(V + base, n, D), gs(dO + base, n, D);
+  const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
+      vs(slice_base(V, S, it.bh, 2), n, S.sl[2]), gs(slice_base(dO, S, it.bh, 3), n, S.sl[3]);
 
   const int qrow = it.tile * BQ + 32 * w + l32;
   bf16x8 qf[D / 16], gf[D / 16];
@@ -357,9 +357,9 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
 
   const int nk = (n + BK - 1) / BK;
-  dma.load(ks, 0, Kb(0));
-  dma.load(ks, BK, Kb(1));
-  dma.load(vs, 0, Vb(0));
+  dma_k.load(ks, 0, Kb(0));
+  dma_k.load(ks, BK, Kb(1));
+  dma_v.load(vs, 0, Vb(0));
   vm_drain();
   __syncthreads();
   f32x16 sA[2], sB[2];
@@ -371,8 +371,8 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
     constexpr int kc = P % 3, k1 = (P + 1) % 3, k2 = (P + 2) % 3;
     f32x16(&cur)[2] = pick<P>(sA, sB);
     f32x16(&nxt)[2] = pick<P + 1>(sA, sB);
-    dma.load(ks, (j + 2) * BK, Kb(k2));
-    dma.load(vs, (j + 1) * BK, Vb((P + 1) % 2));
+    dma_k.load(ks, (j + 2) * BK, Kb(k2));
+    dma_v.load(vs, (j + 1) * BK, Vb((P + 1) % 2));
     const uint16_t* Kt = Kb(kc);
     const uint16_t* Kn = Kb(k1);
     const uint16_t* Vc = Vb(P % 2);
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
 
   if (qrow < n) {
     const float scale = S.out_scale;
-    uint16_t* dst = dQ + base + (size_t)qrow * D;
+    uint16_t* dst = slice_base(dQ, S, it.bh, 4) + (size_t)qrow * S.sl[4];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -424,22 +424,22 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   __shared__ __align__(16) uint16_t lds[6 * TILE];  // Q0 Q1 Q2 G0 G1 G2
 
   if ((int)blockIdx.x >= S.compute_blocks) {
-    zero_padded_rows<D>(S, dK, dV);
+    zero_padded_rows<D>(S, dK, 4, dV, 5);
     return;
   }
   Item it;
   if (!find_item(S, it)) return;
   const int n = it.n;
-  const size_t base = (size_t)it.bh * S.Lmax * D;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c2 = it.c2;
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
-  const TileDma<BQ, D> dma(w, lane);
+  const TileDma<BQ, D> dma_q(w, lane, S.sl[0]), dma_g(w, lane, S.sl[3]);
   auto Qb = [&](int i) { return lds + i * TILE; };
   auto Gb = [&](int i) { return lds + (3 + i) * TILE; };
-  const Slice qs(Q + base, n, D), ks(K + base, n, D), vs(V + base, n, D), gs(dO + base, n, D);
+  const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
+      vs(slice_base(V, S, it.bh, 2), n, S.sl[2]), gs(slice_base(dO, S, it.bh, 3), n, S.sl[3]);
 
   const int krow = it.tile * BKV + 32 * w + l32;
   bf16x8 kf[D / 16], vf[D / 16];
@@ -453,10 +453,10 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   }
 
   const int nq = (n + BQ - 1) / BQ;
-  dma.load(qs, 0, Qb(0));
-  dma.load(gs, 0, Gb(0));
-  dma.load(qs, BQ, Qb(1));
-  dma.load(gs, BQ, Gb(1));
+  dma_q.load(qs, 0, Qb(0));
+  dma_g.load(gs, 0, Gb(0));
+  dma_q.load(qs, BQ, Qb(1));
+  dma_g.load(gs, BQ, Gb(1));
   vm_drain();
   __syncthreads();
   f32x16 sA[NMB], dA[NMB], sB[NMB], dB[NMB];
@@ -472,8 +472,8 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     f32x16(&cd)[NMB] = pick<P>(dA, dB);
     f32x16(&ns)[NMB] = pick<P + 1>(sA, sB);
     f32x16(&nd)[NMB] = pick<P + 1>(dA, dB);
-    dma.load(qs, (j + 2) * BQ, Qb(k2));
-    dma.load(gs, (j + 2) * BQ, Gb(k2));
+    dma_q.load(qs, (j + 2) * BQ, Qb(k2));
+    dma_g.load(gs, (j + 2) * BQ, Gb(k2));
     const uint16_t* Qn = Qb(k1);
     const uint16_t* Gn = Gb(k1);
     const uint16_t* Qt = Qb(kc);
@@ -513,8 +513,8 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
 
   if (krow < n) {
     const float scale = S.out_scale;
-    uint16_t* dstk = dK + base + (size_t)krow * D;
-    uint16_t* dstv = dV + base + (size_t)krow * D;
+    uint16_t* dstk = slice_base(dK, S, it.bh, 4) + (size_t)krow * S.sl[4];
+    uint16_t* dstv = slice_base(dV, S, it.bh, 5) + (size_t)krow * S.sl[5];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll

@@ -54,6 +54,11 @@ struct Sched {
   int32_t zero_b0;               // first sequence zero-filled by this launch
   int32_t zero_nseq;             // sequences zero-filled by this launch (0: none)
   int32_t zero_n[kZeroSeqs];     // their valid lengths
+  // Element strides (sequence, head, row) of each tensor argument of the
+  // launch, in argument order; the head dimension is contiguous.
+  int64_t sb[6];
+  int64_t sh[6];
+  int32_t sl[6];
 };
 
 // Callable from kernels and from host-side checks of the schedule.

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for code in range(10):
+    for code in range(11):
         s = sa.status_str(code)
         assert isinstance(s, str) and s
     assert sa.status_str(0) == "ok"
