@@ -70,7 +70,7 @@ def load_traffic(kernel: str, workload: str, precision: str):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
-def time_workload(name, precision, steps, warmup, seed=0):
+def time_workload(name, precision, steps, warmup, seed=0, layout="bhld"):
     import torch
 
     import sigmoid_attention_amd as sa
@@ -80,9 +80,12 @@ def time_workload(name, precision, steps, warmup, seed=0):
     w = case["workload"]
     n = case["seqlens"]
     dev = torch.device("cuda:0")
-    q, k, v, do = (case[t].to(dev) for t in ("q", "k", "v", "do"))
+    if layout == "blhd":  # [B, Lmax, H, d] activations, as a model holds them
+        q, k, v, do = (case[t].permute(0, 2, 1, 3).contiguous().to(dev) for t in ("q", "k", "v", "do"))
+    else:
+        q, k, v, do = (case[t].to(dev) for t in ("q", "k", "v", "do"))
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
-    kw = dict(precision=precision)
+    kw = dict(precision=precision, layout=layout)
 
     def step(ev=None):
         if ev is not None:
@@ -120,7 +123,8 @@ def time_workload(name, precision, steps, warmup, seed=0):
         "kernel_avg_ms": avg, "kernel_median_ms": med, "kernel_min_ms": {k_: float(np.min(v_)) for k_, v_ in per.items()},
         "pair_flops": base,
         "fwd_flops": 4 * base, "bwd_flops": 10 * base,
-        "outputs": (o, dq, dk, dv), "case": case,
+        "outputs": tuple(t.permute(0, 2, 1, 3) if layout == "blhd" else t for t in (o, dq, dk, dv)),
+        "case": case,
     }
     return res
 
@@ -186,6 +190,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--precision", default="auto", choices=["auto", "fast", "split"])
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--layout", default="bhld", choices=["bhld", "blhd"],
+                    help="tensor layout handed to the library: [B,H,Lmax,d] or [B,Lmax,H,d] (strided path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -220,7 +226,7 @@ def main():
     name = a.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
     precision = a.precision if a.precision != "auto" else ("split" if w.scale_qkv > 1.0 else "fast")
-    r = time_workload(name, precision, a.steps, a.warmup)
+    r = time_workload(name, precision, a.steps, a.warmup, layout=a.layout)
     n = r["seqlens"]
     total = r["fwd_flops"] + r["bwd_flops"]
     value = tflops(total, r["step_ms"])
@@ -258,7 +264,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": name, "B": w.B, "H": w.H, "d": w.d, "Lmax": w.Lmax, "seqlens": [int(x) for x in n],
-            "precision": precision, "bias": "-ln(n_b)",
+            "precision": precision, "bias": "-ln(n_b)", "layout": a.layout,
             "valid_token_frac": round(float(np.sum(n)) / (w.B * w.Lmax), 4),
             "valid_pair_frac": round(float(np.sum(np.asarray(n, np.float64) ** 2)) / (w.B * w.Lmax ** 2), 4),
         },
