@@ -40,6 +40,8 @@ KERNEL_SOURCE = os.path.join(ROOT, "sigmoid_attention_amd", "csrc", "kernels.hip
 # forward: S = QK^T and PV (4); dK/dV kernel: S, dP, dV, dK (8); dQ kernel: dQ (2)
 # (its S and dP recompute what the dK/dV kernel already counts).  Sum: 14 = 4 + 10.
 KERNEL_FLOP_UNITS = {"fwd": 4, "bwd_dq": 2, "bwd_dkdv": 8}
+# The softmax comparison path adds a memory pass (delta = rowsum(dO * O)) that
+# counts no FLOPs; its other kernels follow the same convention.
 
 
 def pair_flops(seqlens, H, d):
@@ -70,7 +72,10 @@ def load_traffic(kernel: str, workload: str, precision: str):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
-def time_workload(name, precision, steps, warmup, seed=0, layout="bhld"):
+def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="sigmoid"):
+    """Time `steps` passes of forward + backward (HIP events around every
+    call, on the launch stream).  attn="softmax" times the softmax comparison
+    path on the same inputs and schedule: forward, the delta pass, dQ, dK/dV."""
     import torch
 
     import sigmoid_attention_amd as sa
@@ -86,35 +91,46 @@ def time_workload(name, precision, steps, warmup, seed=0, layout="bhld"):
         q, k, v, do = (case[t].to(dev) for t in ("q", "k", "v", "do"))
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
     kw = dict(precision=precision, layout=layout)
+    lse2 = delta = None
+    if attn == "softmax":
+        (B, H, L, _), _ = sa._binding.layout_strides(q, layout)
+        lse2 = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+        delta = torch.empty_like(lse2)
+    names = ("fwd", "bwd_dq", "bwd_dkdv") if attn == "sigmoid" else ("fwd", "bwd_prep", "bwd_dq", "bwd_dkdv")
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        sa.fwd(q, k, v, n, o=o, **kw)
-        if ev is not None:
-            ev[1].record()
-        sa.bwd_dq(q, k, v, do, n, dq=dq, **kw)
-        if ev is not None:
-            ev[2].record()
-        sa.bwd_dkdv(q, k, v, do, n, dk=dk, dv=dv, **kw)
-        if ev is not None:
-            ev[3].record()
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        if attn == "sigmoid":
+            sa.fwd(q, k, v, n, o=o, **kw)
+            mark(1)
+            sa.bwd_dq(q, k, v, do, n, dq=dq, **kw)
+            mark(2)
+            sa.bwd_dkdv(q, k, v, do, n, dk=dk, dv=dv, **kw)
+            mark(3)
+        else:
+            sa.softmax_fwd(q, k, v, n, o=o, lse2=lse2, **kw)
+            mark(1)
+            sa.softmax_bwd_prep(o, do, n, delta, **kw)
+            mark(2)
+            sa.softmax_bwd_dq(q, k, v, do, lse2, delta, n, dq, **kw)
+            mark(3)
+            sa.softmax_bwd_dkdv(q, k, v, do, lse2, delta, n, dk, dv, **kw)
+            mark(4)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     host_s = time.perf_counter() - t0
-    per = {"fwd": [], "bwd_dq": [], "bwd_dkdv": []}
-    for ev in events:
-        per["fwd"].append(ev[0].elapsed_time(ev[1]))
-        per["bwd_dq"].append(ev[1].elapsed_time(ev[2]))
-        per["bwd_dkdv"].append(ev[2].elapsed_time(ev[3]))
-    step_ms = events[0][0].elapsed_time(events[-1][3]) / steps
+    per = {kname: [ev[i].elapsed_time(ev[i + 1]) for ev in events] for i, kname in enumerate(names)}
+    step_ms = events[0][0].elapsed_time(events[-1][-1]) / steps
     base = pair_flops(n, w.H, w.d)
     avg = {kname: float(np.mean(v_)) for kname, v_ in per.items()}
     med = {kname: float(np.median(v_)) for kname, v_ in per.items()}
@@ -190,6 +206,10 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--precision", default="auto", choices=["auto", "fast", "split"])
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--attn", default="sigmoid", choices=["sigmoid", "softmax"],
+                    help="time the softmax comparison path instead of sigmoid attention")
+    ap.add_argument("--compare-softmax", action="store_true",
+                    help="also time the softmax path on the same workload (and sweep) and report ratios")
     ap.add_argument("--layout", default="bhld", choices=["bhld", "blhd"],
                     help="tensor layout handed to the library: [B,H,Lmax,d] or [B,Lmax,H,d] (strided path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -226,14 +246,14 @@ def main():
     name = a.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
     precision = a.precision if a.precision != "auto" else ("split" if w.scale_qkv > 1.0 else "fast")
-    r = time_workload(name, precision, a.steps, a.warmup, layout=a.layout)
+    r = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn=a.attn)
     n = r["seqlens"]
     total = r["fwd_flops"] + r["bwd_flops"]
     value = tflops(total, r["step_ms"])
     fwd_tf = tflops(r["fwd_flops"], r["kernel_avg_ms"]["fwd"])
-    bwd_tf = tflops(r["bwd_flops"], r["kernel_avg_ms"]["bwd_dq"] + r["kernel_avg_ms"]["bwd_dkdv"])
+    bwd_tf = tflops(r["bwd_flops"], sum(v_ for k_, v_ in r["kernel_avg_ms"].items() if k_.startswith("bwd")))
 
-    dominant = max(r["kernel_avg_ms"], key=r["kernel_avg_ms"].get)
+    dominant = max(KERNEL_FLOP_UNITS, key=r["kernel_avg_ms"].get)
     dom_flops = KERNEL_FLOP_UNITS[dominant] * r["pair_flops"]
     achieved = tflops(dom_flops, r["kernel_avg_ms"][dominant])
     roofline = {
@@ -249,6 +269,9 @@ def main():
                                                         r["kernel_avg_ms"][kname]), 2)}
             for kname in KERNEL_FLOP_UNITS},
     }
+    if "bwd_prep" in r["kernel_avg_ms"]:
+        roofline["per_kernel"]["bwd_prep"] = {"avg_ms": round(r["kernel_avg_ms"]["bwd_prep"], 5),
+                                              "median_ms": round(r["kernel_median_ms"]["bwd_prep"], 5)}
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -264,7 +287,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": name, "B": w.B, "H": w.H, "d": w.d, "Lmax": w.Lmax, "seqlens": [int(x) for x in n],
-            "precision": precision, "bias": "-ln(n_b)", "layout": a.layout,
+            "precision": precision, "bias": "-ln(n_b)" if a.attn == "sigmoid" else "none (softmax)",
+            "layout": a.layout, "attention": a.attn,
             "valid_token_frac": round(float(np.sum(n)) / (w.B * w.Lmax), 4),
             "valid_pair_frac": round(float(np.sum(np.asarray(n, np.float64) ** 2)) / (w.B * w.Lmax ** 2), 4),
         },
@@ -281,14 +305,23 @@ def main():
         sweep = {}
         base_ms = None
         for sw in ("sweep_b16h16d64_l4096_pad00", "sweep_b16h16d64_l4096_pad25", "sweep_b16h16d64_l4096_pad50"):
-            rs = time_workload(sw, "fast", max(5, a.steps // 2), 2)
+            rs = time_workload(sw, "fast", max(5, a.steps // 2), 2, attn=a.attn)
             ws = rs["workload"]
             fwd_ms = rs["kernel_avg_ms"]["fwd"]
             step_ms = rs["step_ms"]
             if base_ms is None:
                 base_ms = (fwd_ms, step_ms)
             dense_pairs = covered_pairs([ws.Lmax] * ws.B, ws.H, 128, 64)
-            sweep[sw] = {
+            if a.compare_softmax:
+                rc = time_workload(sw, "fast", max(5, a.steps // 2), 2, attn="softmax")
+                cmp_ = {"softmax_fwd_tflops": round(tflops(rc["fwd_flops"], rc["kernel_avg_ms"]["fwd"]), 2),
+                        "softmax_fwd_bwd_tflops": round(tflops(rc["fwd_flops"] + rc["bwd_flops"], rc["step_ms"]), 2),
+                        "sigmoid_fwd_speedup": round(rc["kernel_avg_ms"]["fwd"] / fwd_ms, 4),
+                        "sigmoid_step_speedup": round(rc["step_ms"] / step_ms, 4)}
+                del rc
+            else:
+                cmp_ = {}
+            sweep[sw] = {**cmp_,
                 "seqlens": [int(x) for x in rs["seqlens"]],
                 "padding": round(1 - float(np.sum(rs["seqlens"])) / (ws.B * ws.Lmax), 4),
                 "fwd_tflops": round(tflops(rs["fwd_flops"], fwd_ms), 2),
@@ -303,7 +336,20 @@ def main():
             torch.cuda.empty_cache()
         out["padding_sweep"] = sweep
 
-    if not a.no_cpu_baseline:
+    if a.compare_softmax and a.attn == "sigmoid":
+        rc = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn="softmax")
+        out["softmax_comparison"] = {
+            "value": round(tflops(total, rc["step_ms"]), 2),
+            "fwd_tflops": round(tflops(rc["fwd_flops"], rc["kernel_avg_ms"]["fwd"]), 2),
+            "bwd_tflops": round(tflops(rc["bwd_flops"], sum(v_ for k_, v_ in rc["kernel_avg_ms"].items()
+                                                            if k_.startswith("bwd"))), 2),
+            "kernel_avg_ms": {k_: round(v_, 5) for k_, v_ in rc["kernel_avg_ms"].items()},
+            "sigmoid_fwd_speedup": round(rc["kernel_avg_ms"]["fwd"] / r["kernel_avg_ms"]["fwd"], 4),
+            "sigmoid_step_speedup": round(rc["step_ms"] / r["step_ms"], 4),
+        }
+        del rc
+
+    if not a.no_cpu_baseline and a.attn == "sigmoid":
         rec, worst = cpu_baseline(r["case"], r["outputs"], a.cpu_seconds)
         out["cpu_baseline"] = {k_: v_ for k_, v_ in rec.items() if k_ != "seconds"}
         out["parity_worst_ratio_on_cpu_sample"] = round(worst, 4)

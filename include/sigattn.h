@@ -143,6 +143,33 @@ sigattn_status sigattn_bwd_dq(const sigattn_args *args, const void *q, const voi
 sigattn_status sigattn_bwd_dkdv(const sigattn_args *args, const void *q, const void *k,
                                 const void *v, const void *dout, void *dk, void *dv);
 
+/* Softmax attention on the same padded batches and schedule: the mechanism
+ * sigmoid attention replaces, provided to compare the two on equal terms
+ * ("Better Models, Faster Training: Sigmoid Attention for single-cell
+ * Foundation Models", summary §4A, compares the sigmoid kernel with a softmax
+ * FlashAttention kernel; the FlashAttention section of "Transformer
+ * Attention機構の効率化と最新派生モデル" describes the tiled softmax with a
+ * per-query log-sum-exp).  P = softmax over each query's valid keys of
+ * Q K^T / sqrt(d); a constant bias cancels in a softmax, so bias_mode and
+ * bias_arg are validated but have no effect.  lse2 and delta are fp32
+ * [B, H, Lmax] contiguous arrays, 16-byte aligned:
+ *   lse2_i  = log2 sum_j 2^(x_ij), x_ij = q_i.k_j * log2(e) / sqrt(d)  (the
+ *             forward's per-row normaliser, base 2; 0 on padded rows),
+ *   delta_i = sum_c dO_ic O_ic                    (0 on padded rows).
+ * The backward is dV = P^T dO, dS = P * (dO V^T - delta), dQ = dS K / sqrt(d),
+ * dK = dS^T Q / sqrt(d).  Tensor strides work as for the sigmoid calls
+ * (args->strides entries in argument order, lse2/delta excluded). */
+sigattn_status sigattn_softmax_fwd(const sigattn_args *args, const void *q, const void *k,
+                                   const void *v, void *o, float *lse2);
+sigattn_status sigattn_softmax_bwd_prep(const sigattn_args *args, const void *o,
+                                        const void *dout, float *delta);
+sigattn_status sigattn_softmax_bwd_dq(const sigattn_args *args, const void *q, const void *k,
+                                      const void *v, const void *dout, const float *lse2,
+                                      const float *delta, void *dq);
+sigattn_status sigattn_softmax_bwd_dkdv(const sigattn_args *args, const void *q, const void *k,
+                                        const void *v, const void *dout, const float *lse2,
+                                        const float *delta, void *dk, void *dv);
+
 /* Runs every check the compute call for pass p would run (shape, lengths,
  * bias, precision, null pointers, alignment, strides, aliasing) on the
  * call's tensor arguments, given in argument order (fwd: q, k, v, o; dq: q,

@@ -59,21 +59,26 @@ def head_forward(q, k, v):
     return p @ v, row_logsumexp(x)
 
 
-def head_backward(q, k, v, do):
+def head_backward(q, k, v, do, delta=None):
     """dQ, dK, dV of l = sum(O * dO) on the valid rows, through the dense row
-    Jacobian of the softmax."""
+    Jacobian of the softmax.  The row term sum_k P_ik dP_ik equals
+    rowsum(dO * O); `delta` (one value per row) replaces it, to model a
+    backward that forms it from a stored, rounded O."""
     s = 1.0 / math.sqrt(q.shape[1])
     x = s * (q @ k.T)
     p = row_softmax(x)
     dv = p.T @ do
     dp = do @ v.T
-    dx = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+    row = np.sum(p * dp, axis=-1, keepdims=True) if delta is None else np.asarray(delta)[:, None]
+    dx = p * (dp - row)
     return s * (dx @ k), s * (dx.T @ q), dv
 
 
-def attention(q, k, v, seqlens, do=None):
+def attention(q, k, v, seqlens, do=None, round_o=None):
     """Whole padded batch, float64 [B, H, Lmax, d] inputs.  Returns "o" and
-    "lse" ([B, H, Lmax]) and, with do, "dq", "dk", "dv"; padded rows 0."""
+    "lse" ([B, H, Lmax]) and, with do, "dq", "dk", "dv"; padded rows 0.
+    round_o: optional function applied to each head's O before the backward
+    forms its row term from it (rowsum(dO * round_o(O)))."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -94,6 +99,9 @@ def attention(q, k, v, seqlens, do=None):
             qv, kv, vv = q[bi, h, :n], k[bi, h, :n], v[bi, h, :n]
             out["o"][bi, h, :n], out["lse"][bi, h, :n] = head_forward(qv, kv, vv)
             if do is not None:
-                dq, dk, dv = head_backward(qv, kv, vv, do[bi, h, :n])
+                delta = None
+                if round_o is not None:
+                    delta = np.sum(do[bi, h, :n] * round_o(out["o"][bi, h, :n]), axis=-1)
+                dq, dk, dv = head_backward(qv, kv, vv, do[bi, h, :n], delta)
                 out["dq"][bi, h, :n], out["dk"][bi, h, :n], out["dv"][bi, h, :n] = dq, dk, dv
     return out

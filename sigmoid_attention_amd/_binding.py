@@ -30,7 +30,8 @@ STATUS_NAMES = {
 LAYOUTS = {"bhld": (0, 1, 2, 3), "blhd": (0, 2, 1, 3)}
 
 EXPORTED = ("sigattn_fwd", "sigattn_bwd_dq", "sigattn_bwd_dkdv", "sigattn_status_str",
-            "sigattn_plan_stats", "sigattn_tile_shape", "sigattn_validate")
+            "sigattn_plan_stats", "sigattn_tile_shape", "sigattn_validate", "sigattn_softmax_fwd",
+            "sigattn_softmax_bwd_prep", "sigattn_softmax_bwd_dq", "sigattn_softmax_bwd_dkdv")
 
 
 class SigattnStrides(ctypes.Structure):
@@ -84,6 +85,13 @@ def load() -> ctypes.CDLL:
     lib.sigattn_tile_shape.restype = ctypes.c_int
     lib.sigattn_validate.argtypes = [ap, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
     lib.sigattn_validate.restype = ctypes.c_int
+    lib.sigattn_softmax_fwd.argtypes = [ap, vp, vp, vp, vp, vp]
+    lib.sigattn_softmax_bwd_prep.argtypes = [ap, vp, vp, vp]
+    lib.sigattn_softmax_bwd_dq.argtypes = [ap, vp, vp, vp, vp, vp, vp, vp]
+    lib.sigattn_softmax_bwd_dkdv.argtypes = [ap, vp, vp, vp, vp, vp, vp, vp, vp]
+    for f in (lib.sigattn_softmax_fwd, lib.sigattn_softmax_bwd_prep, lib.sigattn_softmax_bwd_dq,
+              lib.sigattn_softmax_bwd_dkdv):
+        f.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -212,6 +220,100 @@ def bwd_dkdv(q, k, v, dout, seqlens, dk=None, dv=None, bias_mode="seqlen", bias_
                                        dout.data_ptr(), dk.data_ptr(), dv.data_ptr()), "sigattn_bwd_dkdv")
     del keep
     return dk, dv
+
+
+def _rows_like(t, layout):
+    """fp32 [B, H, Lmax] per-row array for a tensor in `layout` order."""
+    import torch
+
+    (B, H, L, d), _ = layout_strides(t, layout)
+    return torch.empty((B, H, L), dtype=torch.float32, device=t.device)
+
+
+def _check_rows(x, like, layout):
+    import torch
+
+    (B, H, L, _), _ = layout_strides(like, layout)
+    if x.dtype != torch.float32 or tuple(x.shape) != (B, H, L) or not x.is_contiguous() or x.device != like.device:
+        raise ValueError("per-row arrays must be contiguous float32 [B, H, Lmax] on the tensors' device")
+
+
+def softmax_fwd(q, k, v, seqlens, o=None, lse2=None, precision="fast", stream=None, layout="bhld"):
+    """Softmax attention forward on the same schedule (comparison path).
+    Returns (O, lse2); lse2 is the base-2 log-sum-exp of each valid row's
+    scores scaled by log2(e)/sqrt(d), fp32 [B, H, Lmax], 0 on padded rows."""
+    import torch
+
+    if o is None:
+        o = _new_like(q)
+    if lse2 is None:
+        lse2 = _rows_like(q, layout)
+    _check_rows(lse2, q, layout)
+    args, keep = _tensor_args((q, k, v, o), seqlens, "seqlen", 0.0, precision, stream, layout)
+    with torch.cuda.device(q.device):
+        _check(load().sigattn_softmax_fwd(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          o.data_ptr(), lse2.data_ptr()), "sigattn_softmax_fwd")
+    del keep
+    return o, lse2
+
+
+def softmax_bwd_prep(o, dout, seqlens, delta=None, precision="fast", stream=None, layout="bhld"):
+    """delta = rowsum(dO * O), fp32 [B, H, Lmax], 0 on padded rows."""
+    import torch
+
+    delta = _rows_like(o, layout) if delta is None else delta
+    _check_rows(delta, o, layout)
+    args, keep = _tensor_args((o, dout), seqlens, "seqlen", 0.0, precision, stream, layout)
+    with torch.cuda.device(o.device):
+        _check(load().sigattn_softmax_bwd_prep(ctypes.byref(args), o.data_ptr(), dout.data_ptr(), delta.data_ptr()),
+               "sigattn_softmax_bwd_prep")
+    del keep
+    return delta
+
+
+def softmax_bwd_dq(q, k, v, dout, lse2, delta, seqlens, dq=None, precision="fast", stream=None, layout="bhld"):
+    """dQ of the softmax path."""
+    import torch
+
+    dq = _new_like(q) if dq is None else dq
+    for x in (lse2, delta):
+        _check_rows(x, q, layout)
+    args, keep = _tensor_args((q, k, v, dout, dq), seqlens, "seqlen", 0.0, precision, stream, layout)
+    with torch.cuda.device(q.device):
+        _check(load().sigattn_softmax_bwd_dq(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                             dout.data_ptr(), lse2.data_ptr(), delta.data_ptr(), dq.data_ptr()),
+               "sigattn_softmax_bwd_dq")
+    del keep
+    return dq
+
+
+def softmax_bwd_dkdv(q, k, v, dout, lse2, delta, seqlens, dk=None, dv=None, precision="fast", stream=None,
+                     layout="bhld"):
+    """dK and dV of the softmax path."""
+    import torch
+
+    dk = _new_like(k) if dk is None else dk
+    dv = _new_like(v) if dv is None else dv
+    for x in (lse2, delta):
+        _check_rows(x, q, layout)
+    args, keep = _tensor_args((q, k, v, dout, dk, dv), seqlens, "seqlen", 0.0, precision, stream, layout)
+    with torch.cuda.device(q.device):
+        _check(load().sigattn_softmax_bwd_dkdv(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                               dout.data_ptr(), lse2.data_ptr(), delta.data_ptr(), dk.data_ptr(),
+                                               dv.data_ptr()), "sigattn_softmax_bwd_dkdv")
+    del keep
+    return dk, dv
+
+
+def softmax_bwd(q, k, v, o, dout, lse2, seqlens, dq=None, dk=None, dv=None, delta=None, precision="fast",
+                stream=None, layout="bhld"):
+    """Softmax attention backward: delta = rowsum(dO * O), then the dQ and
+    the dK/dV kernels.  Returns (dQ, dK, dV)."""
+    kw = dict(precision=precision, stream=stream, layout=layout)
+    delta = softmax_bwd_prep(o, dout, seqlens, delta, **kw)
+    dq = softmax_bwd_dq(q, k, v, dout, lse2, delta, seqlens, dq, **kw)
+    dk, dv = softmax_bwd_dkdv(q, k, v, dout, lse2, delta, seqlens, dk, dv, **kw)
+    return dq, dk, dv
 
 
 def plan_stats(B, H, Lmax, d, seqlens, pass_="fwd", bias_mode="seqlen", bias_arg=0.0, precision="fast"):

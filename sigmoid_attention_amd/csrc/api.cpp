@@ -168,6 +168,31 @@ sigattn_status check_ptrs(const sigattn_args* a, const void* const* in, int nin,
   return SIGATTN_OK;
 }
 
+// fp32 [B, H, Lmax] per-row arrays of the softmax path: null, alignment, and
+// no overlap between an output (row array or tensor) and anything else.
+sigattn_status check_rows(const sigattn_args* a, const void* const* t, int nt, int nt_in, const void* const* r,
+                          int nr, int nr_in) {
+  for (int i = 0; i < nr; ++i) {
+    if (!r[i]) return SIGATTN_ERR_NULL;
+    if ((uintptr_t)r[i] % 16) return SIGATTN_ERR_ALIGN;
+  }
+  const uintptr_t bytes = (uintptr_t)a->B * a->H * a->Lmax * 4;
+  const std::vector<View> v = views(a, t, nt);
+  for (int i = 0; i < nr; ++i) {
+    const uintptr_t lo = (uintptr_t)r[i], hi = lo + bytes;
+    for (int j = 0; j < nr; ++j)
+      if (j != i && (i >= nr_in || j >= nr_in) && lo < (uintptr_t)r[j] + bytes && (uintptr_t)r[j] < hi)
+        return SIGATTN_ERR_ALIAS;
+    for (int j = 0; j < nt; ++j) {
+      if (i < nr_in && j < nt_in) continue;  // input against input
+      uintptr_t tl, th;
+      span(a, v[j], tl, th);
+      if (lo < th && tl < hi) return SIGATTN_ERR_ALIAS;
+    }
+  }
+  return SIGATTN_OK;
+}
+
 // Strides of the call's tensor arguments, in argument order, into the schedule.
 void set_strides(const sigattn_args* a, const void* const* t, int n, Launch& L) {
   const std::vector<View> v = views(a, t, n);
@@ -257,6 +282,88 @@ sigattn_status sigattn_validate(const sigattn_args* a, int32_t pass, const void*
   const int nout = pass == SIGATTN_PASS_BWD_DKDV ? 2 : 1;
   void* out[2] = {const_cast<void*>(t[nin]), nout == 2 ? const_cast<void*>(t[nin + 1]) : nullptr};
   return check_ptrs(a, t, nin, out, nout);
+}
+
+sigattn_status sigattn_softmax_fwd(const sigattn_args* a, const void* q, const void* k, const void* v, void* o,
+                                   float* lse2) {
+  sigattn_status s = check_args(a);
+  if (s != SIGATTN_OK) return s;
+  const void* in[] = {q, k, v};
+  void* out[] = {o};
+  if ((s = check_ptrs(a, in, 3, out, 1)) != SIGATTN_OK) return s;
+  const void* t[] = {q, k, v, o};
+  const void* r[] = {lse2};
+  if ((s = check_rows(a, t, 4, 3, r, 1, 0)) != SIGATTN_OK) return s;
+  const bool split = a->precision == SIGATTN_PREC_SPLIT;
+  return run(a, SIGATTN_PASS_FWD, t, 4, [&](const Launch& L) {
+    return sigattn::launch_softmax_fwd(a->d, split, L, q, k, v, o, lse2, (hipStream_t)a->stream);
+  });
+}
+
+sigattn_status sigattn_softmax_bwd_prep(const sigattn_args* a, const void* o, const void* dout, float* delta) {
+  sigattn_status s = check_args(a);
+  if (s != SIGATTN_OK) return s;
+  const void* t[] = {o, dout};
+  for (const void* p : t) {
+    if (!p) return SIGATTN_ERR_NULL;
+    if ((uintptr_t)p % 16) return SIGATTN_ERR_ALIGN;
+  }
+  const std::vector<View> v = views(a, t, 2);
+  for (const View& x : v)
+    if (x.sb < 0 || x.sh < 0 || x.sl < 0 || x.sb % 8 || x.sh % 8 || x.sl % 8 || x.sl < a->d) return SIGATTN_ERR_STRIDE;
+  const void* r[] = {delta};
+  if ((s = check_rows(a, t, 2, 2, r, 1, 0)) != SIGATTN_OK) return s;
+  (void)hipGetLastError();
+  sigattn::PrepArgs A;
+  A.H = a->H;
+  A.Lmax = a->Lmax;
+  for (int i = 0; i < 2; ++i) {
+    A.sb[i] = v[i].sb;
+    A.sh[i] = v[i].sh;
+    A.sl[i] = (int32_t)v[i].sl;
+  }
+  for (int32_t b0 = 0; b0 < a->B; b0 += sigattn::kPrepSeqs) {
+    A.b0 = b0;
+    A.nb = std::min(a->B - b0, sigattn::kPrepSeqs);
+    for (int32_t i = 0; i < A.nb; ++i) A.n[i] = a->seqlens[b0 + i];
+    if (sigattn::launch_softmax_prep(a->d, A, o, dout, delta, (hipStream_t)a->stream) != hipSuccess)
+      return SIGATTN_ERR_HIP;
+  }
+  return SIGATTN_OK;
+}
+
+sigattn_status sigattn_softmax_bwd_dq(const sigattn_args* a, const void* q, const void* k, const void* v,
+                                      const void* dout, const float* lse2, const float* delta, void* dq) {
+  sigattn_status s = check_args(a);
+  if (s != SIGATTN_OK) return s;
+  const void* in[] = {q, k, v, dout};
+  void* out[] = {dq};
+  if ((s = check_ptrs(a, in, 4, out, 1)) != SIGATTN_OK) return s;
+  const void* t[] = {q, k, v, dout, dq};
+  const void* r[] = {lse2, delta};
+  if ((s = check_rows(a, t, 5, 4, r, 2, 2)) != SIGATTN_OK) return s;
+  const bool split = a->precision == SIGATTN_PREC_SPLIT;
+  return run(a, SIGATTN_PASS_BWD_DQ, t, 5, [&](const Launch& L) {
+    return sigattn::launch_softmax_dq(a->d, split, L, q, k, v, dout, lse2, delta, dq, (hipStream_t)a->stream);
+  });
+}
+
+sigattn_status sigattn_softmax_bwd_dkdv(const sigattn_args* a, const void* q, const void* k, const void* v,
+                                        const void* dout, const float* lse2, const float* delta, void* dk,
+                                        void* dv) {
+  sigattn_status s = check_args(a);
+  if (s != SIGATTN_OK) return s;
+  const void* in[] = {q, k, v, dout};
+  void* out[] = {dk, dv};
+  if ((s = check_ptrs(a, in, 4, out, 2)) != SIGATTN_OK) return s;
+  const void* t[] = {q, k, v, dout, dk, dv};
+  const void* r[] = {lse2, delta};
+  if ((s = check_rows(a, t, 6, 4, r, 2, 2)) != SIGATTN_OK) return s;
+  const bool split = a->precision == SIGATTN_PREC_SPLIT;
+  return run(a, SIGATTN_PASS_BWD_DKDV, t, 6, [&](const Launch& L) {
+    return sigattn::launch_softmax_dkdv(a->d, split, L, q, k, v, dout, lse2, delta, dk, dv,
+                                        (hipStream_t)a->stream);
+  });
 }
 
 const char* sigattn_status_str(sigattn_status s) {

@@ -31,6 +31,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -172,6 +173,27 @@ struct TileDma {
   }
 };
 
+// Direct global -> LDS loading of a per-row fp32 array (one value per row):
+// lane L loads row row0 + L, so one 64-lane instruction fills 64 rows.  Rows
+// >= n read as 0.  The LDS destination must be wave-uniform.
+template <int ROWS>
+struct RowDma {
+  static_assert(ROWS == 64, "one 64-lane instruction per tile");
+  const float* base;
+  int n, off;
+  __device__ __forceinline__ RowDma(const float* base_, int n_, int lane) : base(base_), n(n_), off(4 * lane) {}
+  __device__ __forceinline__ void load(int row0, float* dst) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int rows = n > row0 ? n - row0 : 0;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0), 0, rows * 4, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, off, 0, 0, 0);
+#endif
+  }
+};
+
+__device__ __forceinline__ f32x8 cat8(f32x4 a, f32x4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
+
 // Wait until this wave's outstanding global loads (including LDS DMA) landed.
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -244,7 +266,8 @@ struct FragAddr {
 // two writers.
 template <int D>
 __device__ __forceinline__ void zero_padded_rows(const Sched& S, uint16_t* __restrict__ o1, int t1,
-                                                 uint16_t* __restrict__ o2, int t2) {
+                                                 uint16_t* __restrict__ o2, int t2,
+                                                 float* __restrict__ rows = nullptr) {
   const int zb = (int)blockIdx.x - S.compute_blocks;
   const int bhl = zb / kZeroSplit, part = zb % kZeroSplit;
   const int bl = bhl / S.H;
@@ -261,6 +284,10 @@ __device__ __forceinline__ void zero_padded_rows(const Sched& S, uint16_t* __res
     *(u32x4*)(p1 + (size_t)row * rs1 + col) = z;
     if (o2) *(u32x4*)(p2 + (size_t)row * rs2 + col) = z;
   }
+  // a per-row fp32 output, contiguous [B, H, Lmax] (the softmax lse2)
+  if (rows)
+    for (int row = n + part * (int)blockDim.x + (int)threadIdx.x; row < S.Lmax; row += kZeroSplit * (int)blockDim.x)
+      rows[(size_t)bh * S.Lmax + row] = 0.0f;
 }
 
 // Work item of this workgroup (see plan.h); false for idle blocks.  The

@@ -78,6 +78,55 @@ __device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[NB], const f32
   }
 }
 
+// ---------------------------------------------------------------------------
+// Softmax attention, the workload sigmoid attention replaces, on the same
+// schedule (comparison path).  Per query row the forward keeps a running
+// maximum and sum and hands the base-2 log-sum-exp of the row's scaled scores,
+// lse2 = log2 sum_j 2^(s_ij c1s) with c1s = log2(e)/sqrt(d), to the backward,
+// where P = 2^(s c1s - lse2) and dS = P (dP - delta), delta = rowsum(dO * O).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ constexpr float softmax_c1() {
+  return (float)(1.4426950408889634074 / (D == 64 ? 8.0 : 11.313708498984760390));
+}
+
+// dS for K-chunk c when queries are the lane's column (dQ kernel): one lse2 and
+// delta per lane.
+template <int D, bool SPLIT, int NB>
+__device__ __forceinline__ void dsoftmax_chunk_col(const f32x16 (&sc)[NB], const f32x16 (&dp)[NB], int c, float lse2,
+                                                   float dlt, bf16x8& dh, bf16x8& dl) {
+  const f32x8 sv = chunk8(sc[c >> 1], c & 1), gv = chunk8(dp[c >> 1], c & 1);
+  f32x8 ds;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t], softmax_c1<D>(), -lse2));
+    ds[t] = p * (gv[t] - dlt);
+  }
+  dh = to_bf16x8(ds);
+  if (SPLIT) dl = to_bf16x8(ds - to_f32x8(dh));
+}
+
+// P and dS for K-chunk c when queries are rows (dK/dV kernel): lse2 and delta
+// of the chunk's eight rows held by the lane (rows 16c + 4hf + {0..3} and
+// 16c + 8 + 4hf + {0..3}, in register order).
+template <int D, bool SPLIT, int NB>
+__device__ __forceinline__ void dsoftmax_chunk_row(const f32x16 (&sc)[NB], const f32x16 (&dp)[NB], int c,
+                                                   const f32x8& lse8, const f32x8& dlt8, bf16x8& dh, bf16x8& dl,
+                                                   bf16x8& ph, bf16x8& pl) {
+  const f32x8 sv = chunk8(sc[c >> 1], c & 1), gv = chunk8(dp[c >> 1], c & 1);
+  f32x8 p8, ds;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t], softmax_c1<D>(), -lse8[t]));
+    p8[t] = p;
+    ds[t] = p * (gv[t] - dlt8[t]);
+  }
+  dh = to_bf16x8(ds);
+  if (SPLIT) dl = to_bf16x8(ds - to_f32x8(dh));
+  ph = to_bf16x8(p8);
+  if (SPLIT) pl = to_bf16x8(p8 - to_f32x8(ph));
+}
+
 // Store 4 consecutive fp32 values of an output row as bf16 (8 bytes).
 __device__ __forceinline__ void store4(uint16_t* dst, const f32x16& acc, int i, float scale) {
   f32x8 v8;
@@ -317,16 +366,141 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
 }
 
 // ---------------------------------------------------------------------------
+// Softmax forward (comparison path).  Same items, tiles and LDS pipeline as
+// the sigmoid forward.  Per query (the lane's column of S^T) a running maximum
+// m and running sum l, in base 2: per tile, the maximum over the lane's 32
+// keys and its partner half's, m' = max(m, c1s * max), O and l scaled by
+// 2^(m - m'), then P = 2^(s c1s - m').  Keys at or beyond n_b only occur in
+// the last tile and are set to -inf there (their zero-filled rows would
+// otherwise join the normalisation).  Epilogue: O / l and lse2 = m + log2 l.
+// ---------------------------------------------------------------------------
+template <int D, bool SPLIT>
+__device__ __forceinline__ void softmax_chunk(const f32x16 (&sc)[2], int c, float m, float& l, bf16x8& hi,
+                                              bf16x8& lo) {
+  f32x8 p = chunk8(sc[c >> 1], c & 1);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[t], softmax_c1<D>(), -m));
+    l += p[t];
+  }
+  hi = to_bf16x8(p);
+  if (SPLIT) lo = to_bf16x8(p - to_f32x8(hi));
+}
+
+// Scores of keys >= nv (tile-relative) to -inf; lane half hf holds keys
+// 32b + 8(r/4) + 4hf + r%4 in register r of block b.
+__device__ __forceinline__ void mask_keys(f32x16 (&sc)[2], int nv, int hf) {
+  const int lim = nv - 4 * hf;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * b + 8 * (r >> 2) + (r & 3) >= lim) sc[b][r] = -__builtin_inff();
+}
+
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd_softmax_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, const Sched S) {
+  constexpr int BQ = 128, BK = kInner, TILE = BK * D;
+  __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
+
+  if ((int)blockIdx.x >= S.compute_blocks) {
+    zero_padded_rows<D>(S, O, 3, nullptr, 0, LSE);
+    return;
+  }
+  Item it;
+  if (!find_item(S, it)) return;
+  const int n = it.n;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const TrFrag<D> tr(lane);
+  const FragAddr<D> fa(l32, hf);
+  const TileDma<BK, D> dma_k(w, lane, S.sl[1]), dma_v(w, lane, S.sl[2]);
+  auto Kb = [&](int i) { return lds + i * TILE; };
+  auto Vb = [&](int i) { return lds + (3 + i) * TILE; };
+  const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
+      vs(slice_base(V, S, it.bh, 2), n, S.sl[2]);
+
+  const int qrow = it.tile * BQ + 32 * w + l32;
+  bf16x8 qf[D / 16];
+  load_bfrag<D>(qf, qs, qrow, hf);
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+  float m = -__builtin_inff(), l = 0.0f;
+
+  const int nk = (n + BK - 1) / BK;
+  dma_k.load(ks, 0, Kb(0));
+  dma_k.load(ks, BK, Kb(1));
+  dma_v.load(vs, 0, Vb(0));
+  vm_drain();
+  __syncthreads();
+  f32x16 sA[2], sB[2];
+  zero2(sA);
+  score_steps<D>(sA, Kb(0), qf, 0, D / 16, fa);
+
+  auto step = [&](auto phase, int j) {
+    constexpr int P = decltype(phase)::value;
+    constexpr int k1 = (P + 1) % 3, k2 = (P + 2) % 3;
+    f32x16(&cur)[2] = pick<P>(sA, sB);
+    f32x16(&nxt)[2] = pick<P + 1>(sA, sB);
+    dma_k.load(ks, (j + 2) * BK, Kb(k2));
+    dma_v.load(vs, (j + 1) * BK, Vb((P + 1) % 2));
+    const uint16_t* Kn = Kb(k1);
+    const uint16_t* Vc = Vb(P % 2);
+    zero2(nxt);
+    if (j == nk - 1) mask_keys(cur, n - j * BK, hf);
+    float mt = cur[0][0];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = __builtin_fmaxf(mt, cur[b][r]);
+    mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = __builtin_fmaxf(m, mt * softmax_c1<D>());
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+    l *= alpha;
+    m = mn;
+    bf16x8 ph[4], pl[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      softmax_chunk<D, SPLIT>(cur, c, mn, l, ph[c], pl[c]);
+      if (c > 0) value_chunk<D, SPLIT>(acc, tr, Vc, c - 1, ph[c - 1], pl[c - 1]);
+    }
+    value_chunk<D, SPLIT>(acc, tr, Vc, 3, ph[3], pl[3]);
+    score_steps<D>(nxt, Kn, qf, 0, D / 16, fa);
+    vm_drain();
+    __syncthreads();
+  };
+  run_steps(nk, step);
+
+  l += __shfl_xor(l, 32);
+  if (qrow < n) {
+    const float inv = __builtin_amdgcn_rcpf(l);
+    uint16_t* dst = slice_base(O, S, it.bh, 3) + (size_t)qrow * S.sl[3];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store4(dst + 32 * db + 8 * i + 4 * hf, acc[db], i, inv);
+    if (hf == 0) LSE[(size_t)it.bh * S.Lmax + qrow] = m + __builtin_amdgcn_logf(l);
+  }
+  // rows at or beyond n_b get lse2 = 0 from the trailing workgroups
+}
+
+// ---------------------------------------------------------------------------
 // Backward, dQ.  Item = (b, h, 128-query tile).  Inner loop: 64-key tiles j.
 // Per wave (32 queries): S^T_j = K_j . Q^T, dP^T_j = V_j . dO^T,
 // dS^T_j = dP^T_j * P(1-P), dQ^T (d x 32 queries) += K_j^T . dS^T_j.
 // LDS: K in 3 stages (tile j: transposing reads for dQ; tile j+1: scores;
 // tile j+2: loading), V in 2 stages (tile j: dP; tile j+1: loading).
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool SOFTMAX = false>
 __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, const Sched S) {
+    const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, const float* __restrict__ LSE,
+    const float* __restrict__ DELTA, const Sched S) {
   constexpr int BQ = 128, BK = kInner, TILE = BK * D;
   __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
 
@@ -355,6 +529,13 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+  float lse2 = 0.0f, dlt = 0.0f;  // softmax: this lane's query row
+  if constexpr (SOFTMAX) {
+    if (qrow < n) {
+      lse2 = LSE[(size_t)it.bh * S.Lmax + qrow];
+      dlt = DELTA[(size_t)it.bh * S.Lmax + qrow];
+    }
+  }
 
   const int nk = (n + BK - 1) / BK;
   dma_k.load(ks, 0, Kb(0));
@@ -384,7 +565,10 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), fa);  // MFMA: tile j+1
-      dsigmoid_chunk<D, SPLIT, false>(cur, dp, c, c2, dh[c], dl[c], unused_h, unused_l);
+      if constexpr (SOFTMAX)
+        dsoftmax_chunk_col<D, SPLIT>(cur, dp, c, lse2, dlt, dh[c], dl[c]);
+      else
+        dsigmoid_chunk<D, SPLIT, false>(cur, dp, c, c2, dh[c], dl[c], unused_h, unused_l);
       if (c > 0) value_chunk<D, SPLIT>(acc, tr, Kt, c - 1, dh[c - 1], dl[c - 1]);
     }
     value_chunk<D, SPLIT>(acc, tr, Kt, 3, dh[3], dl[3]);
@@ -415,13 +599,15 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
 // latency is covered; the next tile's S and dP follow, with the fragments of
 // each K-step read one step ahead.
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool SOFTMAX = false>
 __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    const Sched S) {
+    const float* __restrict__ LSE, const float* __restrict__ DELTA, const Sched S) {
   constexpr int BKV = 128, BQ = DkdvCfg<D>::BQ, TILE = BQ * D, NMB = BQ / 32, NC = BQ / 16;
   __shared__ __align__(16) uint16_t lds[6 * TILE];  // Q0 Q1 Q2 G0 G1 G2
+  // softmax: lse2 and delta of each inner tile's rows, 3 stages
+  __shared__ __align__(16) float rowv[SOFTMAX ? 6 * BQ : 4];
 
   if ((int)blockIdx.x >= S.compute_blocks) {
     zero_padded_rows<D>(S, dK, 4, dV, 5);
@@ -453,10 +639,19 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   }
 
   const int nq = (n + BQ - 1) / BQ;
+  // softmax: wave 0 streams lse2, wave 1 delta (one value per lane and row)
+  const RowDma<BQ> rdma(SOFTMAX && w < 2 ? (w == 0 ? LSE : DELTA) + (size_t)it.bh * S.Lmax : nullptr, n, lane);
+  auto Rb = [&](int i) { return rowv + (2 * i + (w & 1)) * BQ; };
+  auto row_load = [&](int row0, int i) {
+    if constexpr (SOFTMAX)
+      if (w < 2) rdma.load(row0, Rb(i));
+  };
   dma_q.load(qs, 0, Qb(0));
   dma_g.load(gs, 0, Gb(0));
   dma_q.load(qs, BQ, Qb(1));
   dma_g.load(gs, BQ, Gb(1));
+  row_load(0, 0);
+  row_load(BQ, 1);
   vm_drain();
   __syncthreads();
   f32x16 sA[NMB], dA[NMB], sB[NMB], dB[NMB];
@@ -474,6 +669,7 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     f32x16(&nd)[NMB] = pick<P + 1>(dA, dB);
     dma_q.load(qs, (j + 2) * BQ, Qb(k2));
     dma_g.load(gs, (j + 2) * BQ, Gb(k2));
+    row_load((j + 2) * BQ, k2);
     const uint16_t* Qn = Qb(k1);
     const uint16_t* Gn = Gb(k1);
     const uint16_t* Qt = Qb(kc);
@@ -491,7 +687,15 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
         read_value_frags<D>(ag[c & 1], tr, Gt, c);
         read_value_frags<D>(aq[c & 1], tr, Qt, c);
         sched_fence();
-        dsigmoid_chunk<D, SPLIT, true>(cs, cd, c, c2, dh[c], dl[c], ph[c], pl[c]);
+        if constexpr (SOFTMAX) {
+          const float* lt = rowv + 2 * kc * BQ;  // lse2 of stage kc; delta follows
+          const int r0 = 16 * c + 4 * hf;
+          const f32x8 lse8 = cat8(*(const f32x4*)(lt + r0), *(const f32x4*)(lt + r0 + 8));
+          const f32x8 dlt8 = cat8(*(const f32x4*)(lt + BQ + r0), *(const f32x4*)(lt + BQ + r0 + 8));
+          dsoftmax_chunk_row<D, SPLIT>(cs, cd, c, lse8, dlt8, dh[c], dl[c], ph[c], pl[c]);
+        } else {
+          dsigmoid_chunk<D, SPLIT, true>(cs, cd, c, c2, dh[c], dl[c], ph[c], pl[c]);
+        }
         if (c > 0) {
           value_chunk_pre<D, SPLIT>(dv, ag[(c - 1) & 1], ph[c - 1], pl[c - 1]);
           value_chunk_pre<D, SPLIT>(dk, aq[(c - 1) & 1], dh[c - 1], dl[c - 1]);
@@ -525,6 +729,32 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   }
 }
 
+// delta = rowsum(dO * O) per row for the softmax backward (0 on padded
+// rows); one thread per row, fp32 accumulation of the bf16 products.
+template <int D>
+__global__ __launch_bounds__(256) void softmax_prep_kernel(const uint16_t* __restrict__ O,
+                                                           const uint16_t* __restrict__ dO,
+                                                           float* __restrict__ DELTA, const PrepArgs A) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)A.nb * A.H * A.Lmax) return;
+  const int i = (int)(gid % A.Lmax);
+  const int bhl = (int)(gid / A.Lmax);
+  const int bl = bhl / A.H, h = bhl - bl * A.H, b = A.b0 + bl;
+  float acc = 0.0f;
+  if (i < A.n[bl]) {
+    const uint16_t* po = O + (size_t)b * A.sb[0] + (size_t)h * A.sh[0] + (size_t)i * A.sl[0];
+    const uint16_t* pg = dO + (size_t)b * A.sb[1] + (size_t)h * A.sh[1] + (size_t)i * A.sl[1];
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      const f32x8 x = to_f32x8(as_bf16x8(*(const u32x4*)(po + 8 * c)));
+      const f32x8 y = to_f32x8(as_bf16x8(*(const u32x4*)(pg + 8 * c)));
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc = __builtin_fmaf(x[t], y[t], acc);
+    }
+  }
+  DELTA[((size_t)b * A.H + h) * A.Lmax + i] = acc;
+}
+
 template <int D, bool SPLIT>
 hipError_t launch_fwd_t(const Launch& L, const void* q, const void* k, const void* v, void* o, hipStream_t st) {
   hipLaunchKernelGGL((fwd_kernel<D, SPLIT>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
@@ -536,7 +766,8 @@ template <int D, bool SPLIT>
 hipError_t launch_dq_t(const Launch& L, const void* q, const void* k, const void* v, const void* g, void* dq,
                        hipStream_t st) {
   hipLaunchKernelGGL((dq_kernel<D, SPLIT>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq, L.sched);
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq, (const float*)nullptr,
+                     (const float*)nullptr, L.sched);
   return hipGetLastError();
 }
 
@@ -545,7 +776,40 @@ hipError_t launch_dkdv_t(const Launch& L, const void* q, const void* k, const vo
                          void* dv, hipStream_t st) {
   hipLaunchKernelGGL((dkdv_kernel<D, SPLIT>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dk, (uint16_t*)dv,
-                     L.sched);
+                     (const float*)nullptr, (const float*)nullptr, L.sched);
+  return hipGetLastError();
+}
+
+template <int D, bool SPLIT>
+hipError_t launch_softmax_fwd_t(const Launch& L, const void* q, const void* k, const void* v, void* o, float* lse,
+                                hipStream_t st) {
+  hipLaunchKernelGGL((fwd_softmax_kernel<D, SPLIT>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, L.sched);
+  return hipGetLastError();
+}
+
+template <int D, bool SPLIT>
+hipError_t launch_softmax_dq_t(const Launch& L, const void* q, const void* k, const void* v, const void* g,
+                               const float* lse, const float* delta, void* dq, hipStream_t st) {
+  hipLaunchKernelGGL((dq_kernel<D, SPLIT, true>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq, lse, delta, L.sched);
+  return hipGetLastError();
+}
+
+template <int D, bool SPLIT>
+hipError_t launch_softmax_dkdv_t(const Launch& L, const void* q, const void* k, const void* v, const void* g,
+                                 const float* lse, const float* delta, void* dk, void* dv, hipStream_t st) {
+  hipLaunchKernelGGL((dkdv_kernel<D, SPLIT, true>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dk, (uint16_t*)dv, lse,
+                     delta, L.sched);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_softmax_prep_t(const PrepArgs& A, const void* o, const void* g, float* delta, hipStream_t st) {
+  const int64_t rows = (int64_t)A.nb * A.H * A.Lmax;
+  hipLaunchKernelGGL((softmax_prep_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
+                     (const uint16_t*)o, (const uint16_t*)g, delta, A);
   return hipGetLastError();
 }
 
@@ -575,6 +839,40 @@ hipError_t launch_bwd_dkdv(int d, bool split, const Launch& L, const void* q, co
                  : launch_dkdv_t<64, false>(L, q, k, v, g, dk, dv, st);
   return split ? launch_dkdv_t<128, true>(L, q, k, v, g, dk, dv, st)
                : launch_dkdv_t<128, false>(L, q, k, v, g, dk, dv, st);
+}
+
+hipError_t launch_softmax_fwd(int d, bool split, const Launch& L, const void* q, const void* k, const void* v,
+                              void* o, float* lse, hipStream_t st) {
+  if (d == 64)
+    return split ? kern::launch_softmax_fwd_t<64, true>(L, q, k, v, o, lse, st)
+                 : kern::launch_softmax_fwd_t<64, false>(L, q, k, v, o, lse, st);
+  return split ? kern::launch_softmax_fwd_t<128, true>(L, q, k, v, o, lse, st)
+               : kern::launch_softmax_fwd_t<128, false>(L, q, k, v, o, lse, st);
+}
+
+hipError_t launch_softmax_dq(int d, bool split, const Launch& L, const void* q, const void* k, const void* v,
+                             const void* g, const float* lse, const float* delta, void* dq, hipStream_t st) {
+  if (d == 64)
+    return split ? kern::launch_softmax_dq_t<64, true>(L, q, k, v, g, lse, delta, dq, st)
+                 : kern::launch_softmax_dq_t<64, false>(L, q, k, v, g, lse, delta, dq, st);
+  return split ? kern::launch_softmax_dq_t<128, true>(L, q, k, v, g, lse, delta, dq, st)
+               : kern::launch_softmax_dq_t<128, false>(L, q, k, v, g, lse, delta, dq, st);
+}
+
+hipError_t launch_softmax_dkdv(int d, bool split, const Launch& L, const void* q, const void* k, const void* v,
+                               const void* g, const float* lse, const float* delta, void* dk, void* dv,
+                               hipStream_t st) {
+  if (d == 64)
+    return split ? kern::launch_softmax_dkdv_t<64, true>(L, q, k, v, g, lse, delta, dk, dv, st)
+                 : kern::launch_softmax_dkdv_t<64, false>(L, q, k, v, g, lse, delta, dk, dv, st);
+  return split ? kern::launch_softmax_dkdv_t<128, true>(L, q, k, v, g, lse, delta, dk, dv, st)
+               : kern::launch_softmax_dkdv_t<128, false>(L, q, k, v, g, lse, delta, dk, dv, st);
+}
+
+hipError_t launch_softmax_prep(int d, const PrepArgs& A, const void* o, const void* g, float* delta,
+                               hipStream_t st) {
+  return d == 64 ? kern::launch_softmax_prep_t<64>(A, o, g, delta, st)
+                 : kern::launch_softmax_prep_t<128>(A, o, g, delta, st);
 }
 
 }  // namespace sigattn

@@ -145,3 +145,16 @@ def pin_zero_length(O):
 ALL_PINS = [pin_unit_values_give_ones, pin_zero_query_is_mean_of_values, pin_single_key, pin_brute_force_loops,
             pin_finite_differences, pin_explicit_jacobian, pin_padding_carries_nothing, pin_key_permutation,
             pin_gradient_rows_sum, pin_zero_length]
+
+
+def pin_row_term_identity(O):
+    """sum_k P_ik dP_ik = rowsum(dO * O): passing the exact O as the rounding
+    function changes no gradient."""
+    q, k, v, do = _rand(11, 1, 2, 6, 4)
+    a = O.attention(q, k, v, [6], do=do)
+    b = O.attention(q, k, v, [6], do=do, round_o=lambda x: x)
+    for key in ("dq", "dk", "dv"):
+        assert np.allclose(a[key], b[key], atol=1e-13), key
+
+
+ALL_PINS.append(pin_row_term_identity)

@@ -18,9 +18,11 @@ MUTATIONS = {
     "normalise_columns": ("return e / np.sum(e, axis=-1, keepdims=True)", "return e / np.sum(e, axis=0, keepdims=True)"),
     "scale_dropped": ("x = (q @ k.T) / math.sqrt(q.shape[1])", "x = (q @ k.T)"),
     "pv_transposed": ("return p @ v, row_logsumexp(x)", "return p.T @ v, row_logsumexp(x)"),
-    "jacobian_row_term_dropped": ("dx = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))", "dx = p * dp"),
-    "jacobian_wrong_axis": ("dx = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))",
-                            "dx = p * (dp - np.sum(p * dp, axis=0, keepdims=True))"),
+    "jacobian_row_term_dropped": ("dx = p * (dp - row)", "dx = p * dp"),
+    "jacobian_wrong_axis": ("row = np.sum(p * dp, axis=-1, keepdims=True) if delta",
+                            "row = np.sum(p * dp, axis=0, keepdims=True) if delta"),
+    "row_term_from_dp_only": ("delta = np.sum(do[bi, h, :n] * round_o(out[\"o\"][bi, h, :n]), axis=-1)",
+                              "delta = np.sum(do[bi, h, :n], axis=-1)"),
     "dv_not_transposed": ("dv = p.T @ do", "dv = p @ do"),
     "dk_uses_k": ("return s * (dx @ k), s * (dx.T @ q), dv", "return s * (dx @ k), s * (dx.T @ k), dv"),
     "keys_include_padding": ("qv, kv, vv = q[bi, h, :n], k[bi, h, :n], v[bi, h, :n]",

@@ -112,3 +112,20 @@ def test_layout_strides_of_torch_views():
     c = torch.empty(2, 4, 5, 64)
     assert layout_strides(c, "bhld") == ((2, 4, 5, 64), (4 * 5 * 64, 5 * 64, 64))
     assert layout_strides(c.permute(0, 2, 1, 3), "blhd") == ((2, 4, 5, 64), (4 * 5 * 64, 5 * 64, 64))
+
+
+def test_softmax_entry_points_validate_row_arrays():
+    import ctypes
+    lib = sa.load()
+    a, keep = sa.make_args(B, H, L, D, (256, 100))
+    r0, r1 = 0x500000000000, 0x600000000000
+    q, k, v, o = P[:4]
+    assert lib.sigattn_softmax_fwd(ctypes.byref(a), q, k, v, o, None) == NULL
+    assert lib.sigattn_softmax_fwd(ctypes.byref(a), q, k, v, o, r0 + 4) == ALIGN
+    assert lib.sigattn_softmax_fwd(ctypes.byref(a), q, k, v, o, o + 64) == ALIAS  # lse2 inside O
+    assert lib.sigattn_softmax_bwd_prep(ctypes.byref(a), o, P[4], o + 1024) == ALIAS  # delta inside O
+    assert lib.sigattn_softmax_bwd_prep(ctypes.byref(a), o, P[4], None) == NULL
+    # an output overlapping an input row array
+    assert lib.sigattn_softmax_bwd_dq(ctypes.byref(a), q, k, v, P[4], r0, r1, r1) == ALIAS
+    assert lib.sigattn_softmax_bwd_dkdv(ctypes.byref(a), q, k, v, P[4], r0, r1, r0, P[6]) == ALIAS
+    assert lib.sigattn_softmax_bwd_dkdv(ctypes.byref(a), q, k, v, P[4], None, r1, P[5], P[6]) == NULL
