@@ -20,6 +20,7 @@ Only one GPU is used: --gpus above 1 exits with a message.
 from __future__ import annotations
 
 import argparse
+import math
 import hashlib
 import json
 import os
@@ -145,6 +146,63 @@ def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="s
     return res
 
 
+def time_layer(attn, steps, warmup, d_model=768, heads=12, mlp=3072, seed=0):
+    """Forward + backward of one pre-norm bidirectional transformer layer of
+    the 160M-parameter class (d_model 768, 12 heads of 64, MLP 3072, bf16,
+    random weights) on the headline batch's lengths: LayerNorm, fused QKV
+    projection, attention on [B, Lmax, H, d] views of it, output projection,
+    residual, LayerNorm, GELU MLP, residual.  attn: "sigmoid", "softmax" (both
+    this library's kernels) or "none" (attention replaced by V, to isolate the
+    rest of the layer).  Returns the mean ms per step (HIP events)."""
+    import torch
+    import torch.nn.functional as F
+
+    import sigmoid_attention_amd as sa
+    import workloads
+
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    n = workloads.lengths(workloads.HEADLINE)
+    B, L, dh = w.B, w.Lmax, d_model // heads
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(seed)
+
+    def param(*shape, fan_in):
+        return (torch.randn(*shape, generator=g) / math.sqrt(fan_in)).to(dev, torch.bfloat16).requires_grad_(True)
+
+    wqkv, wo = param(3 * d_model, d_model, fan_in=d_model), param(d_model, d_model, fan_in=d_model)
+    w1, w2 = param(mlp, d_model, fan_in=d_model), param(d_model, mlp, fan_in=mlp)
+    ln1 = torch.nn.LayerNorm(d_model).to(dev, torch.bfloat16)
+    ln2 = torch.nn.LayerNorm(d_model).to(dev, torch.bfloat16)
+    x = torch.randn(B, L, d_model, generator=g).to(dev, torch.bfloat16).requires_grad_(True)
+    gy = torch.randn(B, L, d_model, generator=g).to(dev, torch.bfloat16)
+
+    def layer(x):
+        qkv = F.linear(ln1(x), wqkv).view(B, L, 3, heads, dh)
+        q, k, v = qkv.unbind(2)
+        if attn == "sigmoid":
+            a = sa.sigmoid_attention(q, k, v, n, layout="blhd")
+        elif attn == "softmax":
+            a = sa.softmax_attention(q, k, v, n, layout="blhd")
+        else:
+            a = v.contiguous()
+        x = x + F.linear(a.reshape(B, L, d_model), wo)
+        return x + F.linear(F.gelu(F.linear(ln2(x), w1)), w2)
+
+    def step():
+        layer(x).backward(gy)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def tflops(flops, ms):
     return flops / (ms * 1e-3) / 1e12
 
@@ -210,6 +268,9 @@ def main():
                     help="time the softmax comparison path instead of sigmoid attention")
     ap.add_argument("--compare-softmax", action="store_true",
                     help="also time the softmax path on the same workload (and sweep) and report ratios")
+    ap.add_argument("--layer", action="store_true",
+                    help="instead: time one 160M-class transformer layer (fwd+bwd) with sigmoid vs softmax "
+                         "attention and print that as the JSON line")
     ap.add_argument("--layout", default="bhld", choices=["bhld", "blhd"],
                     help="tensor layout handed to the library: [B,H,Lmax,d] or [B,Lmax,H,d] (strided path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -241,6 +302,24 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read_per_copy": x.numel() * 2,
                           "bytes_written_per_copy": y.numel() * 2, "copies": 5}))
+        return
+
+    if a.layer:
+        ms = {k_: time_layer(k_, a.steps, a.warmup) for k_ in ("sigmoid", "softmax", "none")}
+        w = workloads.WORKLOADS[workloads.HEADLINE]
+        n = workloads.lengths(workloads.HEADLINE)
+        print(json.dumps({
+            "metric": "ms per forward+backward of one transformer layer (d_model 768, 12 heads, MLP 3072)",
+            "value": round(ms["sigmoid"], 4), "unit": "ms", "higher_is_better": False, "steps": a.steps,
+            "warmup": a.warmup, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": workloads.HEADLINE, "B": w.B, "Lmax": w.Lmax, "seqlens": [int(x) for x in n],
+                       "d_model": 768, "heads": 12, "head_dim": 64, "mlp": 3072, "layout": "blhd (fused QKV views)"},
+            "sigmoid_ms": round(ms["sigmoid"], 4), "softmax_ms": round(ms["softmax"], 4),
+            "no_attention_ms": round(ms["none"], 4),
+            "sigmoid_layer_speedup": round(ms["softmax"] / ms["sigmoid"], 4),
+            "attention_share_sigmoid": round(1 - ms["none"] / ms["sigmoid"], 4),
+            "attention_share_softmax": round(1 - ms["none"] / ms["softmax"], 4),
+        }))
         return
 
     name = a.workload or workloads.HEADLINE

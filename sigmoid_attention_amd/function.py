@@ -81,6 +81,34 @@ def sigmoid_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens
     return _SigmoidAttention.apply(q, k, v, lens, layout, bias_mode, bias_arg, precision)
 
 
+class _SoftmaxAttention(torch.autograd.Function):
+    """Softmax attention on the same schedule (the comparison path)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, lens, layout, precision):
+        o, lse2 = _binding.softmax_fwd(q, k, v, lens, precision=precision, layout=layout)
+        ctx.save_for_backward(q, k, v, o, lse2)
+        ctx.cfg = (lens, layout, precision)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse2 = ctx.saved_tensors
+        lens, layout, precision = ctx.cfg
+        do = _usable(do, layout)
+        dq, dk, dv = _binding.softmax_bwd(q, k, v, o, do, lse2, lens, precision=precision, layout=layout)
+        return dq, dk, dv, None, None, None
+
+
+def softmax_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens, layout: str = "bhld",
+                      precision: str = "fast") -> torch.Tensor:
+    """Differentiable softmax attention over each sequence's valid keys, on the
+    same kernels' schedule: the mechanism sigmoid attention replaces, for
+    like-for-like comparisons.  Arguments as for sigmoid_attention."""
+    lens = _host_lengths(seqlens, q.shape[0])
+    return _SoftmaxAttention.apply(q, k, v, lens, layout, precision)
+
+
 def lengths_from_padding_mask(key_padding_mask: torch.Tensor) -> np.ndarray:
     """Valid lengths from a [B, Lmax] boolean mask (True = padding), which must
     pad on the right only."""

@@ -124,3 +124,19 @@ def test_softmax_blhd_layout_equals_bhld():
     for name, x in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
         assert torch.equal(x.permute(0, 2, 1, 3), a[name]), name
     assert torch.equal(lse2, a["lse2"])
+
+
+def test_softmax_autograd_matches_oracle():
+    case = workloads.random_case(2, 2, 64, 180, [180, 61], seed=12)
+    q, k, v = (case[x].permute(0, 2, 1, 3).contiguous().to(DEV).requires_grad_(True) for x in ("q", "k", "v"))
+    w = case["do"].permute(0, 2, 1, 3).contiguous().to(DEV)
+    o = sa.softmax_attention(q, k, v, case["seqlens"], layout="blhd")
+    (o.float() * w.float()).sum().backward()
+    torch.cuda.synchronize()
+    ref = softmax_oracle.attention(host(case["q"]), host(case["k"]), host(case["v"]), case["seqlens"],
+                                   do=host(case["do"]))
+    got = {"o": o.detach(), "dq": q.grad, "dk": k.grad, "dv": v.grad}
+    for key, t in got.items():
+        r = worst_ratio(host(t.permute(0, 2, 1, 3).contiguous()), ref[key])
+        print(f"[softmax] autograd {key} ratio={r}", flush=True)
+        assert r <= 1.0, key
