@@ -84,18 +84,26 @@ def bias(n: int, mode: str = "seqlen", arg=None) -> float:
     raise ValueError(f"unknown bias mode {mode!r}")
 
 
-def head_forward(q, k, v, b):
+def causal_mask(n: int):
+    """1 where key j <= query i, else 0 (the causal variant; see attention())."""
+    return np.tril(np.ones((n, n)))
+
+
+def head_forward(q, k, v, b, causal: bool = False):
     """One (sequence, head) on its valid block: O = sigma(Q K^T / sqrt(d) + b) V.
 
-    q, k, v: float64 arrays [n, d] holding only the valid rows.
+    q, k, v: float64 arrays [n, d] holding only the valid rows.  causal: weights
+    of keys after the query are 0.
     """
     s = score_scale(q.shape[1])
     x = s * (q @ k.T) + b          # scores, n x n (query i, key j)
     p = logistic(x)                # weights; each one independent (§2A)
+    if causal:
+        p = p * causal_mask(q.shape[0])
     return p @ v
 
 
-def head_backward(q, k, v, do, b, intermediates: bool = False):
+def head_backward(q, k, v, do, b, intermediates: bool = False, causal: bool = False):
     """Gradients of l = sum(O * dO) for one (sequence, head) on its valid block.
 
     With X = s Q K^T + b, P = sigma(X), O = P V (summary §2A) and the diagonal
@@ -111,6 +119,8 @@ def head_backward(q, k, v, do, b, intermediates: bool = False):
     s = score_scale(q.shape[1])
     x = s * (q @ k.T) + b
     p = logistic(x)
+    if causal:  # masked weights are constants 0: no gradient through them
+        p = p * causal_mask(q.shape[0])
     dv = p.T @ do
     dp = do @ v.T
     dx = dp * (p * logistic(-x))
@@ -121,11 +131,16 @@ def head_backward(q, k, v, do, b, intermediates: bool = False):
     return dq, dk, dv
 
 
-def attention(q, k, v, seqlens, do=None, bias_mode: str = "seqlen", bias_arg=None):
+def attention(q, k, v, seqlens, do=None, bias_mode: str = "seqlen", bias_arg=None, causal: bool = False):
     """Whole padded batch.  q, k, v, do: float64 [B, H, Lmax, d]; seqlens: [B].
 
     Returns {"o": ...} and, if do is given, also "dq", "dk", "dv"; every output
     is [B, H, Lmax, d] float64 with padded rows set to 0.
+
+    causal: the variant for autoregressive use (the language experiments of
+    "Theory, Analysis, and Best Practices for Sigmoid Self-Attention", abstract),
+    where query i sees keys 0..i only; the single-cell models of the summary
+    are bidirectional, which is the default.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -146,9 +161,9 @@ def attention(q, k, v, seqlens, do=None, bias_mode: str = "seqlen", bias_arg=Non
         b = bias(n, bias_mode, bias_arg)
         for h in range(H):
             qv, kv, vv = q[bi, h, :n], k[bi, h, :n], v[bi, h, :n]
-            out["o"][bi, h, :n] = head_forward(qv, kv, vv, b)
+            out["o"][bi, h, :n] = head_forward(qv, kv, vv, b, causal)
             if do is not None:
-                dq, dk, dv = head_backward(qv, kv, vv, do[bi, h, :n], b)
+                dq, dk, dv = head_backward(qv, kv, vv, do[bi, h, :n], b, causal=causal)
                 out["dq"][bi, h, :n] = dq
                 out["dk"][bi, h, :n] = dk
                 out["dv"][bi, h, :n] = dv

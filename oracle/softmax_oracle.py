@@ -52,20 +52,28 @@ def row_logsumexp(x):
     return (m + np.log(np.sum(np.exp(x - m), axis=-1, keepdims=True)))[..., 0]
 
 
-def head_forward(q, k, v):
+def _masked(x, causal):
+    """Scores with keys after the query set to -inf (causal variant)."""
+    if not causal:
+        return x
+    n = x.shape[0]
+    return np.where(np.tril(np.ones((n, n))) > 0, x, -np.inf)
+
+
+def head_forward(q, k, v, causal=False):
     """One (sequence, head) on its valid rows: (O, lse).  q, k, v: [n, d]."""
-    x = (q @ k.T) / math.sqrt(q.shape[1])
+    x = _masked((q @ k.T) / math.sqrt(q.shape[1]), causal)
     p = row_softmax(x)
     return p @ v, row_logsumexp(x)
 
 
-def head_backward(q, k, v, do, delta=None):
+def head_backward(q, k, v, do, delta=None, causal=False):
     """dQ, dK, dV of l = sum(O * dO) on the valid rows, through the dense row
     Jacobian of the softmax.  The row term sum_k P_ik dP_ik equals
     rowsum(dO * O); `delta` (one value per row) replaces it, to model a
     backward that forms it from a stored, rounded O."""
     s = 1.0 / math.sqrt(q.shape[1])
-    x = s * (q @ k.T)
+    x = _masked(s * (q @ k.T), causal)
     p = row_softmax(x)
     dv = p.T @ do
     dp = do @ v.T
@@ -74,11 +82,12 @@ def head_backward(q, k, v, do, delta=None):
     return s * (dx @ k), s * (dx.T @ q), dv
 
 
-def attention(q, k, v, seqlens, do=None, round_o=None):
+def attention(q, k, v, seqlens, do=None, round_o=None, causal=False):
     """Whole padded batch, float64 [B, H, Lmax, d] inputs.  Returns "o" and
     "lse" ([B, H, Lmax]) and, with do, "dq", "dk", "dv"; padded rows 0.
     round_o: optional function applied to each head's O before the backward
-    forms its row term from it (rowsum(dO * round_o(O)))."""
+    forms its row term from it (rowsum(dO * round_o(O))).  causal: query i
+    sees keys 0..i only."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -97,11 +106,11 @@ def attention(q, k, v, seqlens, do=None, round_o=None):
             continue
         for h in range(H):
             qv, kv, vv = q[bi, h, :n], k[bi, h, :n], v[bi, h, :n]
-            out["o"][bi, h, :n], out["lse"][bi, h, :n] = head_forward(qv, kv, vv)
+            out["o"][bi, h, :n], out["lse"][bi, h, :n] = head_forward(qv, kv, vv, causal)
             if do is not None:
                 delta = None
                 if round_o is not None:
                     delta = np.sum(do[bi, h, :n] * round_o(out["o"][bi, h, :n]), axis=-1)
-                dq, dk, dv = head_backward(qv, kv, vv, do[bi, h, :n], delta)
+                dq, dk, dv = head_backward(qv, kv, vv, do[bi, h, :n], delta, causal)
                 out["dq"][bi, h, :n], out["dk"][bi, h, :n], out["dv"][bi, h, :n] = dq, dk, dv
     return out

@@ -321,3 +321,77 @@ ALL_PINS = [
     pin_linear_in_values,
     pin_head_matches_batch,
 ]
+
+
+# --- causal variant -----------------------------------------------------------
+
+def pin_causal_zero_query(O):
+    """Causal, Q = 0: every visible weight is 1/(n+1), so O_i = sum_{j<=i} V_j / (n+1)."""
+    B, H, L, d = 2, 2, 10, 4
+    seqlens = [10, 6]
+    v = _rand((B, H, L, d), 41)
+    q, k = np.zeros_like(v), _rand((B, H, L, d), 42)
+    o = O.attention(q, k, v, seqlens, causal=True)["o"]
+    for b, n in enumerate(seqlens):
+        want = np.cumsum(v[b, :, :n], axis=1) / (n + 1)
+        _close(o[b, :, :n], want, what=f"causal q=0 b={b}")
+        assert np.all(o[b, :, n:] == 0.0)
+
+
+def pin_causal_brute_force(O):
+    """Scalar loops over j <= i with math.exp, forward and (via the loss) dV."""
+    L, d = 6, 3
+    q, k, v, do = (_rand((1, 1, L, d), s) for s in (43, 44, 45, 46))
+    n = 5
+    out = O.attention(q, k, v, [n], do=do, causal=True)
+    b = -math.log(n)
+    for i in range(n):
+        for c in range(d):
+            acc = 0.0
+            for j in range(i + 1):
+                x = sum(q[0, 0, i, t] * k[0, 0, j, t] for t in range(d)) / math.sqrt(d) + b
+                acc += v[0, 0, j, c] / (1.0 + math.exp(-x))
+            assert abs(out["o"][0, 0, i, c] - acc) < 1e-12
+    for j in range(n):  # dV_j = sum_{i >= j} P_ij dO_i
+        for c in range(d):
+            acc = 0.0
+            for i in range(j, n):
+                x = sum(q[0, 0, i, t] * k[0, 0, j, t] for t in range(d)) / math.sqrt(d) + b
+                acc += do[0, 0, i, c] / (1.0 + math.exp(-x))
+            assert abs(out["dv"][0, 0, j, c] - acc) < 1e-12
+
+
+def pin_causal_prefix(O):
+    """Rows after i of K and V cannot change O_i (nor dQ_i)."""
+    L, d = 9, 4
+    q, k, v, do = (_rand((1, 2, L, d), s) for s in (47, 48, 49, 50))
+    a = O.attention(q, k, v, [9], do=do, causal=True)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, 5:] += 3.0
+    v2[:, :, 5:] -= 2.0
+    b = O.attention(q, k2, v2, [9], do=do, causal=True)
+    _close(a["o"][:, :, :5], b["o"][:, :, :5], what="causal prefix O")
+    _close(a["dq"][:, :, :5], b["dq"][:, :, :5], what="causal prefix dQ")
+
+
+def pin_causal_finite_differences(O):
+    """Central differences of l = sum(O * dO) in the causal variant."""
+    L, d = 4, 2
+    q, k, v, do = (_rand((1, 1, L, d), s) for s in (51, 52, 53, 54))
+    g = O.attention(q, k, v, [L], do=do, causal=True)
+    h = 1e-6
+    for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv")):
+        base = {"q": q, "k": k, "v": v}
+        for idx in np.ndindex(base[name].shape):
+            xp, xm = dict(base), dict(base)
+            xp[name] = base[name].copy()
+            xm[name] = base[name].copy()
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            lp = np.sum(O.attention(xp["q"], xp["k"], xp["v"], [L], causal=True)["o"] * do)
+            lm = np.sum(O.attention(xm["q"], xm["k"], xm["v"], [L], causal=True)["o"] * do)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g[key][idx]) < 1e-7 * (1 + abs(fd)), (name, idx)
+
+
+ALL_PINS += [pin_causal_zero_query, pin_causal_brute_force, pin_causal_prefix, pin_causal_finite_differences]

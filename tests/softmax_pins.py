@@ -158,3 +158,34 @@ def pin_row_term_identity(O):
 
 
 ALL_PINS.append(pin_row_term_identity)
+
+
+def pin_causal_zero_query(O):
+    """Causal, Q = 0: O_i = mean of V_0..V_i and lse_i = ln(i + 1)."""
+    _, k, v, _ = _rand(12, 1, 2, 7, 3)
+    q = np.zeros_like(k)
+    out = O.attention(q, k, v, [7], causal=True)
+    for i in range(7):
+        assert np.allclose(out["o"][0, :, i], v[0, :, :i + 1].mean(axis=1), atol=1e-13)
+        assert np.allclose(out["lse"][0, :, i], math.log(i + 1), atol=1e-13)
+
+
+def pin_causal_prefix_and_gradients(O):
+    """Rows after i cannot change O_i; central differences of the causal loss."""
+    q, k, v, do = _rand(13, 1, 1, 4, 2)
+    a = O.attention(q, k, v, [4], do=do, causal=True)
+    k2 = k.copy()
+    k2[:, :, 2:] += 5.0
+    b = O.attention(q, k2, v, [4], do=do, causal=True)
+    assert np.allclose(a["o"][:, :, :2], b["o"][:, :, :2], atol=1e-13)
+    h = 1e-6
+    for idx in np.ndindex(q.shape):
+        qp, qm = q.copy(), q.copy()
+        qp[idx] += h
+        qm[idx] -= h
+        fd = (np.sum(O.attention(qp, k, v, [4], causal=True)["o"] * do)
+              - np.sum(O.attention(qm, k, v, [4], causal=True)["o"] * do)) / (2 * h)
+        assert abs(fd - a["dq"][idx]) < 1e-7 * (1 + abs(fd))
+
+
+ALL_PINS += [pin_causal_zero_query, pin_causal_prefix_and_gradients]

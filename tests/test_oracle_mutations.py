@@ -33,6 +33,8 @@ MUTATIONS = {
     "dk_uses_k": ("dk = s * (dx.T @ q)", "dk = s * (dx.T @ k)"),
     "keys_include_padding": ("qv, kv, vv = q[bi, h, :n], k[bi, h, :n], v[bi, h, :n]",
                              "qv, kv, vv = q[bi, h, :n], k[bi, h, :n + 1], v[bi, h, :n + 1]"),
+    "causal_mask_transposed": ("return np.tril(np.ones((n, n)))", "return np.triu(np.ones((n, n)))"),
+    "causal_forward_only": ("    if causal:  # masked weights are constants 0: no gradient through them\n        p = p * causal_mask(q.shape[0])\n", ""),
     "head_drops_last_row": ("o[:n] = head_forward(q[:n], k[:n], v[:n], b)",
                             "o[:n - 1] = head_forward(q[:n], k[:n], v[:n], b)[:n - 1]"),
 }

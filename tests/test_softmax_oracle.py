@@ -16,7 +16,7 @@ with open(SRC_PATH) as f:
 MUTATIONS = {
     "no_row_max_in_lse": ("return (m + np.log(", "return (np.log("),
     "normalise_columns": ("return e / np.sum(e, axis=-1, keepdims=True)", "return e / np.sum(e, axis=0, keepdims=True)"),
-    "scale_dropped": ("x = (q @ k.T) / math.sqrt(q.shape[1])", "x = (q @ k.T)"),
+    "scale_dropped": ("x = _masked((q @ k.T) / math.sqrt(q.shape[1]), causal)", "x = _masked((q @ k.T), causal)"),
     "pv_transposed": ("return p @ v, row_logsumexp(x)", "return p.T @ v, row_logsumexp(x)"),
     "jacobian_row_term_dropped": ("dx = p * (dp - row)", "dx = p * dp"),
     "jacobian_wrong_axis": ("row = np.sum(p * dp, axis=-1, keepdims=True) if delta",
@@ -25,6 +25,8 @@ MUTATIONS = {
                               "delta = np.sum(do[bi, h, :n], axis=-1)"),
     "dv_not_transposed": ("dv = p.T @ do", "dv = p @ do"),
     "dk_uses_k": ("return s * (dx @ k), s * (dx.T @ q), dv", "return s * (dx @ k), s * (dx.T @ k), dv"),
+    "causal_mask_transposed": ("np.where(np.tril(np.ones((n, n))) > 0, x, -np.inf)", "np.where(np.triu(np.ones((n, n))) > 0, x, -np.inf)"),
+    "causal_backward_unmasked": ("x = _masked(s * (q @ k.T), causal)", "x = s * (q @ k.T)"),
     "keys_include_padding": ("qv, kv, vv = q[bi, h, :n], k[bi, h, :n], v[bi, h, :n]",
                              "qv, kv, vv = q[bi, h, :n], k[bi, h, :n + 1], v[bi, h, :n + 1]"),
 }
