@@ -1,7 +1,7 @@
 """Benchmark: valid-token TFLOPS of sigmoid attention (forward + backward) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--precision fast|split|auto]
-                    [--sweep] [--no-cpu-baseline] [--cpu-seconds S]
+                    [--sweep] [--no-cpu-baseline] [--cpu-seconds S] [--causal]
 
 A step is one pass of the whole path over one batch already resident in HBM:
 sigattn_fwd, then sigattn_bwd_dq, then sigattn_bwd_dkdv (one launch each).
@@ -45,9 +45,12 @@ KERNEL_FLOP_UNITS = {"fwd": 4, "bwd_dq": 2, "bwd_dkdv": 8}
 # counts no FLOPs; its other kernels follow the same convention.
 
 
-def pair_flops(seqlens, H, d):
+def pair_flops(seqlens, H, d, causal=False):
+    """H d times the number of valid (query, key) pairs: n^2 per sequence,
+    n (n + 1) / 2 under the causal mask."""
     n = np.asarray(seqlens, dtype=np.float64)
-    return float(H * d * (n * n).sum())
+    pairs = n * (n + 1) / 2 if causal else n * n
+    return float(H * d * pairs.sum())
 
 
 def kernel_source_hash() -> str:
@@ -73,7 +76,7 @@ def load_traffic(kernel: str, workload: str, precision: str):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
-def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="sigmoid"):
+def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="sigmoid", causal=False):
     """Time `steps` passes of forward + backward (HIP events around every
     call, on the launch stream).  attn="softmax" times the softmax comparison
     path on the same inputs and schedule: forward, the delta pass, dQ, dK/dV."""
@@ -93,6 +96,8 @@ def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="s
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
     kw = dict(precision=precision, layout=layout)
     lse2 = delta = None
+    if causal:
+        kw["causal"] = True
     if attn == "softmax":
         (B, H, L, _), _ = sa._binding.layout_strides(q, layout)
         lse2 = torch.empty((B, H, L), dtype=torch.float32, device=dev)
@@ -114,7 +119,7 @@ def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="s
         else:
             sa.softmax_fwd(q, k, v, n, o=o, lse2=lse2, **kw)
             mark(1)
-            sa.softmax_bwd_prep(o, do, n, delta, **kw)
+            sa.softmax_bwd_prep(o, do, n, delta, precision=precision, layout=layout)
             mark(2)
             sa.softmax_bwd_dq(q, k, v, do, lse2, delta, n, dq, **kw)
             mark(3)
@@ -132,7 +137,7 @@ def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="s
     host_s = time.perf_counter() - t0
     per = {kname: [ev[i].elapsed_time(ev[i + 1]) for ev in events] for i, kname in enumerate(names)}
     step_ms = events[0][0].elapsed_time(events[-1][-1]) / steps
-    base = pair_flops(n, w.H, w.d)
+    base = pair_flops(n, w.H, w.d, causal)
     avg = {kname: float(np.mean(v_)) for kname, v_ in per.items()}
     med = {kname: float(np.median(v_)) for kname, v_ in per.items()}
     res = {
@@ -273,6 +278,8 @@ def main():
                          "attention and print that as the JSON line")
     ap.add_argument("--layout", default="bhld", choices=["bhld", "blhd"],
                     help="tensor layout handed to the library: [B,H,Lmax,d] or [B,Lmax,H,d] (strided path)")
+    ap.add_argument("--causal", action="store_true",
+                    help="causal mask (query i sees keys 0..i); FLOPs count the n(n+1)/2 visible pairs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -325,7 +332,7 @@ def main():
     name = a.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
     precision = a.precision if a.precision != "auto" else ("split" if w.scale_qkv > 1.0 else "fast")
-    r = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn=a.attn)
+    r = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn=a.attn, causal=a.causal)
     n = r["seqlens"]
     total = r["fwd_flops"] + r["bwd_flops"]
     value = tflops(total, r["step_ms"])
@@ -367,7 +374,7 @@ def main():
         "config": {
             "workload": name, "B": w.B, "H": w.H, "d": w.d, "Lmax": w.Lmax, "seqlens": [int(x) for x in n],
             "precision": precision, "bias": "-ln(n_b)" if a.attn == "sigmoid" else "none (softmax)",
-            "layout": a.layout, "attention": a.attn,
+            "layout": a.layout, "attention": a.attn, "mask": "causal" if a.causal else "none",
             "valid_token_frac": round(float(np.sum(n)) / (w.B * w.Lmax), 4),
             "valid_pair_frac": round(float(np.sum(np.asarray(n, np.float64) ** 2)) / (w.B * w.Lmax ** 2), 4),
         },
@@ -416,7 +423,7 @@ def main():
         out["padding_sweep"] = sweep
 
     if a.compare_softmax and a.attn == "sigmoid":
-        rc = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn="softmax")
+        rc = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn="softmax", causal=a.causal)
         out["softmax_comparison"] = {
             "value": round(tflops(total, rc["step_ms"]), 2),
             "fwd_tflops": round(tflops(rc["fwd_flops"], rc["kernel_avg_ms"]["fwd"]), 2),
@@ -428,7 +435,7 @@ def main():
         }
         del rc
 
-    if not a.no_cpu_baseline and a.attn == "sigmoid":
+    if not a.no_cpu_baseline and a.attn == "sigmoid" and not a.causal:
         rec, worst = cpu_baseline(r["case"], r["outputs"], a.cpu_seconds)
         out["cpu_baseline"] = {k_: v_ for k_, v_ in rec.items() if k_ != "seconds"}
         out["parity_worst_ratio_on_cpu_sample"] = round(worst, 4)

@@ -11,8 +11,9 @@
  *
  * ("Better Models, Faster Training: Sigmoid Attention for single-cell
  * Foundation Models", technical summary §2A: the SigmoidAttn formula and the
- * bias b = -log(n).)  There is no causal mask: the paper's models are
- * bidirectional (its abstract).  The backward follows from the diagonal
+ * bias b = -log(n).)  By default there is no causal mask: the paper's models
+ * are bidirectional (its abstract); args->mask selects the causal variant
+ * (sigattn_mask).  The backward follows from the diagonal
  * Jacobian of §2B: with dP = dO V^T and dX = dP * P * (1 - P),
  *
  *     dQ = dX K / sqrt(d),   dK = dX^T Q / sqrt(d),   dV = P^T dO.
@@ -68,11 +69,21 @@ typedef enum sigattn_status {
   SIGATTN_ERR_PRECISION = 7, /* unknown precision                                       */
   SIGATTN_ERR_HIP = 8,       /* the HIP runtime rejected a kernel launch                */
   SIGATTN_ERR_PASS = 9,      /* unknown pass id (sigattn_plan_stats only)               */
-  SIGATTN_ERR_STRIDE = 10    /* a stride is negative or not a multiple of 8 elements, a
+  SIGATTN_ERR_STRIDE = 10,   /* a stride is negative or not a multiple of 8 elements, a
                                 row stride is below d or too large for 32-bit offsets
                                 ((Lmax + 256) * l * 2 > 2^31 - 1), or an output view
                                 maps two elements to one address                        */
+  SIGATTN_ERR_MASK = 11      /* unknown mask mode                                       */
 } sigattn_status;
+
+/* Which keys a query sees. */
+typedef enum sigattn_mask {
+  SIGATTN_MASK_NONE = 0,   /* bidirectional: every valid key (the summary's models)   */
+  SIGATTN_MASK_CAUSAL = 1  /* query i sees keys 0..i only: the autoregressive variant
+                              (the language experiments of "Theory, Analysis, and Best
+                              Practices for Sigmoid Self-Attention", abstract); tiles
+                              above the diagonal are skipped like padded ones        */
+} sigattn_mask;
 
 /* The bias b_b of the SigmoidAttn formula (summary §2A, b = -log(n)). */
 typedef enum sigattn_bias_mode {
@@ -124,6 +135,7 @@ typedef struct sigattn_args {
                                of the call, in argument order (fwd: q, k, v, o;
                                dq: q, k, v, dout, dq; dkdv: q, k, v, dout, dk, dv);
                                read during the call only                            */
+  int32_t mask;             /* sigattn_mask; 0 = bidirectional                      */
 } sigattn_args;
 
 /* Forward: O = sigma(Q K^T / sqrt(d) + b) V on valid rows; padded rows of O = 0.

@@ -23,7 +23,7 @@ PASSES = {"fwd": 0, "bwd_dq": 1, "bwd_dkdv": 2}
 STATUS_NAMES = {
     0: "SIGATTN_OK", 1: "SIGATTN_ERR_NULL", 2: "SIGATTN_ERR_SHAPE", 3: "SIGATTN_ERR_SEQLEN",
     4: "SIGATTN_ERR_ALIGN", 5: "SIGATTN_ERR_ALIAS", 6: "SIGATTN_ERR_BIAS", 7: "SIGATTN_ERR_PRECISION",
-    8: "SIGATTN_ERR_HIP", 9: "SIGATTN_ERR_PASS", 10: "SIGATTN_ERR_STRIDE",
+    8: "SIGATTN_ERR_HIP", 9: "SIGATTN_ERR_PASS", 10: "SIGATTN_ERR_STRIDE", 11: "SIGATTN_ERR_MASK",
 }
 
 # Index order of a 4-d tensor for each supported layout, as (b, h, l, d) positions.
@@ -46,6 +46,7 @@ class SigattnArgs(ctypes.Structure):
         ("precision", ctypes.c_int32),
         ("stream", ctypes.c_void_p),
         ("strides", ctypes.POINTER(SigattnStrides)),
+        ("mask", ctypes.c_int32),
     ]
 
 
@@ -101,7 +102,7 @@ def status_str(code: int) -> str:
 
 
 def make_args(B, H, Lmax, d, seqlens, bias_mode="seqlen", bias_arg=0.0, precision="fast", stream=0,
-              strides=None):
+              strides=None, causal=False):
     """Build a sigattn_args struct.  `strides`: None (every tensor contiguous
     [B, H, Lmax, d]) or one (b, h, l) element-stride triple per tensor
     argument, in argument order.  Returns (args, keepalive) — keep the second
@@ -115,6 +116,7 @@ def make_args(B, H, Lmax, d, seqlens, bias_mode="seqlen", bias_arg=0.0, precisio
     a.bias_arg = float(bias_arg)
     a.precision = PRECISIONS[precision] if isinstance(precision, str) else int(precision)
     a.stream = int(stream) if stream else None
+    a.mask = int(causal) if not isinstance(causal, bool) else (1 if causal else 0)
     st = None
     if strides is not None:
         st = (SigattnStrides * len(strides))(*[SigattnStrides(int(b), int(h), int(l)) for b, h, l in strides])
@@ -134,7 +136,7 @@ def layout_strides(t, layout: str = "bhld"):
     return tuple(t.shape[i] for i in pos), (t.stride(pos[0]), t.stride(pos[1]), t.stride(pos[2]))
 
 
-def _tensor_args(ts, seqlens, bias_mode, bias_arg, precision, stream, layout="bhld"):
+def _tensor_args(ts, seqlens, bias_mode, bias_arg, precision, stream, layout="bhld", causal=False):
     """Validate tensors and build the argument block.  Each tensor is 4-d in
     `layout` order ("bhld": [B, H, Lmax, d]; "blhd": [B, Lmax, H, d]) with a
     contiguous last dimension; any other strides (views of a fused projection,
@@ -163,7 +165,7 @@ def _tensor_args(ts, seqlens, bias_mode, bias_arg, precision, stream, layout="bh
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     return make_args(B, H, L, d, seqlens, bias_mode, bias_arg, precision, stream,
-                     None if contiguous else strides)
+                     None if contiguous else strides, causal)
 
 
 def _new_like(t):
@@ -174,15 +176,16 @@ def _new_like(t):
 
 
 def fwd(q, k, v, seqlens: Sequence[int], o=None, bias_mode="seqlen", bias_arg=0.0, precision="fast",
-        stream: Optional[int] = None, layout: str = "bhld"):
-    """O = sigma(Q K^T / sqrt(d) + b) V, padded rows of O zero.  Enqueued on the
+        stream: Optional[int] = None, layout: str = "bhld", causal: bool = False):
+    """O = sigma(Q K^T / sqrt(d) + b) V, padded rows of O zero (causal: query i
+    sees keys 0..i).  Enqueued on the
     current stream (or `stream`); returns O (a new O is contiguous in `layout`
     order)."""
     import torch
 
     if o is None:
         o = _new_like(q)
-    args, keep = _tensor_args((q, k, v, o), seqlens, bias_mode, bias_arg, precision, stream, layout)
+    args, keep = _tensor_args((q, k, v, o), seqlens, bias_mode, bias_arg, precision, stream, layout, causal)
     with torch.cuda.device(q.device):
         _check(load().sigattn_fwd(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()),
                "sigattn_fwd")
@@ -191,13 +194,13 @@ def fwd(q, k, v, seqlens: Sequence[int], o=None, bias_mode="seqlen", bias_arg=0.
 
 
 def bwd_dq(q, k, v, dout, seqlens, dq=None, bias_mode="seqlen", bias_arg=0.0, precision="fast", stream=None,
-           layout: str = "bhld"):
+           layout: str = "bhld", causal: bool = False):
     """dQ of sum(O * dO); padded rows zero.  Returns dQ."""
     import torch
 
     if dq is None:
         dq = _new_like(q)
-    args, keep = _tensor_args((q, k, v, dout, dq), seqlens, bias_mode, bias_arg, precision, stream, layout)
+    args, keep = _tensor_args((q, k, v, dout, dq), seqlens, bias_mode, bias_arg, precision, stream, layout, causal)
     with torch.cuda.device(q.device):
         _check(load().sigattn_bwd_dq(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                      dout.data_ptr(), dq.data_ptr()), "sigattn_bwd_dq")
@@ -206,7 +209,7 @@ def bwd_dq(q, k, v, dout, seqlens, dq=None, bias_mode="seqlen", bias_arg=0.0, pr
 
 
 def bwd_dkdv(q, k, v, dout, seqlens, dk=None, dv=None, bias_mode="seqlen", bias_arg=0.0, precision="fast",
-             stream=None, layout: str = "bhld"):
+             stream=None, layout: str = "bhld", causal: bool = False):
     """dK and dV of sum(O * dO); padded rows zero.  Returns (dK, dV)."""
     import torch
 
@@ -214,7 +217,8 @@ def bwd_dkdv(q, k, v, dout, seqlens, dk=None, dv=None, bias_mode="seqlen", bias_
         dk = _new_like(k)
     if dv is None:
         dv = _new_like(v)
-    args, keep = _tensor_args((q, k, v, dout, dk, dv), seqlens, bias_mode, bias_arg, precision, stream, layout)
+    args, keep = _tensor_args((q, k, v, dout, dk, dv), seqlens, bias_mode, bias_arg, precision, stream, layout,
+                              causal)
     with torch.cuda.device(q.device):
         _check(load().sigattn_bwd_dkdv(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                        dout.data_ptr(), dk.data_ptr(), dv.data_ptr()), "sigattn_bwd_dkdv")
@@ -238,7 +242,7 @@ def _check_rows(x, like, layout):
         raise ValueError("per-row arrays must be contiguous float32 [B, H, Lmax] on the tensors' device")
 
 
-def softmax_fwd(q, k, v, seqlens, o=None, lse2=None, precision="fast", stream=None, layout="bhld"):
+def softmax_fwd(q, k, v, seqlens, o=None, lse2=None, precision="fast", stream=None, layout="bhld", causal=False):
     """Softmax attention forward on the same schedule (comparison path).
     Returns (O, lse2); lse2 is the base-2 log-sum-exp of each valid row's
     scores scaled by log2(e)/sqrt(d), fp32 [B, H, Lmax], 0 on padded rows."""
@@ -249,7 +253,7 @@ def softmax_fwd(q, k, v, seqlens, o=None, lse2=None, precision="fast", stream=No
     if lse2 is None:
         lse2 = _rows_like(q, layout)
     _check_rows(lse2, q, layout)
-    args, keep = _tensor_args((q, k, v, o), seqlens, "seqlen", 0.0, precision, stream, layout)
+    args, keep = _tensor_args((q, k, v, o), seqlens, "seqlen", 0.0, precision, stream, layout, causal)
     with torch.cuda.device(q.device):
         _check(load().sigattn_softmax_fwd(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                           o.data_ptr(), lse2.data_ptr()), "sigattn_softmax_fwd")
@@ -271,14 +275,15 @@ def softmax_bwd_prep(o, dout, seqlens, delta=None, precision="fast", stream=None
     return delta
 
 
-def softmax_bwd_dq(q, k, v, dout, lse2, delta, seqlens, dq=None, precision="fast", stream=None, layout="bhld"):
+def softmax_bwd_dq(q, k, v, dout, lse2, delta, seqlens, dq=None, precision="fast", stream=None, layout="bhld",
+                   causal=False):
     """dQ of the softmax path."""
     import torch
 
     dq = _new_like(q) if dq is None else dq
     for x in (lse2, delta):
         _check_rows(x, q, layout)
-    args, keep = _tensor_args((q, k, v, dout, dq), seqlens, "seqlen", 0.0, precision, stream, layout)
+    args, keep = _tensor_args((q, k, v, dout, dq), seqlens, "seqlen", 0.0, precision, stream, layout, causal)
     with torch.cuda.device(q.device):
         _check(load().sigattn_softmax_bwd_dq(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                              dout.data_ptr(), lse2.data_ptr(), delta.data_ptr(), dq.data_ptr()),
@@ -288,7 +293,7 @@ def softmax_bwd_dq(q, k, v, dout, lse2, delta, seqlens, dq=None, precision="fast
 
 
 def softmax_bwd_dkdv(q, k, v, dout, lse2, delta, seqlens, dk=None, dv=None, precision="fast", stream=None,
-                     layout="bhld"):
+                     layout="bhld", causal=False):
     """dK and dV of the softmax path."""
     import torch
 
@@ -296,7 +301,7 @@ def softmax_bwd_dkdv(q, k, v, dout, lse2, delta, seqlens, dk=None, dv=None, prec
     dv = _new_like(v) if dv is None else dv
     for x in (lse2, delta):
         _check_rows(x, q, layout)
-    args, keep = _tensor_args((q, k, v, dout, dk, dv), seqlens, "seqlen", 0.0, precision, stream, layout)
+    args, keep = _tensor_args((q, k, v, dout, dk, dv), seqlens, "seqlen", 0.0, precision, stream, layout, causal)
     with torch.cuda.device(q.device):
         _check(load().sigattn_softmax_bwd_dkdv(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                                dout.data_ptr(), lse2.data_ptr(), delta.data_ptr(), dk.data_ptr(),
@@ -306,19 +311,20 @@ def softmax_bwd_dkdv(q, k, v, dout, lse2, delta, seqlens, dk=None, dv=None, prec
 
 
 def softmax_bwd(q, k, v, o, dout, lse2, seqlens, dq=None, dk=None, dv=None, delta=None, precision="fast",
-                stream=None, layout="bhld"):
+                stream=None, layout="bhld", causal=False):
     """Softmax attention backward: delta = rowsum(dO * O), then the dQ and
     the dK/dV kernels.  Returns (dQ, dK, dV)."""
     kw = dict(precision=precision, stream=stream, layout=layout)
     delta = softmax_bwd_prep(o, dout, seqlens, delta, **kw)
-    dq = softmax_bwd_dq(q, k, v, dout, lse2, delta, seqlens, dq, **kw)
-    dk, dv = softmax_bwd_dkdv(q, k, v, dout, lse2, delta, seqlens, dk, dv, **kw)
+    dq = softmax_bwd_dq(q, k, v, dout, lse2, delta, seqlens, dq, causal=causal, **kw)
+    dk, dv = softmax_bwd_dkdv(q, k, v, dout, lse2, delta, seqlens, dk, dv, causal=causal, **kw)
     return dq, dk, dv
 
 
-def plan_stats(B, H, Lmax, d, seqlens, pass_="fwd", bias_mode="seqlen", bias_arg=0.0, precision="fast"):
+def plan_stats(B, H, Lmax, d, seqlens, pass_="fwd", bias_mode="seqlen", bias_arg=0.0, precision="fast",
+               causal=False):
     """Host-only: (work_items, tile_pairs, launches) the pass would run."""
-    args, keep = make_args(B, H, Lmax, d, seqlens, bias_mode, bias_arg, precision)
+    args, keep = make_args(B, H, Lmax, d, seqlens, bias_mode, bias_arg, precision, causal=causal)
     items, pairs, launches = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
     _check(load().sigattn_plan_stats(ctypes.byref(args), PASSES[pass_], ctypes.byref(items), ctypes.byref(pairs),
                                      ctypes.byref(launches)), "sigattn_plan_stats")

@@ -56,6 +56,7 @@ sigattn_status check_args(const sigattn_args* a) {
     default: return SIGATTN_ERR_BIAS;
   }
   if (a->precision != SIGATTN_PREC_FAST && a->precision != SIGATTN_PREC_SPLIT) return SIGATTN_ERR_PRECISION;
+  if (a->mask != SIGATTN_MASK_NONE && a->mask != SIGATTN_MASK_CAUSAL) return SIGATTN_ERR_MASK;
   return SIGATTN_OK;
 }
 
@@ -213,6 +214,8 @@ sigattn::PlanInput plan_input(const sigattn_args* a, int32_t pass) {
   tile_rows(pass, &in.outer_rows, &in.inner_rows);
   in.bias_mode = a->bias_mode;
   in.bias_arg = a->bias_arg;
+  in.causal = a->mask == SIGATTN_MASK_CAUSAL;
+  in.outer_is_key = pass == SIGATTN_PASS_BWD_DKDV;
   return in;
 }
 
@@ -378,6 +381,7 @@ const char* sigattn_status_str(sigattn_status s) {
     case SIGATTN_ERR_PRECISION: return "unknown precision mode";
     case SIGATTN_ERR_HIP: return "HIP kernel launch failed";
     case SIGATTN_ERR_PASS: return "unknown pass";
+    case SIGATTN_ERR_MASK: return "unknown mask mode";
     case SIGATTN_ERR_STRIDE:
       return "bad strides: negative, not a multiple of 8, row stride below d or too large, or an output "
              "that maps two elements to one address";

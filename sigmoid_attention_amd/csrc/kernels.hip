@@ -78,6 +78,32 @@ __device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[NB], const f32
   }
 }
 
+// Causal mask (query i sees keys 0..i), applied only in tiles that straddle
+// the diagonal; a score of -inf gives sigma = 0 (and dS = 0) and a softmax
+// weight of 0.
+// S^T layout (keys in registers, the query is the lane's column): keys after
+// the lane's query.  key0 = first key of the tile.
+__device__ __forceinline__ void mask_causal_cols(f32x16 (&sc)[2], int key0, int qrow, int hf) {
+  const int lim = qrow - key0 - 4 * hf;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * b + 8 * (r >> 2) + (r & 3) > lim) sc[b][r] = -__builtin_inff();
+}
+
+// S layout (queries in registers, the key is the lane's column): queries
+// before the lane's key.  q0 = first query of the tile.
+template <int NB>
+__device__ __forceinline__ void mask_causal_rows(f32x16 (&sc)[NB], int q0, int krow, int hf) {
+  const int lim = krow - q0 - 4 * hf;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * b + 8 * (r >> 2) + (r & 3) < lim) sc[b][r] = -__builtin_inff();
+}
+
 // ---------------------------------------------------------------------------
 // Softmax attention, the workload sigmoid attention replaces, on the same
 // schedule (comparison path).  Per query row the forward keeps a running
@@ -313,7 +339,8 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
 
-  const int nk = (n + BK - 1) / BK;
+  const int nk = S.causal ? min((n + BK - 1) / BK, causal_inner_end(it.tile, BQ, BK)) : (n + BK - 1) / BK;
+  const int q0w = it.tile * BQ + 32 * w;  // this wave's first query
   dma_k.load(ks, 0, Kb(0));
   dma_k.load(ks, BK, Kb(1));
   dma_v.load(vs, 0, Vb(0));
@@ -332,6 +359,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
     dma_v.load(vs, (j + 1) * BK, Vb((P + 1) % 2));
     const uint16_t* Kn = Kb(k1);
     const uint16_t* Vc = Vb(P % 2);
+    if (S.causal && j * BK + BK - 1 > q0w) mask_causal_cols(cur, j * BK, qrow, hf);
     zero2(nxt);
     bf16x8 ph[4], pl[4];
     if (LA) {
@@ -430,7 +458,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd_softmax_kernel(
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
   float m = -__builtin_inff(), l = 0.0f;
 
-  const int nk = (n + BK - 1) / BK;
+  const int nk = S.causal ? min((n + BK - 1) / BK, causal_inner_end(it.tile, BQ, BK)) : (n + BK - 1) / BK;
+  const int q0w = it.tile * BQ + 32 * w;  // this wave's first query
   dma_k.load(ks, 0, Kb(0));
   dma_k.load(ks, BK, Kb(1));
   dma_v.load(vs, 0, Vb(0));
@@ -450,7 +479,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd_softmax_kernel(
     const uint16_t* Kn = Kb(k1);
     const uint16_t* Vc = Vb(P % 2);
     zero2(nxt);
-    if (j == nk - 1) mask_keys(cur, n - j * BK, hf);
+    if (S.causal && j * BK + BK - 1 > q0w) mask_causal_cols(cur, j * BK, qrow, hf);
+    if (j * BK + BK > n) mask_keys(cur, n - j * BK, hf);
     float mt = cur[0][0];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -537,7 +567,8 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
     }
   }
 
-  const int nk = (n + BK - 1) / BK;
+  const int nk = S.causal ? min((n + BK - 1) / BK, causal_inner_end(it.tile, BQ, BK)) : (n + BK - 1) / BK;
+  const int q0w = it.tile * BQ + 32 * w;  // this wave's first query
   dma_k.load(ks, 0, Kb(0));
   dma_k.load(ks, BK, Kb(1));
   dma_v.load(vs, 0, Vb(0));
@@ -557,6 +588,7 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
     const uint16_t* Kt = Kb(kc);
     const uint16_t* Kn = Kb(k1);
     const uint16_t* Vc = Vb(P % 2);
+    if (S.causal && j * BK + BK - 1 > q0w) mask_causal_cols(cur, j * BK, qrow, hf);
     f32x16 dp[2];
     zero2(dp);
     zero2(nxt);
@@ -639,6 +671,9 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   }
 
   const int nq = (n + BQ - 1) / BQ;
+  // causal: query tiles before this key tile's first key see none of it
+  const int j0 = S.causal ? causal_first_inner(it.tile, BKV, BQ) : 0;
+  const int k0w = it.tile * BKV + 32 * w;  // this wave's first key
   // softmax: wave 0 streams lse2, wave 1 delta (one value per lane and row)
   const RowDma<BQ> rdma(SOFTMAX && w < 2 ? (w == 0 ? LSE : DELTA) + (size_t)it.bh * S.Lmax : nullptr, n, lane);
   auto Rb = [&](int i) { return rowv + (2 * i + (w & 1)) * BQ; };
@@ -646,12 +681,12 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     if constexpr (SOFTMAX)
       if (w < 2) rdma.load(row0, Rb(i));
   };
-  dma_q.load(qs, 0, Qb(0));
-  dma_g.load(gs, 0, Gb(0));
-  dma_q.load(qs, BQ, Qb(1));
-  dma_g.load(gs, BQ, Gb(1));
-  row_load(0, 0);
-  row_load(BQ, 1);
+  dma_q.load(qs, j0 * BQ, Qb(0));
+  dma_g.load(gs, j0 * BQ, Gb(0));
+  dma_q.load(qs, (j0 + 1) * BQ, Qb(1));
+  dma_g.load(gs, (j0 + 1) * BQ, Gb(1));
+  row_load(j0 * BQ, 0);
+  row_load((j0 + 1) * BQ, 1);
   vm_drain();
   __syncthreads();
   f32x16 sA[NMB], dA[NMB], sB[NMB], dB[NMB];
@@ -660,7 +695,8 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   score_steps<D>(sA, Qb(0), kf, 0, D / 16, fa);
   score_steps<D>(dA, Gb(0), vf, 0, D / 16, fa);
 
-  auto step = [&](auto phase, int j) {
+  auto step = [&](auto phase, int jr) {
+    const int j = j0 + jr;  // inner (query) tile
     constexpr int P = decltype(phase)::value;
     constexpr int kc = P % 3, k1 = (P + 1) % 3, k2 = (P + 2) % 3;
     f32x16(&cs)[NMB] = pick<P>(sA, sB);
@@ -670,6 +706,7 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     dma_q.load(qs, (j + 2) * BQ, Qb(k2));
     dma_g.load(gs, (j + 2) * BQ, Gb(k2));
     row_load((j + 2) * BQ, k2);
+    if (S.causal && j * BQ < k0w + 31) mask_causal_rows(cs, j * BQ, krow, hf);
     const uint16_t* Qn = Qb(k1);
     const uint16_t* Gn = Gb(k1);
     const uint16_t* Qt = Qb(kc);
@@ -713,7 +750,7 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     vm_drain();
     __syncthreads();
   };
-  run_steps(nq, step);
+  run_steps(nq - j0, step);
 
   if (krow < n) {
     const float scale = S.out_scale;

@@ -13,11 +13,30 @@ namespace {
 struct Piece {
   int32_t b, h0, nh, t0, nt;
   int32_t n;
-  int64_t item_cost;   // inner tiles per item
-  int64_t cost() const { return (int64_t)nh * nt * item_cost; }
+  int64_t item_cost;   // inner tiles of the piece's longest item
+  int64_t total;       // inner tiles over all its items
+  int64_t cost() const { return total; }
 };
 
 int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+// Inner tiles visited by item t (outer tile t) of a sequence of length n.
+int64_t item_inner(const PlanInput& in, int32_t n, int32_t t) {
+  const int32_t inner = ceil_div(n, in.inner_rows);
+  if (!in.causal) return inner;
+  if (in.outer_is_key) return std::max(0, inner - causal_first_inner(t, in.outer_rows, in.inner_rows));
+  return std::min(inner, causal_inner_end(t, in.outer_rows, in.inner_rows));
+}
+
+Piece make_piece(const PlanInput& in, int32_t b, int32_t h0, int32_t nh, int32_t t0, int32_t nt, int32_t n) {
+  int64_t sum = 0, mx = 0;
+  for (int32_t t = t0; t < t0 + nt; ++t) {
+    const int64_t c = item_inner(in, n, t);
+    sum += c;
+    mx = std::max(mx, c);
+  }
+  return {b, h0, nh, t0, nt, n, mx, sum * nh};
+}
 
 // Pieces of at most about `target` tile pairs, cut evenly: whole sequences
 // (all heads) when small, else runs of heads, else runs of tiles of one head.
@@ -27,21 +46,18 @@ std::vector<Piece> make_pieces(const PlanInput& in, int64_t target) {
     const int32_t n = in.seqlens[b];
     if (n <= 0) continue;
     const int32_t items = ceil_div(n, in.outer_rows);
-    const int64_t inner = ceil_div(n, in.inner_rows);
-    const int64_t head_cost = items * inner;
+    const int64_t head_cost = make_piece(in, b, 0, 1, 0, items, n).total;
     if (head_cost * in.H <= target) {
-      pieces.push_back({b, 0, in.H, 0, items, n, inner});
+      pieces.push_back(make_piece(in, b, 0, in.H, 0, items, n));
     } else if (head_cost <= target) {
       const int32_t parts = (int32_t)((head_cost * in.H + target - 1) / target);
       const int32_t k = ceil_div(in.H, parts);
-      for (int32_t h = 0; h < in.H; h += k)
-        pieces.push_back({b, h, std::min(k, in.H - h), 0, items, n, inner});
+      for (int32_t h = 0; h < in.H; h += k) pieces.push_back(make_piece(in, b, h, std::min(k, in.H - h), 0, items, n));
     } else {
       const int32_t parts = (int32_t)std::min<int64_t>(items, (head_cost + target - 1) / target);
       const int32_t m = ceil_div(items, parts);
       for (int32_t h = 0; h < in.H; ++h)
-        for (int32_t t = 0; t < items; t += m)
-          pieces.push_back({b, h, 1, t, std::min(m, items - t), n, inner});
+        for (int32_t t = 0; t < items; t += m) pieces.push_back(make_piece(in, b, h, 1, t, std::min(m, items - t), n));
     }
   }
   return pieces;
@@ -63,10 +79,9 @@ std::vector<Launch> build_plan(const PlanInput& in, PlanStats* stats) {
   for (int32_t b = 0; b < in.B; ++b) {
     const int32_t n = in.seqlens[b];
     if (n <= 0) continue;
-    const int64_t items = ceil_div(n, in.outer_rows);
-    const int64_t inner = ceil_div(n, in.inner_rows);
-    total_items += items * in.H;
-    total_cost += items * inner * in.H;
+    const int32_t items = ceil_div(n, in.outer_rows);
+    total_items += (int64_t)items * in.H;
+    total_cost += make_piece(in, b, 0, in.H, 0, items, n).total;
   }
   if (stats) {
     stats->items = total_items;
@@ -116,6 +131,7 @@ std::vector<Launch> build_plan(const PlanInput& in, PlanStats* stats) {
     L.sched.H = in.H;
     L.sched.Lmax = in.Lmax;
     L.sched.out_scale = (float)(1.0 / std::sqrt((double)in.d));
+    L.sched.causal = in.causal;
     int32_t g = 0, max_items = 0;
     for (int x = 0; x < kXcds; ++x) {
       // Within a list, items with the most inner tiles start first.

@@ -54,6 +54,7 @@ struct Sched {
   int32_t zero_b0;               // first sequence zero-filled by this launch
   int32_t zero_nseq;             // sequences zero-filled by this launch (0: none)
   int32_t zero_n[kZeroSeqs];     // their valid lengths
+  int32_t causal;                // causal mask (see PlanInput)
   // Element strides (sequence, head, row) of each tensor argument of the
   // launch, in argument order; the head dimension is contiguous.
   int64_t sb[6];
@@ -106,7 +107,19 @@ struct PlanInput {
   int32_t inner_rows;  // rows per inner-loop tile
   int32_t bias_mode;
   float bias_arg;
+  int32_t causal = 0;        // query i sees keys 0..i only
+  int32_t outer_is_key = 0;  // outer tiles are key tiles (the dK/dV pass)
 };
+
+// Inner tiles visited by the item of outer tile t of a sequence of length n:
+// all of them, or with a causal mask only those on the visible side of the
+// diagonal (the kernels use the same bounds).
+inline SIGATTN_HD int32_t causal_first_inner(int32_t t, int32_t outer_rows, int32_t inner_rows) {
+  return t * outer_rows / inner_rows;  // first query tile that can see key tile t
+}
+inline SIGATTN_HD int32_t causal_inner_end(int32_t t, int32_t outer_rows, int32_t inner_rows) {
+  return ((t + 1) * outer_rows + inner_rows - 1) / inner_rows;  // key tiles up to query tile t's last row
+}
 
 struct PlanStats {
   int64_t items = 0;

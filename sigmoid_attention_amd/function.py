@@ -44,29 +44,30 @@ def _usable(t: torch.Tensor, layout: str) -> torch.Tensor:
 
 class _SigmoidAttention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, lens, layout, bias_mode, bias_arg, precision):
+    def forward(ctx, q, k, v, lens, layout, bias_mode, bias_arg, precision, causal):
         o = _binding.fwd(q, k, v, lens, bias_mode=bias_mode, bias_arg=bias_arg, precision=precision,
-                         layout=layout)
+                         layout=layout, causal=causal)
         ctx.save_for_backward(q, k, v)
-        ctx.cfg = (lens, layout, bias_mode, bias_arg, precision)
+        ctx.cfg = (lens, layout, bias_mode, bias_arg, precision, causal)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v = ctx.saved_tensors
-        lens, layout, bias_mode, bias_arg, precision = ctx.cfg
+        lens, layout, bias_mode, bias_arg, precision, causal = ctx.cfg
         do = _usable(do, layout)
-        kw = dict(bias_mode=bias_mode, bias_arg=bias_arg, precision=precision, layout=layout)
+        kw = dict(bias_mode=bias_mode, bias_arg=bias_arg, precision=precision, layout=layout, causal=causal)
         dq = dk = dv = None
         if ctx.needs_input_grad[0]:
             dq = _binding.bwd_dq(q, k, v, do, lens, **kw)
         if ctx.needs_input_grad[1] or ctx.needs_input_grad[2]:
             dk, dv = _binding.bwd_dkdv(q, k, v, do, lens, **kw)
-        return dq, dk, dv, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None
 
 
 def sigmoid_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens, layout: str = "bhld",
-                      bias_mode: str = "seqlen", bias_arg: float = 0.0, precision: str = "fast") -> torch.Tensor:
+                      bias_mode: str = "seqlen", bias_arg: float = 0.0, precision: str = "fast",
+                      causal: bool = False) -> torch.Tensor:
     """O = sigma(Q K^T / sqrt(d) + b) V per sequence and head, differentiable.
 
     q, k, v: bf16 CUDA tensors, 4-d in `layout` order ("bhld" = [B, H, Lmax, d],
@@ -74,39 +75,40 @@ def sigmoid_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens
     seqlens: B valid lengths (right padding), host sequence or tensor.  Rows at
     or beyond a sequence's length are ignored on input and zero on output (and
     in the gradients).  bias_mode / bias_arg / precision as in
-    sigmoid_attention_amd.fwd.
+    sigmoid_attention_amd.fwd.  causal: query i sees keys 0..i only.
     """
     B = q.shape[0]
     lens = _host_lengths(seqlens, B)
-    return _SigmoidAttention.apply(q, k, v, lens, layout, bias_mode, bias_arg, precision)
+    return _SigmoidAttention.apply(q, k, v, lens, layout, bias_mode, bias_arg, precision, bool(causal))
 
 
 class _SoftmaxAttention(torch.autograd.Function):
     """Softmax attention on the same schedule (the comparison path)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, lens, layout, precision):
-        o, lse2 = _binding.softmax_fwd(q, k, v, lens, precision=precision, layout=layout)
+    def forward(ctx, q, k, v, lens, layout, precision, causal):
+        o, lse2 = _binding.softmax_fwd(q, k, v, lens, precision=precision, layout=layout, causal=causal)
         ctx.save_for_backward(q, k, v, o, lse2)
-        ctx.cfg = (lens, layout, precision)
+        ctx.cfg = (lens, layout, precision, causal)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse2 = ctx.saved_tensors
-        lens, layout, precision = ctx.cfg
+        lens, layout, precision, causal = ctx.cfg
         do = _usable(do, layout)
-        dq, dk, dv = _binding.softmax_bwd(q, k, v, o, do, lse2, lens, precision=precision, layout=layout)
-        return dq, dk, dv, None, None, None
+        dq, dk, dv = _binding.softmax_bwd(q, k, v, o, do, lse2, lens, precision=precision, layout=layout,
+                                          causal=causal)
+        return dq, dk, dv, None, None, None, None
 
 
 def softmax_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens, layout: str = "bhld",
-                      precision: str = "fast") -> torch.Tensor:
+                      precision: str = "fast", causal: bool = False) -> torch.Tensor:
     """Differentiable softmax attention over each sequence's valid keys, on the
     same kernels' schedule: the mechanism sigmoid attention replaces, for
     like-for-like comparisons.  Arguments as for sigmoid_attention."""
     lens = _host_lengths(seqlens, q.shape[0])
-    return _SoftmaxAttention.apply(q, k, v, lens, layout, precision)
+    return _SoftmaxAttention.apply(q, k, v, lens, layout, precision, bool(causal))
 
 
 def lengths_from_padding_mask(key_padding_mask: torch.Tensor) -> np.ndarray:
@@ -131,11 +133,12 @@ class SigmoidAttention(torch.nn.Module):
     """
 
     def __init__(self, layout: str = "blhd", bias_mode: str = "seqlen", bias_arg: float = 0.0,
-                 precision: str = "fast"):
+                 precision: str = "fast", causal: bool = False):
         super().__init__()
         if layout not in _binding.LAYOUTS:
             raise ValueError(f"layout must be one of {sorted(_binding.LAYOUTS)}")
         self.layout, self.bias_mode, self.bias_arg, self.precision = layout, bias_mode, bias_arg, precision
+        self.causal = bool(causal)
 
     def forward(self, q, k, v, seqlens: Optional[Sequence[int]] = None,
                 key_padding_mask: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -145,7 +148,9 @@ class SigmoidAttention(torch.nn.Module):
             else:
                 L = q.shape[_binding.LAYOUTS[self.layout][2]]
                 seqlens = [L] * q.shape[0]
-        return sigmoid_attention(q, k, v, seqlens, self.layout, self.bias_mode, self.bias_arg, self.precision)
+        return sigmoid_attention(q, k, v, seqlens, self.layout, self.bias_mode, self.bias_arg, self.precision,
+                                 self.causal)
 
     def extra_repr(self) -> str:
-        return f"layout={self.layout}, bias_mode={self.bias_mode}, precision={self.precision}"
+        return (f"layout={self.layout}, bias_mode={self.bias_mode}, precision={self.precision}, "
+                f"causal={self.causal}")

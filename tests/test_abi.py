@@ -203,3 +203,32 @@ def test_no_oracle_in_product_path():
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), f
                 assert "oracle/" not in src, f
+
+
+@pytest.mark.parametrize("pass_", ["fwd", "bwd_dq", "bwd_dkdv"])
+def test_plan_stats_causal_closed_forms(pass_):
+    """Causal: only tiles on the visible side of the diagonal are visited.  A
+    query tile t (outer R rows) visits key tiles 0 .. ceil((t+1) R / r) - 1; a
+    key tile t visits query tiles floor(t R / r) .. ceil(n / r) - 1."""
+    lens = [1124, 2023, 0, 545, 64, 65, 2048]
+    outer, inner = sa.tile_shape(pass_, 64)
+    items, pairs, _ = sa.plan_stats(len(lens), 4, 2048, 64, lens, pass_, causal=True)
+    want_items = want_pairs = 0
+    for n in lens:
+        nt, ni = -(-n // outer), -(-n // inner)
+        want_items += 4 * nt
+        for t in range(nt):
+            if pass_ == "bwd_dkdv":
+                want_pairs += 4 * (ni - t * outer // inner)
+            else:
+                want_pairs += 4 * min(ni, -(-(t + 1) * outer // inner))
+    assert (items, pairs) == (want_items, want_pairs)
+    full = sa.plan_stats(len(lens), 4, 2048, 64, lens, pass_)[1]
+    assert pairs < full  # roughly half the tile pairs are skipped
+
+
+def test_bad_mask_mode():
+    a, keep = args()
+    a.mask = 2
+    for f in (fwd, dq, dkdv):
+        assert f(a) == 11
