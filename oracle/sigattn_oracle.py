@@ -34,7 +34,9 @@ Readings where the pages are silent or ambiguous (each one is a choice):
 * padded query rows of O and dQ, and padded key rows of dK and dV, are 0;
   padded rows of dO are ignored; a sequence with n_b = 0 gives all-zero outputs
   and no logarithm is evaluated for it.
-* the bias is a constant (no gradient flows to it).
+* the bias is a constant by default.  The learnable variant ("per_head": one
+  trained value per head) also reports the gradient of the bias: per key, the
+  sum over queries of dX (see attention()).
 
 Every function here is pinned by tests that do not re-run this code's own
 formulas: closed forms, a textbook logistic, finite differences, automatic
@@ -46,7 +48,7 @@ import math
 
 import numpy as np
 
-BIAS_MODES = ("seqlen", "fixed_n", "const")
+BIAS_MODES = ("seqlen", "fixed_n", "const", "per_head")
 
 
 def logistic(x):
@@ -82,6 +84,15 @@ def bias(n: int, mode: str = "seqlen", arg=None) -> float:
             raise ValueError("const bias needs a finite arg")
         return float(arg)
     raise ValueError(f"unknown bias mode {mode!r}")
+
+
+def per_head_bias(values, h: int) -> float:
+    """The learnable variant: one bias value per head, b = values[h] (the
+    summary's additive bias term made a trained parameter, one per head)."""
+    vals = np.asarray(values, dtype=np.float64)
+    if vals.ndim != 1 or not np.all(np.isfinite(vals)):
+        raise ValueError("per_head bias needs a 1-D array of finite values, one per head")
+    return float(vals[h])
 
 
 def causal_mask(n: int):
@@ -135,7 +146,13 @@ def attention(q, k, v, seqlens, do=None, bias_mode: str = "seqlen", bias_arg=Non
     """Whole padded batch.  q, k, v, do: float64 [B, H, Lmax, d]; seqlens: [B].
 
     Returns {"o": ...} and, if do is given, also "dq", "dk", "dv"; every output
-    is [B, H, Lmax, d] float64 with padded rows set to 0.
+    is [B, H, Lmax, d] float64 with padded rows set to 0.  With do, "dbias"
+    ([B, H, Lmax]) holds for every valid key j the sum over queries i of dX_ij:
+    since each score is X_ij = s q_i.k_j + b, the derivative of l with respect
+    to that (sequence, head)'s bias is the sum of this row, and a per-head bias
+    gets the sum over sequences and keys.  Padded entries are 0.
+
+    bias_mode "per_head": bias_arg is an array of H values, b = bias_arg[h].
 
     causal: the variant for autoregressive use (the language experiments of
     "Theory, Analysis, and Best Practices for Sigmoid Self-Attention", abstract),
@@ -154,19 +171,24 @@ def attention(q, k, v, seqlens, do=None, bias_mode: str = "seqlen", bias_arg=Non
         do = np.asarray(do, dtype=np.float64)
         for key in ("dq", "dk", "dv"):
             out[key] = np.zeros((B, H, L, d))
+        out["dbias"] = np.zeros((B, H, L))
+    if bias_mode == "per_head":
+        per_head_bias(bias_arg, H - 1)  # validates the array (and that it holds H values)
     for bi in range(B):
         n = int(seqlens[bi])
         if n == 0:
             continue
-        b = bias(n, bias_mode, bias_arg)
+        b = bias(n, bias_mode, bias_arg) if bias_mode != "per_head" else None
         for h in range(H):
+            bh = b if b is not None else per_head_bias(bias_arg, h)
             qv, kv, vv = q[bi, h, :n], k[bi, h, :n], v[bi, h, :n]
-            out["o"][bi, h, :n] = head_forward(qv, kv, vv, b, causal)
+            out["o"][bi, h, :n] = head_forward(qv, kv, vv, bh, causal)
             if do is not None:
-                dq, dk, dv = head_backward(qv, kv, vv, do[bi, h, :n], b, causal=causal)
+                dq, dk, dv, it = head_backward(qv, kv, vv, do[bi, h, :n], bh, intermediates=True, causal=causal)
                 out["dq"][bi, h, :n] = dq
                 out["dk"][bi, h, :n] = dk
                 out["dv"][bi, h, :n] = dv
+                out["dbias"][bi, h, :n] = it["dx"].sum(axis=0)  # over queries i, per key j
     return out
 
 

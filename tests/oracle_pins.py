@@ -395,3 +395,65 @@ def pin_causal_finite_differences(O):
 
 
 ALL_PINS += [pin_causal_zero_query, pin_causal_brute_force, pin_causal_prefix, pin_causal_finite_differences]
+
+
+# --- learnable per-head bias and its gradient -------------------------------
+
+def pin_dbias_zero_scores_closed_form(O):
+    """Q = K = 0 makes every score equal to the head's bias b_h, so
+    dX_ij = sigma'(b_h) (dO_i . V_j) and the per-key sum over queries is
+    sigma'(b_h) (sum_i dO_i) . V_j (over i >= j in the causal variant);
+    sigma' from scipy's logistic."""
+    B, H, L, d = 2, 2, 7, 3
+    seqlens = [7, 4]
+    vals = np.array([0.4, -1.3])
+    v, do = _rand((B, H, L, d), 61), _rand((B, H, L, d), 62)
+    q = k = np.zeros((B, H, L, d))
+    for causal in (False, True):
+        g = O.attention(q, k, v, seqlens, do=do, bias_mode="per_head", bias_arg=vals, causal=causal)
+        for b, n in enumerate(seqlens):
+            for h in range(H):
+                sp = scipy.special.expit(vals[h]) * scipy.special.expit(-vals[h])
+                for j in range(n):
+                    rows = range(j, n) if causal else range(n)
+                    want = sp * sum(float(do[b, h, i] @ v[b, h, j]) for i in rows)
+                    assert abs(g["dbias"][b, h, j] - want) < 1e-12, (causal, b, h, j)
+            assert np.all(g["dbias"][b, :, n:] == 0.0)
+
+
+def pin_dbias_finite_differences(O):
+    """Central differences of l = sum(O * dO) with respect to each head's bias
+    value equal the sum of that head's dbias over sequences and keys."""
+    B, H, L, d = 2, 2, 5, 2
+    seqlens = [5, 3]
+    q, k, v, do = (_rand((B, H, L, d), s) for s in (63, 64, 65, 66))
+    vals = np.array([-0.7, 0.2])
+    for causal in (False, True):
+        g = O.attention(q, k, v, seqlens, do=do, bias_mode="per_head", bias_arg=vals, causal=causal)
+        eps = 1e-6
+        for h in range(H):
+            vp, vm = vals.copy(), vals.copy()
+            vp[h] += eps
+            vm[h] -= eps
+            lp = np.sum(O.attention(q, k, v, seqlens, bias_mode="per_head", bias_arg=vp, causal=causal)["o"] * do)
+            lm = np.sum(O.attention(q, k, v, seqlens, bias_mode="per_head", bias_arg=vm, causal=causal)["o"] * do)
+            fd = (lp - lm) / (2 * eps)
+            got = g["dbias"][:, h].sum()
+            assert abs(fd - got) < 1e-7 * (1 + abs(fd)), (causal, h, fd, got)
+
+
+def pin_per_head_matches_constant(O):
+    """Head h under per-head values equals the constant-bias mode with that
+    head's value, outputs and gradients (fixes which head reads which value)."""
+    B, H, L, d = 2, 3, 6, 4
+    seqlens = [6, 2]
+    q, k, v, do = (_rand((B, H, L, d), s) for s in (67, 68, 69, 70))
+    vals = np.array([0.5, -2.0, 1.25])
+    g = O.attention(q, k, v, seqlens, do=do, bias_mode="per_head", bias_arg=vals)
+    for h in range(H):
+        c = O.attention(q, k, v, seqlens, do=do, bias_mode="const", bias_arg=float(vals[h]))
+        for key in ("o", "dq", "dk", "dv", "dbias"):
+            _close(g[key][:, h], c[key][:, h], what=f"per-head {key} h={h}")
+
+
+ALL_PINS += [pin_dbias_zero_scores_closed_form, pin_dbias_finite_differences, pin_per_head_matches_constant]

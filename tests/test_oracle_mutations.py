@@ -16,7 +16,12 @@ SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__
 MUTATIONS = {
     "bias_sign": ("return -math.log(n)", "return math.log(n)"),
     "bias_log10": ("return -math.log(n)", "return -math.log10(n)"),
-    "bias_uses_lmax": ("b = bias(n, bias_mode, bias_arg)\n        for h", "b = bias(L, bias_mode, bias_arg)\n        for h"),
+    "bias_uses_lmax": ("b = bias(n, bias_mode, bias_arg) if", "b = bias(L, bias_mode, bias_arg) if"),
+    "dbias_sums_over_keys": ('it["dx"].sum(axis=0)', 'it["dx"].sum(axis=1)'),
+    "dbias_uses_dp": ('it["dx"].sum(axis=0)', 'it["dp"].sum(axis=0)'),
+    "dbias_uses_p": ('it["dx"].sum(axis=0)', 'it["p"].sum(axis=0)'),
+    "per_head_bias_first_head": ("return float(vals[h])", "return float(vals[0])"),
+    "per_head_bias_negated": ("return float(vals[h])", "return -float(vals[h])"),
     "scale_1_over_d": ("return 1.0 / math.sqrt(d)", "return 1.0 / d"),
     "scale_dropped": ("x = s * (q @ k.T) + b          # scores", "x = (q @ k.T) + b          # scores"),
     "scores_transposed": ("x = s * (q @ k.T) + b          # scores", "x = s * (k @ q.T) + b          # scores"),
