@@ -76,10 +76,13 @@ def load_traffic(kernel: str, workload: str, precision: str):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
-def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="sigmoid", causal=False):
+def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="sigmoid", causal=False,
+                  bias="seqlen"):
     """Time `steps` passes of forward + backward (HIP events around every
     call, on the launch stream).  attn="softmax" times the softmax comparison
-    path on the same inputs and schedule: forward, the delta pass, dQ, dK/dV."""
+    path on the same inputs and schedule: forward, the delta pass, dQ, dK/dV.
+    bias="per_head": a learnable per-head bias (values -ln of the mean
+    length), its gradient rows from the dK/dV call and the per-head sum."""
     import torch
 
     import sigmoid_attention_amd as sa
@@ -98,11 +101,20 @@ def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="s
     lse2 = delta = None
     if causal:
         kw["causal"] = True
+    rows = db = None
+    if bias == "per_head":
+        (_, H_, _, _), _ = sa._binding.layout_strides(q, layout)
+        kw["bias_mode"] = "per_head"
+        kw["bias_arg"] = torch.full((H_,), -math.log(max(1.0, float(np.mean(n)))), dtype=torch.float32, device=dev)
+        rows = sa._binding._rows_like(q, layout)
+        db = torch.empty(H_, dtype=torch.float32, device=dev)
     if attn == "softmax":
         (B, H, L, _), _ = sa._binding.layout_strides(q, layout)
         lse2 = torch.empty((B, H, L), dtype=torch.float32, device=dev)
         delta = torch.empty_like(lse2)
     names = ("fwd", "bwd_dq", "bwd_dkdv") if attn == "sigmoid" else ("fwd", "bwd_prep", "bwd_dq", "bwd_dkdv")
+    if rows is not None:
+        names += ("bwd_bias_grad",)
 
     def step(ev=None):
         def mark(i):
@@ -114,8 +126,14 @@ def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="s
             mark(1)
             sa.bwd_dq(q, k, v, do, n, dq=dq, **kw)
             mark(2)
-            sa.bwd_dkdv(q, k, v, do, n, dk=dk, dv=dv, **kw)
-            mark(3)
+            if rows is None:
+                sa.bwd_dkdv(q, k, v, do, n, dk=dk, dv=dv, **kw)
+                mark(3)
+            else:
+                sa.bwd_dkdv_dbias(q, k, v, do, n, dk=dk, dv=dv, dbias=rows, **kw)
+                mark(3)
+                sa.bias_grad(rows, n, db=db)
+                mark(4)
         else:
             sa.softmax_fwd(q, k, v, n, o=o, lse2=lse2, **kw)
             mark(1)
@@ -280,6 +298,8 @@ def main():
                     help="tensor layout handed to the library: [B,H,Lmax,d] or [B,Lmax,H,d] (strided path)")
     ap.add_argument("--causal", action="store_true",
                     help="causal mask (query i sees keys 0..i); FLOPs count the n(n+1)/2 visible pairs")
+    ap.add_argument("--bias", default="seqlen", choices=["seqlen", "per_head"],
+                    help="per_head: a learnable per-head bias, with its gradient computed in the backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -332,7 +352,8 @@ def main():
     name = a.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
     precision = a.precision if a.precision != "auto" else ("split" if w.scale_qkv > 1.0 else "fast")
-    r = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn=a.attn, causal=a.causal)
+    r = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn=a.attn, causal=a.causal,
+                      bias=a.bias)
     n = r["seqlens"]
     total = r["fwd_flops"] + r["bwd_flops"]
     value = tflops(total, r["step_ms"])
@@ -355,6 +376,9 @@ def main():
                                                         r["kernel_avg_ms"][kname]), 2)}
             for kname in KERNEL_FLOP_UNITS},
     }
+    if "bwd_bias_grad" in r["kernel_avg_ms"]:
+        roofline["per_kernel"]["bwd_bias_grad"] = {"avg_ms": round(r["kernel_avg_ms"]["bwd_bias_grad"], 5),
+                                               "median_ms": round(r["kernel_median_ms"]["bwd_bias_grad"], 5)}
     if "bwd_prep" in r["kernel_avg_ms"]:
         roofline["per_kernel"]["bwd_prep"] = {"avg_ms": round(r["kernel_avg_ms"]["bwd_prep"], 5),
                                               "median_ms": round(r["kernel_median_ms"]["bwd_prep"], 5)}
@@ -373,7 +397,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": name, "B": w.B, "H": w.H, "d": w.d, "Lmax": w.Lmax, "seqlens": [int(x) for x in n],
-            "precision": precision, "bias": "-ln(n_b)" if a.attn == "sigmoid" else "none (softmax)",
+            "precision": precision,
+            "bias": ("none (softmax)" if a.attn != "sigmoid" else
+                     "learnable per head, with gradient" if a.bias == "per_head" else "-ln(n_b)"),
             "layout": a.layout, "attention": a.attn, "mask": "causal" if a.causal else "none",
             "valid_token_frac": round(float(np.sum(n)) / (w.B * w.Lmax), 4),
             "valid_pair_frac": round(float(np.sum(np.asarray(n, np.float64) ** 2)) / (w.B * w.Lmax ** 2), 4),
@@ -435,7 +461,7 @@ def main():
         }
         del rc
 
-    if not a.no_cpu_baseline and a.attn == "sigmoid" and not a.causal:
+    if not a.no_cpu_baseline and a.attn == "sigmoid" and not a.causal and a.bias == "seqlen":
         rec, worst = cpu_baseline(r["case"], r["outputs"], a.cpu_seconds)
         out["cpu_baseline"] = {k_: v_ for k_, v_ in rec.items() if k_ != "seconds"}
         out["parity_worst_ratio_on_cpu_sample"] = round(worst, 4)

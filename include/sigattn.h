@@ -58,12 +58,15 @@ extern "C" {
 
 typedef enum sigattn_status {
   SIGATTN_OK = 0,
-  SIGATTN_ERR_NULL = 1,      /* args, a tensor pointer or seqlens is NULL               */
+  SIGATTN_ERR_NULL = 1,      /* args, a tensor pointer, seqlens, or (bias mode 3)
+                                head_bias is NULL                                       */
   SIGATTN_ERR_SHAPE = 2,     /* B, H or Lmax < 1, d not 64 or 128, sizes overflow, or
                                 (Lmax + 256) * d * 2 > 2^31 - 1 (32-bit slice offsets)  */
   SIGATTN_ERR_SEQLEN = 3,    /* some seqlens[b] outside [0, Lmax]                       */
-  SIGATTN_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned                 */
-  SIGATTN_ERR_ALIAS = 5,     /* an output overlaps an input or another output           */
+  SIGATTN_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned (head_bias and
+                                sigattn_bias_grad's db: 4-byte)                         */
+  SIGATTN_ERR_ALIAS = 5,     /* an output overlaps an input or another output (or the
+                                per-head bias values)                                   */
   SIGATTN_ERR_BIAS = 6,      /* unknown bias_mode, non-finite bias_arg, or bias_arg <= 0
                                 with SIGATTN_BIAS_NEG_LOG_N                             */
   SIGATTN_ERR_PRECISION = 7, /* unknown precision                                       */
@@ -89,7 +92,12 @@ typedef enum sigattn_mask {
 typedef enum sigattn_bias_mode {
   SIGATTN_BIAS_NEG_LOG_SEQLEN = 0, /* b_b = -ln(n_b), n_b = valid length (default)  */
   SIGATTN_BIAS_NEG_LOG_N = 1,      /* b = -ln(bias_arg), a fixed n (e.g. Lmax)      */
-  SIGATTN_BIAS_CONST = 2           /* b = bias_arg                                  */
+  SIGATTN_BIAS_CONST = 2,          /* b = bias_arg                                  */
+  SIGATTN_BIAS_PER_HEAD = 3        /* b_h = head_bias[h]: one value per head, read
+                                      from device memory by the kernels, so that a
+                                      trained bias needs no host round trip (the
+                                      learnable variant; its gradient comes from
+                                      sigattn_bwd_dkdv_dbias)                       */
 } sigattn_bias_mode;
 
 /* How P (forward, dV) and dX (dQ, dK) enter the second bf16 matrix product. */
@@ -136,6 +144,10 @@ typedef struct sigattn_args {
                                dq: q, k, v, dout, dq; dkdv: q, k, v, dout, dk, dv);
                                read during the call only                            */
   int32_t mask;             /* sigattn_mask; 0 = bidirectional                      */
+  const float *head_bias;   /* DEVICE pointer to H fp32 bias values, 4-byte aligned,
+                               read by the kernels in bias mode 3 (the values must
+                               be finite; they are not checked); ignored in the
+                               other modes                                          */
 } sigattn_args;
 
 /* Forward: O = sigma(Q K^T / sqrt(d) + b) V on valid rows; padded rows of O = 0.
@@ -154,6 +166,27 @@ sigattn_status sigattn_bwd_dq(const sigattn_args *args, const void *q, const voi
  * atomics (§2C). */
 sigattn_status sigattn_bwd_dkdv(const sigattn_args *args, const void *q, const void *k,
                                 const void *v, const void *dout, void *dk, void *dv);
+
+/* Backward, key side, with the gradient of the bias: as sigattn_bwd_dkdv, and
+ * also, per key row, dbias[b, h, j] = sum over valid queries i of dX_ij, where
+ * dX = dO V^T * P * (1 - P) is the gradient of the scores X_ij = q_i.k_j /
+ * sqrt(d) + b (summary §2A formula, §2B derivative).  Because b enters every
+ * score of its (sequence, head) with coefficient 1, dl/db for that (b, h) is
+ * the sum of its row of dbias; a per-head bias sums over sequences too
+ * (sigattn_bias_grad).  dbias: device fp32, contiguous [B, H, Lmax], 16-byte
+ * aligned, written in full (0 on padded rows j >= n_b), must not overlap a
+ * tensor argument.  Each row has a single writer: no atomics.  Any bias mode. */
+sigattn_status sigattn_bwd_dkdv_dbias(const sigattn_args *args, const void *q, const void *k,
+                                      const void *v, const void *dout, void *dk, void *dv,
+                                      float *dbias);
+
+/* Per-head bias gradient: db[h] = sum over b and j of dbias[b, h, j] (dbias as
+ * written by sigattn_bwd_dkdv_dbias).  db: device fp32 [H], 4-byte aligned,
+ * must not overlap dbias.  One workgroup per head sums in a fixed order, so
+ * the result is deterministic.  Uses args' B, H, Lmax, seqlens (validated as
+ * for the other calls) and stream; bias, precision and mask are ignored
+ * except for validation. */
+sigattn_status sigattn_bias_grad(const sigattn_args *args, const float *dbias, float *db);
 
 /* Softmax attention on the same padded batches and schedule: the mechanism
  * sigmoid attention replaces, provided to compare the two on equal terms

@@ -16,7 +16,7 @@ import numpy as np
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsigattn.so")
 _lib = None
 
-BIAS_MODES = {"seqlen": 0, "fixed_n": 1, "const": 2}
+BIAS_MODES = {"seqlen": 0, "fixed_n": 1, "const": 2, "per_head": 3}
 PRECISIONS = {"fast": 0, "split": 1}
 PASSES = {"fwd": 0, "bwd_dq": 1, "bwd_dkdv": 2}
 
@@ -31,7 +31,8 @@ LAYOUTS = {"bhld": (0, 1, 2, 3), "blhd": (0, 2, 1, 3)}
 
 EXPORTED = ("sigattn_fwd", "sigattn_bwd_dq", "sigattn_bwd_dkdv", "sigattn_status_str",
             "sigattn_plan_stats", "sigattn_tile_shape", "sigattn_validate", "sigattn_softmax_fwd",
-            "sigattn_softmax_bwd_prep", "sigattn_softmax_bwd_dq", "sigattn_softmax_bwd_dkdv")
+            "sigattn_softmax_bwd_prep", "sigattn_softmax_bwd_dq", "sigattn_softmax_bwd_dkdv",
+            "sigattn_bwd_dkdv_dbias", "sigattn_bias_grad")
 
 
 class SigattnStrides(ctypes.Structure):
@@ -47,6 +48,7 @@ class SigattnArgs(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("strides", ctypes.POINTER(SigattnStrides)),
         ("mask", ctypes.c_int32),
+        ("head_bias", ctypes.c_void_p),
     ]
 
 
@@ -90,8 +92,10 @@ def load() -> ctypes.CDLL:
     lib.sigattn_softmax_bwd_prep.argtypes = [ap, vp, vp, vp]
     lib.sigattn_softmax_bwd_dq.argtypes = [ap, vp, vp, vp, vp, vp, vp, vp]
     lib.sigattn_softmax_bwd_dkdv.argtypes = [ap, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sigattn_bwd_dkdv_dbias.argtypes = [ap, vp, vp, vp, vp, vp, vp, vp]
+    lib.sigattn_bias_grad.argtypes = [ap, vp, vp]
     for f in (lib.sigattn_softmax_fwd, lib.sigattn_softmax_bwd_prep, lib.sigattn_softmax_bwd_dq,
-              lib.sigattn_softmax_bwd_dkdv):
+              lib.sigattn_softmax_bwd_dkdv, lib.sigattn_bwd_dkdv_dbias, lib.sigattn_bias_grad):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -102,12 +106,13 @@ def status_str(code: int) -> str:
 
 
 def make_args(B, H, Lmax, d, seqlens, bias_mode="seqlen", bias_arg=0.0, precision="fast", stream=0,
-              strides=None, causal=False):
+              strides=None, causal=False, head_bias=None):
     """Build a sigattn_args struct.  `strides`: None (every tensor contiguous
     [B, H, Lmax, d]) or one (b, h, l) element-stride triple per tensor
-    argument, in argument order.  Returns (args, keepalive) — keep the second
-    object alive for as long as the struct is used (it owns the lengths and
-    strides)."""
+    argument, in argument order.  `head_bias`: device address of H fp32
+    values (bias mode "per_head").  Returns (args, keepalive) — keep the
+    second object alive for as long as the struct is used (it owns the
+    lengths and strides)."""
     lens = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
     a = SigattnArgs()
     a.B, a.H, a.Lmax, a.d = int(B), int(H), int(Lmax), int(d)
@@ -117,6 +122,7 @@ def make_args(B, H, Lmax, d, seqlens, bias_mode="seqlen", bias_arg=0.0, precisio
     a.precision = PRECISIONS[precision] if isinstance(precision, str) else int(precision)
     a.stream = int(stream) if stream else None
     a.mask = int(causal) if not isinstance(causal, bool) else (1 if causal else 0)
+    a.head_bias = int(head_bias) if head_bias else None
     st = None
     if strides is not None:
         st = (SigattnStrides * len(strides))(*[SigattnStrides(int(b), int(h), int(l)) for b, h, l in strides])
@@ -164,8 +170,16 @@ def _tensor_args(ts, seqlens, bias_mode, bias_arg, precision, stream, layout="bh
     contiguous = all(s == (H * L * d, L * d, d) for s in strides)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    head_bias = None
+    if bias_mode == "per_head" or bias_mode == BIAS_MODES["per_head"]:
+        hb = bias_arg
+        if (not isinstance(hb, torch.Tensor) or hb.dtype != torch.float32 or tuple(hb.shape) != (H,)
+                or not hb.is_contiguous() or hb.device != q.device):
+            raise ValueError("bias mode per_head takes bias_arg = a contiguous float32 tensor of H values "
+                             "on the tensors' device")
+        head_bias, bias_arg = hb.data_ptr(), 0.0
     return make_args(B, H, L, d, seqlens, bias_mode, bias_arg, precision, stream,
-                     None if contiguous else strides, causal)
+                     None if contiguous else strides, causal, head_bias)
 
 
 def _new_like(t):
@@ -224,6 +238,48 @@ def bwd_dkdv(q, k, v, dout, seqlens, dk=None, dv=None, bias_mode="seqlen", bias_
                                        dout.data_ptr(), dk.data_ptr(), dv.data_ptr()), "sigattn_bwd_dkdv")
     del keep
     return dk, dv
+
+
+def bwd_dkdv_dbias(q, k, v, dout, seqlens, dk=None, dv=None, dbias=None, bias_mode="seqlen", bias_arg=0.0,
+                   precision="fast", stream=None, layout: str = "bhld", causal: bool = False):
+    """dK, dV and the bias gradient rows: dbias[b, h, j] = sum over valid
+    queries i of dX_ij (fp32 [B, H, Lmax], 0 on padded rows).  Returns
+    (dK, dV, dbias)."""
+    import torch
+
+    dk = _new_like(k) if dk is None else dk
+    dv = _new_like(v) if dv is None else dv
+    dbias = _rows_like(q, layout) if dbias is None else dbias
+    _check_rows(dbias, q, layout)
+    args, keep = _tensor_args((q, k, v, dout, dk, dv), seqlens, bias_mode, bias_arg, precision, stream, layout,
+                              causal)
+    with torch.cuda.device(q.device):
+        _check(load().sigattn_bwd_dkdv_dbias(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                             dout.data_ptr(), dk.data_ptr(), dv.data_ptr(), dbias.data_ptr()),
+               "sigattn_bwd_dkdv_dbias")
+    del keep
+    return dk, dv, dbias
+
+
+def bias_grad(dbias, seqlens, db=None, stream=None):
+    """db[h] = sum over sequences and rows of dbias[:, h, :] (fp32 [H]), the
+    gradient of a per-head bias.  dbias as returned by bwd_dkdv_dbias."""
+    import torch
+
+    if dbias.dtype != torch.float32 or dbias.dim() != 3 or not dbias.is_contiguous() or not dbias.is_cuda:
+        raise ValueError("dbias must be a contiguous float32 [B, H, Lmax] tensor on the GPU")
+    B, H, L = dbias.shape
+    db = torch.empty(H, dtype=torch.float32, device=dbias.device) if db is None else db
+    if db.dtype != torch.float32 or tuple(db.shape) != (H,) or not db.is_contiguous() or db.device != dbias.device:
+        raise ValueError("db must be a contiguous float32 [H] tensor on dbias's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(dbias.device).cuda_stream
+    # d is not used by this call (it is validated like the others)
+    args, keep = make_args(B, H, L, 64, seqlens, stream=stream)
+    with torch.cuda.device(dbias.device):
+        _check(load().sigattn_bias_grad(ctypes.byref(args), dbias.data_ptr(), db.data_ptr()), "sigattn_bias_grad")
+    del keep
+    return db
 
 
 def _rows_like(t, layout):

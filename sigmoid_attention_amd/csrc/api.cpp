@@ -53,6 +53,10 @@ sigattn_status check_args(const sigattn_args* a) {
     case SIGATTN_BIAS_CONST:
       if (!std::isfinite(a->bias_arg)) return SIGATTN_ERR_BIAS;
       break;
+    case SIGATTN_BIAS_PER_HEAD:
+      if (!a->head_bias) return SIGATTN_ERR_NULL;
+      if ((uintptr_t)a->head_bias % 4) return SIGATTN_ERR_ALIGN;
+      break;
     default: return SIGATTN_ERR_BIAS;
   }
   if (a->precision != SIGATTN_PREC_FAST && a->precision != SIGATTN_PREC_SPLIT) return SIGATTN_ERR_PRECISION;
@@ -169,6 +173,24 @@ sigattn_status check_ptrs(const sigattn_args* a, const void* const* in, int nin,
   return SIGATTN_OK;
 }
 
+// The per-head bias values are read while the outputs are written: they may
+// overlap inputs but no output (tensors t[nt_in..nt-1], row arrays r[0..nr-1]).
+sigattn_status check_head_bias(const sigattn_args* a, const void* const* t, int nt, int nt_in,
+                               const void* const* r = nullptr, int nr = 0) {
+  if (a->bias_mode != SIGATTN_BIAS_PER_HEAD) return SIGATTN_OK;
+  const uintptr_t lo = (uintptr_t)a->head_bias, hi = lo + 4 * (uintptr_t)a->H;
+  const std::vector<View> v = views(a, t, nt);
+  for (int j = nt_in; j < nt; ++j) {
+    uintptr_t tl, th;
+    span(a, v[j], tl, th);
+    if (lo < th && tl < hi) return SIGATTN_ERR_ALIAS;
+  }
+  const uintptr_t bytes = (uintptr_t)a->B * a->H * a->Lmax * 4;
+  for (int j = 0; j < nr; ++j)
+    if (lo < (uintptr_t)r[j] + bytes && (uintptr_t)r[j] < hi) return SIGATTN_ERR_ALIAS;
+  return SIGATTN_OK;
+}
+
 // fp32 [B, H, Lmax] per-row arrays of the softmax path: null, alignment, and
 // no overlap between an output (row array or tensor) and anything else.
 sigattn_status check_rows(const sigattn_args* a, const void* const* t, int nt, int nt_in, const void* const* r,
@@ -225,6 +247,7 @@ sigattn_status run(const sigattn_args* a, int32_t pass, const void* const* t, in
   (void)hipGetLastError();  // start from a clean per-thread error state
   for (Launch& L : plan) {
     set_strides(a, t, n, L);
+    L.sched.head_bias = a->bias_mode == SIGATTN_BIAS_PER_HEAD ? a->head_bias : nullptr;
     if (launch_one(L) != hipSuccess) return SIGATTN_ERR_HIP;
   }
   return SIGATTN_OK;
@@ -242,6 +265,7 @@ sigattn_status sigattn_fwd(const sigattn_args* a, const void* q, const void* k, 
   if ((s = check_ptrs(a, in, 3, out, 1)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
   const void* t[] = {q, k, v, o};
+  if ((s = check_head_bias(a, t, 4, 3)) != SIGATTN_OK) return s;
   return run(a, SIGATTN_PASS_FWD, t, 4, [&](const Launch& L) {
     return sigattn::launch_fwd(a->d, split, L, q, k, v, o, (hipStream_t)a->stream);
   });
@@ -256,6 +280,7 @@ sigattn_status sigattn_bwd_dq(const sigattn_args* a, const void* q, const void* 
   if ((s = check_ptrs(a, in, 4, out, 1)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
   const void* t[] = {q, k, v, dout, dq};
+  if ((s = check_head_bias(a, t, 5, 4)) != SIGATTN_OK) return s;
   return run(a, SIGATTN_PASS_BWD_DQ, t, 5, [&](const Launch& L) {
     return sigattn::launch_bwd_dq(a->d, split, L, q, k, v, dout, dq, (hipStream_t)a->stream);
   });
@@ -270,9 +295,41 @@ sigattn_status sigattn_bwd_dkdv(const sigattn_args* a, const void* q, const void
   if ((s = check_ptrs(a, in, 4, out, 2)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
   const void* t[] = {q, k, v, dout, dk, dv};
+  if ((s = check_head_bias(a, t, 6, 4)) != SIGATTN_OK) return s;
   return run(a, SIGATTN_PASS_BWD_DKDV, t, 6, [&](const Launch& L) {
-    return sigattn::launch_bwd_dkdv(a->d, split, L, q, k, v, dout, dk, dv, (hipStream_t)a->stream);
+    return sigattn::launch_bwd_dkdv(a->d, split, L, q, k, v, dout, dk, dv, nullptr, (hipStream_t)a->stream);
   });
+}
+
+sigattn_status sigattn_bwd_dkdv_dbias(const sigattn_args* a, const void* q, const void* k, const void* v,
+                                      const void* dout, void* dk, void* dv, float* dbias) {
+  sigattn_status s = check_args(a);
+  if (s != SIGATTN_OK) return s;
+  const void* in[] = {q, k, v, dout};
+  void* out[] = {dk, dv};
+  if ((s = check_ptrs(a, in, 4, out, 2)) != SIGATTN_OK) return s;
+  const void* t[] = {q, k, v, dout, dk, dv};
+  const void* r[] = {dbias};
+  if ((s = check_rows(a, t, 6, 4, r, 1, 0)) != SIGATTN_OK) return s;
+  if ((s = check_head_bias(a, t, 6, 4, r, 1)) != SIGATTN_OK) return s;
+  const bool split = a->precision == SIGATTN_PREC_SPLIT;
+  return run(a, SIGATTN_PASS_BWD_DKDV, t, 6, [&](const Launch& L) {
+    return sigattn::launch_bwd_dkdv(a->d, split, L, q, k, v, dout, dk, dv, dbias, (hipStream_t)a->stream);
+  });
+}
+
+sigattn_status sigattn_bias_grad(const sigattn_args* a, const float* dbias, float* db) {
+  sigattn_status s = check_args(a);
+  if (s != SIGATTN_OK) return s;
+  if (!dbias || !db) return SIGATTN_ERR_NULL;
+  if ((uintptr_t)dbias % 16 || (uintptr_t)db % 4) return SIGATTN_ERR_ALIGN;
+  const uintptr_t rl = (uintptr_t)dbias, rh = rl + (uintptr_t)a->B * a->H * a->Lmax * 4;
+  const uintptr_t ol = (uintptr_t)db, oh = ol + 4 * (uintptr_t)a->H;
+  if (ol < rh && rl < oh) return SIGATTN_ERR_ALIAS;
+  (void)hipGetLastError();
+  if (sigattn::launch_bias_grad(a->B, a->H, a->Lmax, dbias, db, (hipStream_t)a->stream) != hipSuccess)
+    return SIGATTN_ERR_HIP;
+  return SIGATTN_OK;
 }
 
 sigattn_status sigattn_validate(const sigattn_args* a, int32_t pass, const void* const* t) {
@@ -284,7 +341,8 @@ sigattn_status sigattn_validate(const sigattn_args* a, int32_t pass, const void*
   const int nin = pass == SIGATTN_PASS_FWD ? 3 : 4;
   const int nout = pass == SIGATTN_PASS_BWD_DKDV ? 2 : 1;
   void* out[2] = {const_cast<void*>(t[nin]), nout == 2 ? const_cast<void*>(t[nin + 1]) : nullptr};
-  return check_ptrs(a, t, nin, out, nout);
+  if ((s = check_ptrs(a, t, nin, out, nout)) != SIGATTN_OK) return s;
+  return check_head_bias(a, t, nin + nout, nin);
 }
 
 sigattn_status sigattn_softmax_fwd(const sigattn_args* a, const void* q, const void* k, const void* v, void* o,
@@ -372,11 +430,11 @@ sigattn_status sigattn_softmax_bwd_dkdv(const sigattn_args* a, const void* q, co
 const char* sigattn_status_str(sigattn_status s) {
   switch (s) {
     case SIGATTN_OK: return "ok";
-    case SIGATTN_ERR_NULL: return "null pointer (args, tensor or seqlens)";
+    case SIGATTN_ERR_NULL: return "null pointer (args, tensor, seqlens or per-head bias)";
     case SIGATTN_ERR_SHAPE: return "bad shape: B, H, Lmax must be >= 1 and d must be 64 or 128";
     case SIGATTN_ERR_SEQLEN: return "a valid length lies outside [0, Lmax]";
-    case SIGATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-    case SIGATTN_ERR_ALIAS: return "an output overlaps an input or another output";
+    case SIGATTN_ERR_ALIGN: return "a pointer is misaligned (tensors 16 bytes, per-head bias values 4 bytes)";
+    case SIGATTN_ERR_ALIAS: return "an output overlaps an input, another output or the per-head bias values";
     case SIGATTN_ERR_BIAS: return "bad bias: unknown mode, non-finite argument, or n <= 0 for a fixed-n bias";
     case SIGATTN_ERR_PRECISION: return "unknown precision mode";
     case SIGATTN_ERR_HIP: return "HIP kernel launch failed";

@@ -290,6 +290,12 @@ __device__ __forceinline__ void zero_padded_rows(const Sched& S, uint16_t* __res
       rows[(size_t)bh * S.Lmax + row] = 0.0f;
 }
 
+// -b log2(e) for the item's (sequence, head): from the schedule, or for a
+// per-head bias from the values in device memory (a uniform scalar load).
+__device__ __forceinline__ float item_c2(const Sched& S, const Item& it) {
+  return S.head_bias ? -1.4426950408889634f * S.head_bias[it.bh % S.H] : it.c2;
+}
+
 // Work item of this workgroup (see plan.h); false for idle blocks.  The
 // result is uniform across the workgroup.
 __device__ __forceinline__ bool find_item(const Sched& S, Item& it) {

@@ -58,10 +58,12 @@ __device__ __forceinline__ void sigmoid_chunk(const f32x16 (&sc)[2], int c, floa
   if (SPLIT) lo = to_bf16x8(p - to_f32x8(hi));
 }
 
-// dS = dP * sigma * (1 - sigma) for K-chunk c (and optionally sigma itself).
-template <int D, bool SPLIT, bool WANT_P, int NB>
+// dS = dP * sigma * (1 - sigma) for K-chunk c (and optionally sigma itself;
+// with DSUM, the chunk's eight fp32 dS values are also added to *dsum).
+template <int D, bool SPLIT, bool WANT_P, bool DSUM = false, int NB>
 __device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[NB], const f32x16 (&dp)[NB], int c, float c2,
-                                               bf16x8& dh, bf16x8& dl, bf16x8& ph, bf16x8& pl) {
+                                               bf16x8& dh, bf16x8& dl, bf16x8& ph, bf16x8& pl,
+                                               float* dsum = nullptr) {
   const f32x8 sv = chunk8(sc[c >> 1], c & 1), gv = chunk8(dp[c >> 1], c & 1);
   f32x8 p8, ds;
 #pragma unroll
@@ -76,6 +78,8 @@ __device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[NB], const f32
     ph = to_bf16x8(p8);
     if (SPLIT) pl = to_bf16x8(p8 - to_f32x8(ph));
   }
+  if constexpr (DSUM)  // pairwise: keeps the eight values' live ranges short
+    *dsum += ((ds[0] + ds[1]) + (ds[2] + ds[3])) + ((ds[4] + ds[5]) + (ds[6] + ds[7]));
 }
 
 // Causal mask (query i sees keys 0..i), applied only in tiles that straddle
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const float c2 = it.c2;
+  const float c2 = item_c2(S, it);
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BK, D> dma_k(w, lane, S.sl[1]), dma_v(w, lane, S.sl[2]);
@@ -543,7 +547,7 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const float c2 = it.c2;
+  const float c2 = item_c2(S, it);
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BK, D> dma_k(w, lane, S.sl[1]), dma_v(w, lane, S.sl[2]);
@@ -631,18 +635,18 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
 // latency is covered; the next tile's S and dP follow, with the fragments of
 // each K-step read one step ahead.
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT, bool SOFTMAX = false>
+template <int D, bool SPLIT, bool SOFTMAX = false, bool DB = false>
 __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    const float* __restrict__ LSE, const float* __restrict__ DELTA, const Sched S) {
+    const float* __restrict__ LSE, const float* __restrict__ DELTA, float* __restrict__ DBIAS, const Sched S) {
   constexpr int BKV = 128, BQ = DkdvCfg<D>::BQ, TILE = BQ * D, NMB = BQ / 32, NC = BQ / 16;
   __shared__ __align__(16) uint16_t lds[6 * TILE];  // Q0 Q1 Q2 G0 G1 G2
   // softmax: lse2 and delta of each inner tile's rows, 3 stages
   __shared__ __align__(16) float rowv[SOFTMAX ? 6 * BQ : 4];
 
   if ((int)blockIdx.x >= S.compute_blocks) {
-    zero_padded_rows<D>(S, dK, 4, dV, 5);
+    zero_padded_rows<D>(S, dK, 4, dV, 5, DB ? DBIAS : nullptr);
     return;
   }
   Item it;
@@ -650,7 +654,7 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const float c2 = it.c2;
+  const float c2 = item_c2(S, it);
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BQ, D> dma_q(w, lane, S.sl[0]), dma_g(w, lane, S.sl[3]);
@@ -695,6 +699,7 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   score_steps<D>(sA, Qb(0), kf, 0, D / 16, fa);
   score_steps<D>(dA, Gb(0), vf, 0, D / 16, fa);
 
+  float dsum = 0.0f;  // with DB: sum of this lane's dS values (its key column)
   auto step = [&](auto phase, int jr) {
     const int j = j0 + jr;  // inner (query) tile
     constexpr int P = decltype(phase)::value;
@@ -731,7 +736,7 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
           const f32x8 dlt8 = cat8(*(const f32x4*)(lt + BQ + r0), *(const f32x4*)(lt + BQ + r0 + 8));
           dsoftmax_chunk_row<D, SPLIT>(cs, cd, c, lse8, dlt8, dh[c], dl[c], ph[c], pl[c]);
         } else {
-          dsigmoid_chunk<D, SPLIT, true>(cs, cd, c, c2, dh[c], dl[c], ph[c], pl[c]);
+          dsigmoid_chunk<D, SPLIT, true, DB>(cs, cd, c, c2, dh[c], dl[c], ph[c], pl[c], &dsum);
         }
         if (c > 0) {
           value_chunk_pre<D, SPLIT>(dv, ag[(c - 1) & 1], ph[c - 1], pl[c - 1]);
@@ -752,6 +757,10 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   };
   run_steps(nq - j0, step);
 
+  if constexpr (DB) {
+    dsum += __shfl_xor(dsum, 32);  // the other half of the column's query rows
+    if (krow < n && hf == 0) DBIAS[(size_t)it.bh * S.Lmax + krow] = dsum;
+  }
   if (krow < n) {
     const float scale = S.out_scale;
     uint16_t* dstk = slice_base(dK, S, it.bh, 4) + (size_t)krow * S.sl[4];
@@ -810,11 +819,53 @@ hipError_t launch_dq_t(const Launch& L, const void* q, const void* k, const void
 
 template <int D, bool SPLIT>
 hipError_t launch_dkdv_t(const Launch& L, const void* q, const void* k, const void* v, const void* g, void* dk,
-                         void* dv, hipStream_t st) {
-  hipLaunchKernelGGL((dkdv_kernel<D, SPLIT>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dk, (uint16_t*)dv,
-                     (const float*)nullptr, (const float*)nullptr, L.sched);
+                         void* dv, float* dbias, hipStream_t st) {
+  if (dbias)
+    hipLaunchKernelGGL((dkdv_kernel<D, SPLIT, false, true>), dim3(L.blocks), dim3(kThreads), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dk,
+                       (uint16_t*)dv, (const float*)nullptr, (const float*)nullptr, dbias, L.sched);
+  else
+    hipLaunchKernelGGL((dkdv_kernel<D, SPLIT>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dk, (uint16_t*)dv,
+                       (const float*)nullptr, (const float*)nullptr, (float*)nullptr, L.sched);
   return hipGetLastError();
+}
+
+// db[h] = sum over sequences b and rows j of dbias[b, h, j]: one workgroup of
+// 1024 threads per head, each thread summing a fixed strided subset (16-byte
+// loads when the rows are 16-byte aligned), then a fixed-order tree: the
+// result does not depend on timing.
+constexpr int kBiasGradThreads = 1024;
+__global__ __launch_bounds__(kBiasGradThreads) void bias_grad_kernel(const float* __restrict__ dbias,
+                                                                     float* __restrict__ db, int32_t B, int32_t H,
+                                                                     int32_t Lmax) {
+  __shared__ float part[kBiasGradThreads];
+  const int h = (int)blockIdx.x, tid = (int)threadIdx.x;
+  float acc = 0.0f;
+  if (Lmax % 4 == 0) {
+    const int32_t n4 = Lmax / 4;
+#pragma unroll 4
+    for (int32_t b = 0; b < B; ++b) {
+      const f32x4* row = (const f32x4*)(dbias + ((size_t)b * H + h) * Lmax);
+      for (int32_t j = tid; j < n4; j += kBiasGradThreads) {
+        const f32x4 x = row[j];
+        acc += (x[0] + x[1]) + (x[2] + x[3]);
+      }
+    }
+  } else {
+    for (int32_t b = 0; b < B; ++b) {
+      const float* row = dbias + ((size_t)b * H + h) * Lmax;
+      for (int32_t j = tid; j < Lmax; j += kBiasGradThreads) acc += row[j];
+    }
+  }
+  part[tid] = acc;
+  __syncthreads();
+#pragma unroll
+  for (int s = kBiasGradThreads / 2; s > 0; s >>= 1) {
+    if (tid < s) part[tid] += part[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0) db[h] = part[0];
 }
 
 template <int D, bool SPLIT>
@@ -838,7 +889,7 @@ hipError_t launch_softmax_dkdv_t(const Launch& L, const void* q, const void* k, 
                                  const float* lse, const float* delta, void* dk, void* dv, hipStream_t st) {
   hipLaunchKernelGGL((dkdv_kernel<D, SPLIT, true>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dk, (uint16_t*)dv, lse,
-                     delta, L.sched);
+                     delta, (float*)nullptr, L.sched);
   return hipGetLastError();
 }
 
@@ -870,12 +921,18 @@ hipError_t launch_bwd_dq(int d, bool split, const Launch& L, const void* q, cons
 }
 
 hipError_t launch_bwd_dkdv(int d, bool split, const Launch& L, const void* q, const void* k, const void* v,
-                           const void* g, void* dk, void* dv, hipStream_t st) {
+                           const void* g, void* dk, void* dv, float* dbias, hipStream_t st) {
   if (d == 64)
-    return split ? launch_dkdv_t<64, true>(L, q, k, v, g, dk, dv, st)
-                 : launch_dkdv_t<64, false>(L, q, k, v, g, dk, dv, st);
-  return split ? launch_dkdv_t<128, true>(L, q, k, v, g, dk, dv, st)
-               : launch_dkdv_t<128, false>(L, q, k, v, g, dk, dv, st);
+    return split ? launch_dkdv_t<64, true>(L, q, k, v, g, dk, dv, dbias, st)
+                 : launch_dkdv_t<64, false>(L, q, k, v, g, dk, dv, dbias, st);
+  return split ? launch_dkdv_t<128, true>(L, q, k, v, g, dk, dv, dbias, st)
+               : launch_dkdv_t<128, false>(L, q, k, v, g, dk, dv, dbias, st);
+}
+
+hipError_t launch_bias_grad(int32_t B, int32_t H, int32_t Lmax, const float* dbias, float* db, hipStream_t st) {
+  hipLaunchKernelGGL(kern::bias_grad_kernel, dim3((unsigned)H), dim3(kern::kBiasGradThreads), 0, st, dbias, db, B,
+                     H, Lmax);
+  return hipGetLastError();
 }
 
 hipError_t launch_softmax_fwd(int d, bool split, const Launch& L, const void* q, const void* k, const void* v,

@@ -12,8 +12,11 @@ hipError_t launch_fwd(int d, bool split, const Launch& L, const void* q, const v
                       hipStream_t st);
 hipError_t launch_bwd_dq(int d, bool split, const Launch& L, const void* q, const void* k, const void* v,
                          const void* g, void* dq, hipStream_t st);
+// dbias: null, or fp32 [B, H, Lmax] per-key sums of dX (the bias gradient).
 hipError_t launch_bwd_dkdv(int d, bool split, const Launch& L, const void* q, const void* k, const void* v,
-                           const void* g, void* dk, void* dv, hipStream_t st);
+                           const void* g, void* dk, void* dv, float* dbias, hipStream_t st);
+// db[h] = sum over b, j of dbias[b, h, j].
+hipError_t launch_bias_grad(int32_t B, int32_t H, int32_t Lmax, const float* dbias, float* db, hipStream_t st);
 
 // Softmax attention (comparison path): lse2 and delta are fp32 [B, H, Lmax].
 hipError_t launch_softmax_fwd(int d, bool split, const Launch& L, const void* q, const void* k, const void* v,

@@ -69,6 +69,7 @@ double bias_value(int32_t n, int32_t mode, float arg) {
   // Summary §2A: b = -log(n).  Mode 0 reads n as the sequence's valid length.
   if (mode == 0) return -std::log((double)n);
   if (mode == 1) return -std::log((double)arg);
+  if (mode == 3) return 0.0;  // per-head values: the kernels read them from device memory
   return (double)arg;
 }
 

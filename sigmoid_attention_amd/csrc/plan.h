@@ -55,6 +55,7 @@ struct Sched {
   int32_t zero_nseq;             // sequences zero-filled by this launch (0: none)
   int32_t zero_n[kZeroSeqs];     // their valid lengths
   int32_t causal;                // causal mask (see PlanInput)
+  const float* head_bias;        // device: one bias per head (replaces c2), or null
   // Element strides (sequence, head, row) of each tensor argument of the
   // launch, in argument order; the head dimension is contiguous.
   int64_t sb[6];

@@ -44,29 +44,35 @@ def _usable(t: torch.Tensor, layout: str) -> torch.Tensor:
 
 class _SigmoidAttention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, lens, layout, bias_mode, bias_arg, precision, causal):
-        o = _binding.fwd(q, k, v, lens, bias_mode=bias_mode, bias_arg=bias_arg, precision=precision,
+    def forward(ctx, q, k, v, head_bias, lens, layout, bias_mode, bias_arg, precision, causal):
+        arg = head_bias if head_bias is not None else bias_arg
+        o = _binding.fwd(q, k, v, lens, bias_mode=bias_mode, bias_arg=arg, precision=precision,
                          layout=layout, causal=causal)
-        ctx.save_for_backward(q, k, v)
+        ctx.save_for_backward(q, k, v, head_bias)
         ctx.cfg = (lens, layout, bias_mode, bias_arg, precision, causal)
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v = ctx.saved_tensors
+        q, k, v, head_bias = ctx.saved_tensors
         lens, layout, bias_mode, bias_arg, precision, causal = ctx.cfg
         do = _usable(do, layout)
-        kw = dict(bias_mode=bias_mode, bias_arg=bias_arg, precision=precision, layout=layout, causal=causal)
-        dq = dk = dv = None
+        arg = head_bias if head_bias is not None else bias_arg
+        kw = dict(bias_mode=bias_mode, bias_arg=arg, precision=precision, layout=layout, causal=causal)
+        dq = dk = dv = db = None
+        want_db = head_bias is not None and ctx.needs_input_grad[3]
         if ctx.needs_input_grad[0]:
             dq = _binding.bwd_dq(q, k, v, do, lens, **kw)
-        if ctx.needs_input_grad[1] or ctx.needs_input_grad[2]:
+        if want_db:
+            dk, dv, rows = _binding.bwd_dkdv_dbias(q, k, v, do, lens, **kw)
+            db = _binding.bias_grad(rows, lens)
+        elif ctx.needs_input_grad[1] or ctx.needs_input_grad[2]:
             dk, dv = _binding.bwd_dkdv(q, k, v, do, lens, **kw)
-        return dq, dk, dv, None, None, None, None, None, None
+        return dq, dk, dv, db, None, None, None, None, None, None
 
 
 def sigmoid_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens, layout: str = "bhld",
-                      bias_mode: str = "seqlen", bias_arg: float = 0.0, precision: str = "fast",
+                      bias_mode: str = "seqlen", bias_arg=0.0, precision: str = "fast",
                       causal: bool = False) -> torch.Tensor:
     """O = sigma(Q K^T / sqrt(d) + b) V per sequence and head, differentiable.
 
@@ -76,10 +82,15 @@ def sigmoid_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens
     or beyond a sequence's length are ignored on input and zero on output (and
     in the gradients).  bias_mode / bias_arg / precision as in
     sigmoid_attention_amd.fwd.  causal: query i sees keys 0..i only.
+    bias_mode "per_head": bias_arg is a float32 tensor of H values on the
+    device, b_h = bias_arg[h]; if it requires grad, its gradient (the sum of
+    dX over each head's valid (query, key) pairs) is computed by the kernels.
     """
     B = q.shape[0]
     lens = _host_lengths(seqlens, B)
-    return _SigmoidAttention.apply(q, k, v, lens, layout, bias_mode, bias_arg, precision, bool(causal))
+    if bias_mode == "per_head":
+        return _SigmoidAttention.apply(q, k, v, bias_arg, lens, layout, bias_mode, 0.0, precision, bool(causal))
+    return _SigmoidAttention.apply(q, k, v, None, lens, layout, bias_mode, bias_arg, precision, bool(causal))
 
 
 class _SoftmaxAttention(torch.autograd.Function):
@@ -130,15 +141,24 @@ class SigmoidAttention(torch.nn.Module):
     valid lengths or a right-padding mask (True = pad); with neither, every
     row is valid.  Tensors are in `layout` order ([B, Lmax, H, d] by default,
     the usual layout after a projection and a view).
+
+    bias_mode "per_head" makes the bias a trained parameter, one value per
+    head (`heads` of them, initialised to `bias_arg`, e.g. -ln of a typical
+    length); its gradient comes from the kernels.
     """
 
     def __init__(self, layout: str = "blhd", bias_mode: str = "seqlen", bias_arg: float = 0.0,
-                 precision: str = "fast", causal: bool = False):
+                 precision: str = "fast", causal: bool = False, heads: Optional[int] = None):
         super().__init__()
         if layout not in _binding.LAYOUTS:
             raise ValueError(f"layout must be one of {sorted(_binding.LAYOUTS)}")
         self.layout, self.bias_mode, self.bias_arg, self.precision = layout, bias_mode, bias_arg, precision
         self.causal = bool(causal)
+        self.head_bias = None
+        if bias_mode == "per_head":
+            if not heads or heads < 1:
+                raise ValueError("bias_mode per_head needs heads >= 1")
+            self.head_bias = torch.nn.Parameter(torch.full((heads,), float(bias_arg), dtype=torch.float32))
 
     def forward(self, q, k, v, seqlens: Optional[Sequence[int]] = None,
                 key_padding_mask: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -148,8 +168,8 @@ class SigmoidAttention(torch.nn.Module):
             else:
                 L = q.shape[_binding.LAYOUTS[self.layout][2]]
                 seqlens = [L] * q.shape[0]
-        return sigmoid_attention(q, k, v, seqlens, self.layout, self.bias_mode, self.bias_arg, self.precision,
-                                 self.causal)
+        arg = self.head_bias if self.head_bias is not None else self.bias_arg
+        return sigmoid_attention(q, k, v, seqlens, self.layout, self.bias_mode, arg, self.precision, self.causal)
 
     def extra_repr(self) -> str:
         return (f"layout={self.layout}, bias_mode={self.bias_mode}, precision={self.precision}, "

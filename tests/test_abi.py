@@ -135,7 +135,7 @@ def test_inputs_may_alias_each_other_but_output_checks_still_run():
     assert fwd(a, q=P[0], k=P[0], v=P[0], o=P[0]) == ALIAS
 
 
-@pytest.mark.parametrize("mode,arg", [(3, 0.0), (-1, 0.0), (1, 0.0), (1, -5.0), (1, float("nan")),
+@pytest.mark.parametrize("mode,arg", [(4, 0.0), (-1, 0.0), (1, 0.0), (1, -5.0), (1, float("nan")),
                                       (2, float("inf")), (2, float("nan"))])
 def test_bad_bias(mode, arg):
     a, keep = args(bias_mode=mode, bias_arg=arg)
@@ -232,3 +232,60 @@ def test_bad_mask_mode():
     a.mask = 2
     for f in (fwd, dq, dkdv):
         assert f(a) == 11
+
+
+def validate(a, pass_, ptrs):
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    return sa.load().sigattn_validate(ctypes.byref(a), pass_, arr)
+
+
+def test_per_head_bias_checks():
+    """Bias mode 3 reads H fp32 values from device memory: the pointer must be
+    set and 4-byte aligned, and may overlap inputs but no output."""
+    hb = P[6]
+    a, keep = args(bias_mode=3, head_bias=hb)
+    assert validate(a, 0, P[:4]) == OK
+    assert validate(a, 2, P[:6]) == OK
+    a0, keep0 = args(bias_mode=3)  # no head_bias pointer
+    for f in (fwd, dq, dkdv):
+        assert f(a0) == NULL
+    a2, keep2 = args(bias_mode=3, head_bias=hb + 2)
+    for f in (fwd, dq, dkdv):
+        assert f(a2) == ALIGN
+    a4, keep4 = args(bias_mode=3, head_bias=hb + 4)  # 4-byte alignment suffices
+    assert validate(a4, 1, P[:5]) == OK
+    a5, keep5 = args(bias_mode=3, head_bias=P[0] + 64)  # inside the q input: allowed
+    assert validate(a5, 0, P[:4]) == OK
+    a6, keep6 = args(bias_mode=3, head_bias=P[3] + 64)  # inside the o output
+    assert validate(a6, 0, P[:4]) == ALIAS
+    assert fwd(a6) == ALIAS
+    a7, keep7 = args(bias_mode=3, head_bias=P[5] + 64)  # inside dv
+    assert dkdv(a7) == ALIAS
+
+
+def dkdv_db(a, db, q=P[0], k=P[1], v=P[2], g=P[3], dk=P[4], dv=P[5]):
+    return sa.load().sigattn_bwd_dkdv_dbias(ctypes.byref(a), q, k, v, g, dk, dv, db)
+
+
+def test_dbias_rows_checks():
+    a, keep = args()
+    assert dkdv_db(a, None) == NULL
+    assert dkdv_db(a, P[6] + 8) == ALIGN
+    assert dkdv_db(a, P[4] + 64) == ALIAS   # inside dk
+    assert dkdv_db(a, P[0] + 64) == ALIAS   # inside q (an output may overlap nothing)
+    ab, keepb = args(lens=(129, 77))
+    assert dkdv_db(ab, P[6]) == SEQLEN
+    a3, keep3 = args(bias_mode=3, head_bias=P[6] + 256)  # bias values inside the dbias rows
+    assert dkdv_db(a3, P[6]) == ALIAS
+
+
+def test_bias_grad_checks():
+    lib = sa.load()
+    a, keep = args()
+    assert lib.sigattn_bias_grad(ctypes.byref(a), None, P[7]) == NULL
+    assert lib.sigattn_bias_grad(ctypes.byref(a), P[6], None) == NULL
+    assert lib.sigattn_bias_grad(ctypes.byref(a), P[6] + 4, P[7]) == ALIGN
+    assert lib.sigattn_bias_grad(ctypes.byref(a), P[6], P[7] + 2) == ALIGN
+    assert lib.sigattn_bias_grad(ctypes.byref(a), P[6], P[6] + 4 * 2 * 2 * 128 - 4) == ALIAS
+    ab, keepb = args(lens=(5, -1))
+    assert lib.sigattn_bias_grad(ctypes.byref(ab), P[6], P[7]) == SEQLEN
