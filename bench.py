@@ -2,6 +2,8 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--precision fast|split|auto]
                     [--sweep] [--no-cpu-baseline] [--cpu-seconds S] [--causal]
+                    [--bias seqlen|per_head] [--dtype bf16|fp16] [--layout bhld|blhd]
+                    [--attn sigmoid|softmax] [--compare-softmax] [--layer]
 
 A step is one pass of the whole path over one batch already resident in HBM:
 sigattn_fwd, then sigattn_bwd_dq, then sigattn_bwd_dkdv (one launch each).
@@ -77,7 +79,7 @@ def load_traffic(kernel: str, workload: str, precision: str):
 
 
 def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="sigmoid", causal=False,
-                  bias="seqlen"):
+                  bias="seqlen", dtype="bf16"):
     """Time `steps` passes of forward + backward (HIP events around every
     call, on the launch stream).  attn="softmax" times the softmax comparison
     path on the same inputs and schedule: forward, the delta pass, dQ, dK/dV.
@@ -88,7 +90,7 @@ def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="s
     import sigmoid_attention_amd as sa
     import workloads
 
-    case = workloads.make(name, seed=seed)
+    case = workloads.make(name, seed=seed, dtype=torch.float16 if dtype == "fp16" else torch.bfloat16)
     w = case["workload"]
     n = case["seqlens"]
     dev = torch.device("cuda:0")
@@ -300,6 +302,8 @@ def main():
                     help="causal mask (query i sees keys 0..i); FLOPs count the n(n+1)/2 visible pairs")
     ap.add_argument("--bias", default="seqlen", choices=["seqlen", "per_head"],
                     help="per_head: a learnable per-head bias, with its gradient computed in the backward")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
+                    help="element type of the tensors (fp16: the fp16 build of the kernels)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -353,7 +357,7 @@ def main():
     w = workloads.WORKLOADS[name]
     precision = a.precision if a.precision != "auto" else ("split" if w.scale_qkv > 1.0 else "fast")
     r = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn=a.attn, causal=a.causal,
-                      bias=a.bias)
+                      bias=a.bias, dtype=a.dtype)
     n = r["seqlens"]
     total = r["fwd_flops"] + r["bwd_flops"]
     value = tflops(total, r["step_ms"])
@@ -393,7 +397,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": a.dtype,
         "data": "synthetic",
         "config": {
             "workload": name, "B": w.B, "H": w.H, "d": w.d, "Lmax": w.Lmax, "seqlens": [int(x) for x in n],

@@ -30,7 +30,7 @@
  * zero; a sequence with n_b = 0 produces all-zero outputs.
  *
  * Tensors.  Q, K, V, dO, O, dQ, dK, dV are device pointers to bf16 arrays
- * seen as [B, H, Lmax, d], 16-byte aligned.  By default each is contiguous
+ * (or fp16, args->dtype) seen as [B, H, Lmax, d], 16-byte aligned.  By default each is contiguous
  * (row-major: d fastest); with args->strides each tensor argument may be any
  * strided view whose head dimension is contiguous (for example [B, Lmax, H, d]
  * activations, or the q/k/v slices of a fused QKV projection), so a caller
@@ -76,7 +76,8 @@ typedef enum sigattn_status {
                                 row stride is below d or too large for 32-bit offsets
                                 ((Lmax + 256) * l * 2 > 2^31 - 1), or an output view
                                 maps two elements to one address                        */
-  SIGATTN_ERR_MASK = 11      /* unknown mask mode                                       */
+  SIGATTN_ERR_MASK = 11,     /* unknown mask mode                                       */
+  SIGATTN_ERR_DTYPE = 12     /* unknown element type                                    */
 } sigattn_status;
 
 /* Which keys a query sees. */
@@ -87,6 +88,14 @@ typedef enum sigattn_mask {
                               Practices for Sigmoid Self-Attention", abstract); tiles
                               above the diagonal are skipped like padded ones        */
 } sigattn_mask;
+
+/* Element type of every tensor argument of a call (all tensors share it). */
+typedef enum sigattn_dtype {
+  SIGATTN_DTYPE_BF16 = 0,  /* bfloat16 (the pages' precision)                          */
+  SIGATTN_DTYPE_F16 = 1    /* IEEE binary16: the products use the fp16 MFMA; P and dX
+                              are rounded to fp16 (11 significant bits against bf16's
+                              8); outputs are fp16, so |values| must stay below 65504 */
+} sigattn_dtype;
 
 /* The bias b_b of the SigmoidAttn formula (summary §2A, b = -log(n)). */
 typedef enum sigattn_bias_mode {
@@ -100,12 +109,14 @@ typedef enum sigattn_bias_mode {
                                       sigattn_bwd_dkdv_dbias)                       */
 } sigattn_bias_mode;
 
-/* How P (forward, dV) and dX (dQ, dK) enter the second bf16 matrix product. */
+/* How P (forward, dV) and dX (dQ, dK) enter the second matrix product (in
+ * the tensors' element type, written e16 below: bf16 or fp16). */
 typedef enum sigattn_precision {
-  SIGATTN_PREC_FAST = 0,  /* rounded once to bf16 (round-to-nearest-even)          */
-  SIGATTN_PREC_SPLIT = 1  /* as a pair hi = bf16(x), lo = bf16(x - hi): two products,
-                             ~16 significant bits; needed when scores saturate
-                             the sigmoid (|x| >> 10) and many small weights sum   */
+  SIGATTN_PREC_FAST = 0,  /* rounded once to e16 (round-to-nearest-even)           */
+  SIGATTN_PREC_SPLIT = 1  /* as a pair hi = e16(x), lo = e16(x - hi): two products,
+                             ~16 (bf16) or ~22 (fp16) significant bits; needed with
+                             bf16 when scores saturate the sigmoid (|x| >> 10) and
+                             many small weights sum                               */
 } sigattn_precision;
 
 /* Which pass sigattn_plan_stats describes. */
@@ -148,6 +159,7 @@ typedef struct sigattn_args {
                                read by the kernels in bias mode 3 (the values must
                                be finite; they are not checked); ignored in the
                                other modes                                          */
+  int32_t dtype;            /* sigattn_dtype of the tensors; 0 = bf16               */
 } sigattn_args;
 
 /* Forward: O = sigma(Q K^T / sqrt(d) + b) V on valid rows; padded rows of O = 0.

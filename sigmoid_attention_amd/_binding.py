@@ -18,12 +18,14 @@ _lib = None
 
 BIAS_MODES = {"seqlen": 0, "fixed_n": 1, "const": 2, "per_head": 3}
 PRECISIONS = {"fast": 0, "split": 1}
+DTYPES = {"bf16": 0, "fp16": 1}
 PASSES = {"fwd": 0, "bwd_dq": 1, "bwd_dkdv": 2}
 
 STATUS_NAMES = {
     0: "SIGATTN_OK", 1: "SIGATTN_ERR_NULL", 2: "SIGATTN_ERR_SHAPE", 3: "SIGATTN_ERR_SEQLEN",
     4: "SIGATTN_ERR_ALIGN", 5: "SIGATTN_ERR_ALIAS", 6: "SIGATTN_ERR_BIAS", 7: "SIGATTN_ERR_PRECISION",
     8: "SIGATTN_ERR_HIP", 9: "SIGATTN_ERR_PASS", 10: "SIGATTN_ERR_STRIDE", 11: "SIGATTN_ERR_MASK",
+    12: "SIGATTN_ERR_DTYPE",
 }
 
 # Index order of a 4-d tensor for each supported layout, as (b, h, l, d) positions.
@@ -49,6 +51,7 @@ class SigattnArgs(ctypes.Structure):
         ("strides", ctypes.POINTER(SigattnStrides)),
         ("mask", ctypes.c_int32),
         ("head_bias", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
     ]
 
 
@@ -106,11 +109,12 @@ def status_str(code: int) -> str:
 
 
 def make_args(B, H, Lmax, d, seqlens, bias_mode="seqlen", bias_arg=0.0, precision="fast", stream=0,
-              strides=None, causal=False, head_bias=None):
+              strides=None, causal=False, head_bias=None, dtype="bf16"):
     """Build a sigattn_args struct.  `strides`: None (every tensor contiguous
     [B, H, Lmax, d]) or one (b, h, l) element-stride triple per tensor
     argument, in argument order.  `head_bias`: device address of H fp32
-    values (bias mode "per_head").  Returns (args, keepalive) — keep the
+    values (bias mode "per_head").  `dtype`: "bf16" or "fp16", the element
+    type of every tensor of the call.  Returns (args, keepalive) — keep the
     second object alive for as long as the struct is used (it owns the
     lengths and strides)."""
     lens = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
@@ -123,6 +127,7 @@ def make_args(B, H, Lmax, d, seqlens, bias_mode="seqlen", bias_arg=0.0, precisio
     a.stream = int(stream) if stream else None
     a.mask = int(causal) if not isinstance(causal, bool) else (1 if causal else 0)
     a.head_bias = int(head_bias) if head_bias else None
+    a.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     st = None
     if strides is not None:
         st = (SigattnStrides * len(strides))(*[SigattnStrides(int(b), int(h), int(l)) for b, h, l in strides])
@@ -155,8 +160,8 @@ def _tensor_args(ts, seqlens, bias_mode, bias_arg, precision, stream, layout="bh
     for t in ts:
         if not isinstance(t, torch.Tensor):
             raise TypeError("expected torch tensors")
-        if t.dtype != torch.bfloat16:
-            raise TypeError(f"expected bfloat16 tensors, got {t.dtype}")
+        if t.dtype not in (torch.bfloat16, torch.float16) or t.dtype != q.dtype:
+            raise TypeError(f"expected bfloat16 or float16 tensors of one type, got {t.dtype} and {q.dtype}")
         if not t.is_cuda:
             raise ValueError("tensors must live on the GPU")
         if t.dim() != 4:
@@ -179,7 +184,8 @@ def _tensor_args(ts, seqlens, bias_mode, bias_arg, precision, stream, layout="bh
                              "on the tensors' device")
         head_bias, bias_arg = hb.data_ptr(), 0.0
     return make_args(B, H, L, d, seqlens, bias_mode, bias_arg, precision, stream,
-                     None if contiguous else strides, causal, head_bias)
+                     None if contiguous else strides, causal, head_bias,
+                     "fp16" if q.dtype == torch.float16 else "bf16")
 
 
 def _new_like(t):

@@ -23,7 +23,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsigattn.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["kernels.hip"]
+# (source, extra flags): the kernels are compiled once per element type.
+HIP_SOURCES = [("kernels.hip", []), ("kernels.hip", ["-DSIGATTN_FP16"])]
 CXX_SOURCES = ["api.cpp", "plan.cpp"]
 
 
@@ -60,9 +61,9 @@ def build(verbose: bool = False) -> str:
     try:
         jobs = []
         objs = []
-        for src in HIP_SOURCES:
-            obj = os.path.join(tmp, src + ".o")
-            jobs.append([cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
+        for i, (src, flags) in enumerate(HIP_SOURCES):
+            obj = os.path.join(tmp, f"{src}.{i}.o")
+            jobs.append([cc, *COMMON, *DEVICE, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
         for src in CXX_SOURCES:
             obj = os.path.join(tmp, src + ".o")

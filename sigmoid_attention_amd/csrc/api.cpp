@@ -29,7 +29,10 @@ sigattn_status tile_rows(int32_t pass, int32_t* outer, int32_t* inner) {
   }
 }
 
-// Shape, lengths, bias and precision (no pointers).
+// Whether the call's tensors are fp16 (else bf16): picks the kernel build.
+bool f16(const sigattn_args* a) { return a->dtype == SIGATTN_DTYPE_F16; }
+
+// Shape, lengths, bias, precision, mask and element type (no pointers).
 constexpr int64_t kLmaxSlack = 256;  // rows a tile may reach past Lmax, with margin
 
 sigattn_status check_args(const sigattn_args* a) {
@@ -61,6 +64,7 @@ sigattn_status check_args(const sigattn_args* a) {
   }
   if (a->precision != SIGATTN_PREC_FAST && a->precision != SIGATTN_PREC_SPLIT) return SIGATTN_ERR_PRECISION;
   if (a->mask != SIGATTN_MASK_NONE && a->mask != SIGATTN_MASK_CAUSAL) return SIGATTN_ERR_MASK;
+  if (a->dtype != SIGATTN_DTYPE_BF16 && a->dtype != SIGATTN_DTYPE_F16) return SIGATTN_ERR_DTYPE;
   return SIGATTN_OK;
 }
 
@@ -267,7 +271,7 @@ sigattn_status sigattn_fwd(const sigattn_args* a, const void* q, const void* k, 
   const void* t[] = {q, k, v, o};
   if ((s = check_head_bias(a, t, 4, 3)) != SIGATTN_OK) return s;
   return run(a, SIGATTN_PASS_FWD, t, 4, [&](const Launch& L) {
-    return sigattn::launch_fwd(a->d, split, L, q, k, v, o, (hipStream_t)a->stream);
+    return (f16(a) ? sigattn::f16::launch_fwd : sigattn::bf16::launch_fwd)(a->d, split, L, q, k, v, o, (hipStream_t)a->stream);
   });
 }
 
@@ -282,7 +286,7 @@ sigattn_status sigattn_bwd_dq(const sigattn_args* a, const void* q, const void* 
   const void* t[] = {q, k, v, dout, dq};
   if ((s = check_head_bias(a, t, 5, 4)) != SIGATTN_OK) return s;
   return run(a, SIGATTN_PASS_BWD_DQ, t, 5, [&](const Launch& L) {
-    return sigattn::launch_bwd_dq(a->d, split, L, q, k, v, dout, dq, (hipStream_t)a->stream);
+    return (f16(a) ? sigattn::f16::launch_bwd_dq : sigattn::bf16::launch_bwd_dq)(a->d, split, L, q, k, v, dout, dq, (hipStream_t)a->stream);
   });
 }
 
@@ -297,7 +301,7 @@ sigattn_status sigattn_bwd_dkdv(const sigattn_args* a, const void* q, const void
   const void* t[] = {q, k, v, dout, dk, dv};
   if ((s = check_head_bias(a, t, 6, 4)) != SIGATTN_OK) return s;
   return run(a, SIGATTN_PASS_BWD_DKDV, t, 6, [&](const Launch& L) {
-    return sigattn::launch_bwd_dkdv(a->d, split, L, q, k, v, dout, dk, dv, nullptr, (hipStream_t)a->stream);
+    return (f16(a) ? sigattn::f16::launch_bwd_dkdv : sigattn::bf16::launch_bwd_dkdv)(a->d, split, L, q, k, v, dout, dk, dv, nullptr, (hipStream_t)a->stream);
   });
 }
 
@@ -314,7 +318,7 @@ sigattn_status sigattn_bwd_dkdv_dbias(const sigattn_args* a, const void* q, cons
   if ((s = check_head_bias(a, t, 6, 4, r, 1)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
   return run(a, SIGATTN_PASS_BWD_DKDV, t, 6, [&](const Launch& L) {
-    return sigattn::launch_bwd_dkdv(a->d, split, L, q, k, v, dout, dk, dv, dbias, (hipStream_t)a->stream);
+    return (f16(a) ? sigattn::f16::launch_bwd_dkdv : sigattn::bf16::launch_bwd_dkdv)(a->d, split, L, q, k, v, dout, dk, dv, dbias, (hipStream_t)a->stream);
   });
 }
 
@@ -327,7 +331,7 @@ sigattn_status sigattn_bias_grad(const sigattn_args* a, const float* dbias, floa
   const uintptr_t ol = (uintptr_t)db, oh = ol + 4 * (uintptr_t)a->H;
   if (ol < rh && rl < oh) return SIGATTN_ERR_ALIAS;
   (void)hipGetLastError();
-  if (sigattn::launch_bias_grad(a->B, a->H, a->Lmax, dbias, db, (hipStream_t)a->stream) != hipSuccess)
+  if (sigattn::bf16::launch_bias_grad(a->B, a->H, a->Lmax, dbias, db, (hipStream_t)a->stream) != hipSuccess)
     return SIGATTN_ERR_HIP;
   return SIGATTN_OK;
 }
@@ -357,7 +361,7 @@ sigattn_status sigattn_softmax_fwd(const sigattn_args* a, const void* q, const v
   if ((s = check_rows(a, t, 4, 3, r, 1, 0)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
   return run(a, SIGATTN_PASS_FWD, t, 4, [&](const Launch& L) {
-    return sigattn::launch_softmax_fwd(a->d, split, L, q, k, v, o, lse2, (hipStream_t)a->stream);
+    return (f16(a) ? sigattn::f16::launch_softmax_fwd : sigattn::bf16::launch_softmax_fwd)(a->d, split, L, q, k, v, o, lse2, (hipStream_t)a->stream);
   });
 }
 
@@ -387,7 +391,7 @@ sigattn_status sigattn_softmax_bwd_prep(const sigattn_args* a, const void* o, co
     A.b0 = b0;
     A.nb = std::min(a->B - b0, sigattn::kPrepSeqs);
     for (int32_t i = 0; i < A.nb; ++i) A.n[i] = a->seqlens[b0 + i];
-    if (sigattn::launch_softmax_prep(a->d, A, o, dout, delta, (hipStream_t)a->stream) != hipSuccess)
+    if ((f16(a) ? sigattn::f16::launch_softmax_prep : sigattn::bf16::launch_softmax_prep)(a->d, A, o, dout, delta, (hipStream_t)a->stream) != hipSuccess)
       return SIGATTN_ERR_HIP;
   }
   return SIGATTN_OK;
@@ -405,7 +409,7 @@ sigattn_status sigattn_softmax_bwd_dq(const sigattn_args* a, const void* q, cons
   if ((s = check_rows(a, t, 5, 4, r, 2, 2)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
   return run(a, SIGATTN_PASS_BWD_DQ, t, 5, [&](const Launch& L) {
-    return sigattn::launch_softmax_dq(a->d, split, L, q, k, v, dout, lse2, delta, dq, (hipStream_t)a->stream);
+    return (f16(a) ? sigattn::f16::launch_softmax_dq : sigattn::bf16::launch_softmax_dq)(a->d, split, L, q, k, v, dout, lse2, delta, dq, (hipStream_t)a->stream);
   });
 }
 
@@ -422,7 +426,7 @@ sigattn_status sigattn_softmax_bwd_dkdv(const sigattn_args* a, const void* q, co
   if ((s = check_rows(a, t, 6, 4, r, 2, 2)) != SIGATTN_OK) return s;
   const bool split = a->precision == SIGATTN_PREC_SPLIT;
   return run(a, SIGATTN_PASS_BWD_DKDV, t, 6, [&](const Launch& L) {
-    return sigattn::launch_softmax_dkdv(a->d, split, L, q, k, v, dout, lse2, delta, dk, dv,
+    return (f16(a) ? sigattn::f16::launch_softmax_dkdv : sigattn::bf16::launch_softmax_dkdv)(a->d, split, L, q, k, v, dout, lse2, delta, dk, dv,
                                         (hipStream_t)a->stream);
   });
 }
@@ -440,6 +444,7 @@ const char* sigattn_status_str(sigattn_status s) {
     case SIGATTN_ERR_HIP: return "HIP kernel launch failed";
     case SIGATTN_ERR_PASS: return "unknown pass";
     case SIGATTN_ERR_MASK: return "unknown mask mode";
+    case SIGATTN_ERR_DTYPE: return "unknown element type (bf16 or fp16)";
     case SIGATTN_ERR_STRIDE:
       return "bad strides: negative, not a multiple of 8, row stride below d or too large, or an output "
              "that maps two elements to one address";

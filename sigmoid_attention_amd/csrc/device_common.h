@@ -1,6 +1,11 @@
 // Device helpers shared by the sigmoid attention kernels (gfx950 / CDNA4).
 //
-// Matrix products use v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32
+// Element type.  The tensors hold 16-bit floats: bf16, or fp16 when the
+// kernels are compiled with SIGATTN_FP16.  The library compiles the kernels
+// once for each; every definition lives in the namespace sigattn::bf16 or
+// sigattn::f16 accordingly, so the two builds link side by side.
+//
+// Matrix products use v_mfma_f32_32x32x16_bf16 (or _f16; 16-bit inputs, fp32
 // accumulate).  Its register layout, per 64-lane wave, with l32 = lane % 32
 // and hf = lane / 32:
 //   A (32 x 16, M x K): lane holds row l32, K-slots 8*hf .. 8*hf+7
@@ -25,20 +30,35 @@
 
 #include "plan.h"
 
-namespace sigattn {
+#if defined(SIGATTN_FP16)
+#define SIGATTN_ELT f16
+#else
+#define SIGATTN_ELT bf16
+#endif
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+namespace sigattn {
+namespace SIGATTN_ELT {
+
+#if defined(SIGATTN_FP16)
+typedef _Float16 e16x8 __attribute__((ext_vector_type(8)));
+#else
+typedef __bf16 e16x8 __attribute__((ext_vector_type(8)));
+#endif
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+__device__ __forceinline__ f32x16 mfma(e16x8 a, e16x8 b, f32x16 c) {
+#if defined(SIGATTN_FP16)
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+#else
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+#endif
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+__device__ __forceinline__ e16x8 as_e16x8(u32x4 v) { return __builtin_bit_cast(e16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(e16x8 v) { return __builtin_bit_cast(u32x4, v); }
 
 // sigma(x) with x = s * score + b, in base 2: t = c1 * score + c2 where
 // c1 = -log2(e)/sqrt(d), c2 = -b*log2(e); sigma = 1/(1 + 2^t).  This is the
@@ -58,11 +78,12 @@ __device__ __forceinline__ float sigmoid2(float score, float c1, float c2) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(score, c1, c2)));
 }
 
-// Round 8 floats to bf16 (round-to-nearest-even, v_cvt_pk_bf16_f32).
-__device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
+// Round 8 floats to the element type (round-to-nearest-even,
+// v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
+__device__ __forceinline__ e16x8 to_e16x8(f32x8 x) { return __builtin_convertvector(x, e16x8); }
 
-// Widen bf16 back to float exactly (bits << 16).
-__device__ __forceinline__ f32x8 to_f32x8(bf16x8 x) { return __builtin_convertvector(x, f32x8); }
+// Widen back to float exactly.
+__device__ __forceinline__ f32x8 to_f32x8(e16x8 x) { return __builtin_convertvector(x, f32x8); }
 
 // The eight values of C register block `blk` that form K-chunk `half` (0/1).
 __device__ __forceinline__ f32x8 chunk8(const f32x16& c, int half) {
@@ -73,7 +94,7 @@ __device__ __forceinline__ f32x8 chunk8(const f32x16& c, int half) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile layout.  A tile holds ROWS rows of D bf16 values (keys or queries
+// LDS tile layout.  A tile holds ROWS rows of D 16-bit values (keys or queries
 // by d).  Row r keeps its D/8 16-byte groups in order up to an XOR of the
 // group index by X(r):
 //     slot(r, g) = r * D/8 + (g ^ X(r))        (16-byte slots)
@@ -102,7 +123,7 @@ __device__ __forceinline__ int tile_slot(int r, int g) {
   return r * (D / 8) + (g ^ tile_xor<D>(r));
 }
 
-// Range-checked view of one (sequence, head) slice: rows 0..n-1 of D bf16
+// Range-checked view of one (sequence, head) slice: rows 0..n-1 of D 16-bit
 // values, row r at element r * rs.  Loads go through a raw buffer resource
 // whose size is n * rs * 2 bytes, so a load at or beyond row n returns zeros
 // without touching memory: padded rows are zero-filled by the hardware, with
@@ -200,14 +221,16 @@ __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0); }
 // B-operand fragments of one row of a slice (this lane's row), K-slots along
 // d: 16s + 8hf .. +7.  Rows >= n read as zero.
 template <int D>
-__device__ __forceinline__ void load_bfrag(bf16x8 (&f)[D / 16], const Slice& src, int row, int hf) {
+__device__ __forceinline__ void load_bfrag(e16x8 (&f)[D / 16], const Slice& src, int row, int hf) {
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) f[s] = as_bf16x8(src.load16(row * src.rs + 16 * s + 8 * hf));
+  for (int s = 0; s < D / 16; ++s) f[s] = as_e16x8(src.load16(row * src.rs + 16 * s + 8 * hf));
 }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-// Transposing 8-byte LDS read (ds_read_b64_tr_b16).
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16): a move of 16-bit lanes,
+// the same for either element type (the bf16 form of the builtin is used and
+// the result reinterpreted).
 __device__ __forceinline__ bf16x4 lds_tr4(const uint16_t* p) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
@@ -238,10 +261,10 @@ struct TrFrag {
         off[db][h] = 8 * tile_slot<D>(row_lane + 8 * h, ch >> 1) + 4 * (ch & 1);
       }
   }
-  __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int db, int c) const {
+  __device__ __forceinline__ e16x8 read(const uint16_t* tile, int db, int c) const {
     const bf16x4 lo = lds_tr4(tile + 16 * c * D + off[db][0]);
     const bf16x4 hi = lds_tr4(tile + 16 * c * D + off[db][1]);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(e16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 };
 
@@ -255,8 +278,8 @@ struct FragAddr {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) off[s] = 8 * tile_slot<D>(l32, 2 * s + hf);
   }
-  __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int mb, int s) const {
-    return as_bf16x8(*(const u32x4*)(tile + 32 * mb * D + off[s]));
+  __device__ __forceinline__ e16x8 read(const uint16_t* tile, int mb, int s) const {
+    return as_e16x8(*(const u32x4*)(tile + 32 * mb * D + off[s]));
   }
 };
 
@@ -302,4 +325,5 @@ __device__ __forceinline__ bool find_item(const Sched& S, Item& it) {
   return decode_item(S, (int32_t)(blockIdx.x & 7), (int32_t)(blockIdx.x >> 3), it);
 }
 
+}  // namespace SIGATTN_ELT
 }  // namespace sigattn

@@ -32,6 +32,7 @@
 #include "plan.h"
 
 namespace sigattn {
+namespace SIGATTN_ELT {
 
 namespace kern {
 
@@ -50,19 +51,19 @@ template <int D> struct DkdvCfg { static constexpr int BQ = 64; static constexpr
 // sigma of the eight score values of K-chunk c, rounded to bf16 (hi) and, in
 // split precision, the bf16 remainder (lo).
 template <int D, bool SPLIT>
-__device__ __forceinline__ void sigmoid_chunk(const f32x16 (&sc)[2], int c, float c2, bf16x8& hi, bf16x8& lo) {
+__device__ __forceinline__ void sigmoid_chunk(const f32x16 (&sc)[2], int c, float c2, e16x8& hi, e16x8& lo) {
   f32x8 p = chunk8(sc[c >> 1], c & 1);
 #pragma unroll
   for (int t = 0; t < 8; ++t) p[t] = sigmoid2(p[t], score_c1<D>(), c2);
-  hi = to_bf16x8(p);
-  if (SPLIT) lo = to_bf16x8(p - to_f32x8(hi));
+  hi = to_e16x8(p);
+  if (SPLIT) lo = to_e16x8(p - to_f32x8(hi));
 }
 
 // dS = dP * sigma * (1 - sigma) for K-chunk c (and optionally sigma itself;
 // with DSUM, the chunk's eight fp32 dS values are also added to *dsum).
 template <int D, bool SPLIT, bool WANT_P, bool DSUM = false, int NB>
 __device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[NB], const f32x16 (&dp)[NB], int c, float c2,
-                                               bf16x8& dh, bf16x8& dl, bf16x8& ph, bf16x8& pl,
+                                               e16x8& dh, e16x8& dl, e16x8& ph, e16x8& pl,
                                                float* dsum = nullptr) {
   const f32x8 sv = chunk8(sc[c >> 1], c & 1), gv = chunk8(dp[c >> 1], c & 1);
   f32x8 p8, ds;
@@ -72,11 +73,11 @@ __device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[NB], const f32
     p8[t] = p;
     ds[t] = gv[t] * __builtin_fmaf(-p, p, p);  // dP * p (1 - p)
   }
-  dh = to_bf16x8(ds);
-  if (SPLIT) dl = to_bf16x8(ds - to_f32x8(dh));
+  dh = to_e16x8(ds);
+  if (SPLIT) dl = to_e16x8(ds - to_f32x8(dh));
   if (WANT_P) {
-    ph = to_bf16x8(p8);
-    if (SPLIT) pl = to_bf16x8(p8 - to_f32x8(ph));
+    ph = to_e16x8(p8);
+    if (SPLIT) pl = to_e16x8(p8 - to_f32x8(ph));
   }
   if constexpr (DSUM)  // pairwise: keeps the eight values' live ranges short
     *dsum += ((ds[0] + ds[1]) + (ds[2] + ds[3])) + ((ds[4] + ds[5]) + (ds[6] + ds[7]));
@@ -124,7 +125,7 @@ __device__ __forceinline__ constexpr float softmax_c1() {
 // delta per lane.
 template <int D, bool SPLIT, int NB>
 __device__ __forceinline__ void dsoftmax_chunk_col(const f32x16 (&sc)[NB], const f32x16 (&dp)[NB], int c, float lse2,
-                                                   float dlt, bf16x8& dh, bf16x8& dl) {
+                                                   float dlt, e16x8& dh, e16x8& dl) {
   const f32x8 sv = chunk8(sc[c >> 1], c & 1), gv = chunk8(dp[c >> 1], c & 1);
   f32x8 ds;
 #pragma unroll
@@ -132,8 +133,8 @@ __device__ __forceinline__ void dsoftmax_chunk_col(const f32x16 (&sc)[NB], const
     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t], softmax_c1<D>(), -lse2));
     ds[t] = p * (gv[t] - dlt);
   }
-  dh = to_bf16x8(ds);
-  if (SPLIT) dl = to_bf16x8(ds - to_f32x8(dh));
+  dh = to_e16x8(ds);
+  if (SPLIT) dl = to_e16x8(ds - to_f32x8(dh));
 }
 
 // P and dS for K-chunk c when queries are rows (dK/dV kernel): lse2 and delta
@@ -141,8 +142,8 @@ __device__ __forceinline__ void dsoftmax_chunk_col(const f32x16 (&sc)[NB], const
 // 16c + 8 + 4hf + {0..3}, in register order).
 template <int D, bool SPLIT, int NB>
 __device__ __forceinline__ void dsoftmax_chunk_row(const f32x16 (&sc)[NB], const f32x16 (&dp)[NB], int c,
-                                                   const f32x8& lse8, const f32x8& dlt8, bf16x8& dh, bf16x8& dl,
-                                                   bf16x8& ph, bf16x8& pl) {
+                                                   const f32x8& lse8, const f32x8& dlt8, e16x8& dh, e16x8& dl,
+                                                   e16x8& ph, e16x8& pl) {
   const f32x8 sv = chunk8(sc[c >> 1], c & 1), gv = chunk8(dp[c >> 1], c & 1);
   f32x8 p8, ds;
 #pragma unroll
@@ -151,10 +152,10 @@ __device__ __forceinline__ void dsoftmax_chunk_row(const f32x16 (&sc)[NB], const
     p8[t] = p;
     ds[t] = p * (gv[t] - dlt8[t]);
   }
-  dh = to_bf16x8(ds);
-  if (SPLIT) dl = to_bf16x8(ds - to_f32x8(dh));
-  ph = to_bf16x8(p8);
-  if (SPLIT) pl = to_bf16x8(p8 - to_f32x8(ph));
+  dh = to_e16x8(ds);
+  if (SPLIT) dl = to_e16x8(ds - to_f32x8(dh));
+  ph = to_e16x8(p8);
+  if (SPLIT) pl = to_e16x8(p8 - to_f32x8(ph));
 }
 
 // Store 4 consecutive fp32 values of an output row as bf16 (8 bytes).
@@ -165,7 +166,7 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x16& acc, int i, 
     v8[t] = scale * acc[4 * i + t];
     v8[4 + t] = 0.0f;
   }
-  const u32x4 packed = as_u32x4(to_bf16x8(v8));
+  const u32x4 packed = as_u32x4(to_e16x8(v8));
   *(uint2*)dst = (uint2){packed[0], packed[1]};
 }
 
@@ -173,7 +174,7 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x16& acc, int i, 
 // (this wave's 32 rows of the other operand).  Block mb covers tile rows
 // 32mb .. 32mb+31; K-steps s cover d = 16s .. 16s+15.
 template <int D, int NB>
-__device__ __forceinline__ void score_steps(f32x16 (&acc)[NB], const uint16_t* tile, const bf16x8 (&bf)[D / 16],
+__device__ __forceinline__ void score_steps(f32x16 (&acc)[NB], const uint16_t* tile, const e16x8 (&bf)[D / 16],
                                             int s0, int s1, const FragAddr<D>& fa) {
 #pragma unroll
   for (int s = s0; s < s1; ++s)
@@ -182,7 +183,7 @@ __device__ __forceinline__ void score_steps(f32x16 (&acc)[NB], const uint16_t* t
 }
 
 template <int D>
-__device__ __forceinline__ void score_block(f32x16& acc, const uint16_t* tile, const bf16x8 (&bf)[D / 16], int mb,
+__device__ __forceinline__ void score_block(f32x16& acc, const uint16_t* tile, const e16x8 (&bf)[D / 16], int mb,
                                             const FragAddr<D>& fa) {
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) acc = mfma(fa.read(tile, mb, s), bf[s], acc);
@@ -191,10 +192,10 @@ __device__ __forceinline__ void score_block(f32x16& acc, const uint16_t* tile, c
 // Second-product step for K-chunk c: acc[db] += A(tile rows d, K-chunk c) . B.
 template <int D, bool SPLIT>
 __device__ __forceinline__ void value_chunk(f32x16 (&acc)[D / 32], const TrFrag<D>& tr, const uint16_t* tile, int c,
-                                            const bf16x8& bh, const bf16x8& bl) {
+                                            const e16x8& bh, const e16x8& bl) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
-    const bf16x8 a = tr.read(tile, db, c);
+    const e16x8 a = tr.read(tile, db, c);
     acc[db] = mfma(a, bh, acc[db]);
     if (SPLIT) acc[db] = mfma(a, bl, acc[db]);
   }
@@ -202,8 +203,8 @@ __device__ __forceinline__ void value_chunk(f32x16 (&acc)[D / 32], const TrFrag<
 
 // The same, with the A fragments read beforehand (see read_value_frags).
 template <int D, bool SPLIT>
-__device__ __forceinline__ void value_chunk_pre(f32x16 (&acc)[D / 32], const bf16x8 (&a)[D / 32], const bf16x8& bh,
-                                                const bf16x8& bl) {
+__device__ __forceinline__ void value_chunk_pre(f32x16 (&acc)[D / 32], const e16x8 (&a)[D / 32], const e16x8& bh,
+                                                const e16x8& bl) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     acc[db] = mfma(a[db], bh, acc[db]);
@@ -212,7 +213,7 @@ __device__ __forceinline__ void value_chunk_pre(f32x16 (&acc)[D / 32], const bf1
 }
 
 template <int D>
-__device__ __forceinline__ void read_value_frags(bf16x8 (&a)[D / 32], const TrFrag<D>& tr, const uint16_t* tile,
+__device__ __forceinline__ void read_value_frags(e16x8 (&a)[D / 32], const TrFrag<D>& tr, const uint16_t* tile,
                                                  int c) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) a[db] = tr.read(tile, db, c);
@@ -226,9 +227,9 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // Score product over all K-steps with the A fragments of step s+1 read while
 // step s multiplies (one step of read-ahead).
 template <int D, int NB>
-__device__ __forceinline__ void score_pipelined(f32x16 (&acc)[NB], const uint16_t* tile, const bf16x8 (&bf)[D / 16],
+__device__ __forceinline__ void score_pipelined(f32x16 (&acc)[NB], const uint16_t* tile, const e16x8 (&bf)[D / 16],
                                                 const FragAddr<D>& fa) {
-  bf16x8 a0[NB], a1[NB];
+  e16x8 a0[NB], a1[NB];
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb) a0[mb] = fa.read(tile, mb, 0);
 #pragma unroll
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]);
 
   const int qrow = it.tile * BQ + 32 * w + l32;
-  bf16x8 qf[D / 16];
+  e16x8 qf[D / 16];
   load_bfrag<D>(qf, qs, qrow, hf);
   f32x16 acc[D / 32];
 #pragma unroll
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
     const uint16_t* Vc = Vb(P % 2);
     if (S.causal && j * BK + BK - 1 > q0w) mask_causal_cols(cur, j * BK, qrow, hf);
     zero2(nxt);
-    bf16x8 ph[4], pl[4];
+    e16x8 ph[4], pl[4];
     if (LA) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -407,16 +408,16 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
 // otherwise join the normalisation).  Epilogue: O / l and lse2 = m + log2 l.
 // ---------------------------------------------------------------------------
 template <int D, bool SPLIT>
-__device__ __forceinline__ void softmax_chunk(const f32x16 (&sc)[2], int c, float m, float& l, bf16x8& hi,
-                                              bf16x8& lo) {
+__device__ __forceinline__ void softmax_chunk(const f32x16 (&sc)[2], int c, float m, float& l, e16x8& hi,
+                                              e16x8& lo) {
   f32x8 p = chunk8(sc[c >> 1], c & 1);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[t], softmax_c1<D>(), -m));
     l += p[t];
   }
-  hi = to_bf16x8(p);
-  if (SPLIT) lo = to_bf16x8(p - to_f32x8(hi));
+  hi = to_e16x8(p);
+  if (SPLIT) lo = to_e16x8(p - to_f32x8(hi));
 }
 
 // Scores of keys >= nv (tile-relative) to -inf; lane half hf holds keys
@@ -455,7 +456,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd_softmax_kernel(
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]);
 
   const int qrow = it.tile * BQ + 32 * w + l32;
-  bf16x8 qf[D / 16];
+  e16x8 qf[D / 16];
   load_bfrag<D>(qf, qs, qrow, hf);
   f32x16 acc[D / 32];
 #pragma unroll
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd_softmax_kernel(
     for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
     l *= alpha;
     m = mn;
-    bf16x8 ph[4], pl[4];
+    e16x8 ph[4], pl[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       softmax_chunk<D, SPLIT>(cur, c, mn, l, ph[c], pl[c]);
@@ -557,7 +558,7 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]), gs(slice_base(dO, S, it.bh, 3), n, S.sl[3]);
 
   const int qrow = it.tile * BQ + 32 * w + l32;
-  bf16x8 qf[D / 16], gf[D / 16];
+  e16x8 qf[D / 16], gf[D / 16];
   load_bfrag<D>(qf, qs, qrow, hf);
   load_bfrag<D>(gf, gs, qrow, hf);
   f32x16 acc[D / 32];
@@ -597,7 +598,7 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
     zero2(dp);
     zero2(nxt);
     score_pipelined<D>(dp, Vc, gf, fa);
-    bf16x8 dh[4], dl[4], unused_h, unused_l;
+    e16x8 dh[4], dl[4], unused_h, unused_l;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), fa);  // MFMA: tile j+1
@@ -664,7 +665,7 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]), gs(slice_base(dO, S, it.bh, 3), n, S.sl[3]);
 
   const int krow = it.tile * BKV + 32 * w + l32;
-  bf16x8 kf[D / 16], vf[D / 16];
+  e16x8 kf[D / 16], vf[D / 16];
   load_bfrag<D>(kf, ks, krow, hf);
   load_bfrag<D>(vf, vs, krow, hf);
   f32x16 dk[D / 32], dv[D / 32];
@@ -718,12 +719,12 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     const uint16_t* Gt = Gb(kc);
     zero2(ns);
     zero2(nd);
-    bf16x8 dh[NC], dl[NC], ph[NC], pl[NC];
+    e16x8 dh[NC], dl[NC], ph[NC], pl[NC];
     {
       // Per chunk: issue the transposing reads of dO^T and Q^T, evaluate
       // P and dS on the VALU while they land, with the previous chunk's
       // dV and dK products interleaved into that VALU work.
-      bf16x8 ag[2][D / 32], aq[2][D / 32];
+      e16x8 ag[2][D / 32], aq[2][D / 32];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         read_value_frags<D>(ag[c & 1], tr, Gt, c);
@@ -792,8 +793,8 @@ __global__ __launch_bounds__(256) void softmax_prep_kernel(const uint16_t* __res
     const uint16_t* pg = dO + (size_t)b * A.sb[1] + (size_t)h * A.sh[1] + (size_t)i * A.sl[1];
 #pragma unroll
     for (int c = 0; c < D / 8; ++c) {
-      const f32x8 x = to_f32x8(as_bf16x8(*(const u32x4*)(po + 8 * c)));
-      const f32x8 y = to_f32x8(as_bf16x8(*(const u32x4*)(pg + 8 * c)));
+      const f32x8 x = to_f32x8(as_e16x8(*(const u32x4*)(po + 8 * c)));
+      const f32x8 y = to_f32x8(as_e16x8(*(const u32x4*)(pg + 8 * c)));
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc = __builtin_fmaf(x[t], y[t], acc);
     }
@@ -969,4 +970,5 @@ hipError_t launch_softmax_prep(int d, const PrepArgs& A, const void* o, const vo
                  : kern::launch_softmax_prep_t<128>(A, o, g, delta, st);
 }
 
+}  // namespace SIGATTN_ELT
 }  // namespace sigattn

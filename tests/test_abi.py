@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for code in range(11):
+    for code in range(13):
         s = sa.status_str(code)
         assert isinstance(s, str) and s
     assert sa.status_str(0) == "ok"
@@ -289,3 +289,17 @@ def test_bias_grad_checks():
     assert lib.sigattn_bias_grad(ctypes.byref(a), P[6], P[6] + 4 * 2 * 2 * 128 - 4) == ALIAS
     ab, keepb = args(lens=(5, -1))
     assert lib.sigattn_bias_grad(ctypes.byref(ab), P[6], P[7]) == SEQLEN
+
+
+@pytest.mark.parametrize("dtype", [2, -1, 7])
+def test_bad_dtype(dtype):
+    a, keep = args(dtype=dtype)
+    for f in (fwd, dq, dkdv):
+        assert f(a) == 12  # SIGATTN_ERR_DTYPE
+    assert validate(a, 0, P[:4]) == 12
+
+
+def test_fp16_dtype_validates():
+    a, keep = args(dtype="fp16")
+    assert validate(a, 0, P[:4]) == OK
+    assert validate(a, 2, P[:6]) == OK

@@ -104,8 +104,9 @@ def lengths(name: str, seed: int = 0) -> np.ndarray:
     return draw_lengths(w, g)
 
 
-def make(name: str, seed: int = 0, with_dout: bool = True) -> dict:
-    """Draw a workload.  Returns CPU tensors (bf16) and lengths (int32 numpy)."""
+def make(name: str, seed: int = 0, with_dout: bool = True, dtype=torch.bfloat16) -> dict:
+    """Draw a workload.  Returns CPU tensors (bf16, or `dtype`) and lengths
+    (int32 numpy)."""
     w = WORKLOADS[name]
     g = torch.Generator().manual_seed(seed)
     n = draw_lengths(w, g)
@@ -116,13 +117,14 @@ def make(name: str, seed: int = 0, with_dout: bool = True) -> dict:
         x = torch.randn(shape, generator=g, dtype=torch.float32)
         if t != "do" and w.scale_qkv != 1.0:
             x.mul_(w.scale_qkv)
-        out[t] = x.to(torch.bfloat16)
+        out[t] = x.to(dtype)
         del x
     return out
 
 
-def random_case(B, H, d, Lmax, seqlens, seed=0, scale_qkv=1.0) -> dict:
-    """Same recipe for an ad-hoc shape (parity edge cases)."""
+def random_case(B, H, d, Lmax, seqlens, seed=0, scale_qkv=1.0, dtype=torch.bfloat16) -> dict:
+    """Same recipe for an ad-hoc shape (parity edge cases); `dtype` is the
+    16-bit type the float32 draws are rounded to (bf16, or fp16)."""
     g = torch.Generator().manual_seed(seed)
     shape = (B, H, Lmax, d)
     out = {"seqlens": np.asarray(seqlens, dtype=np.int32)}
@@ -130,7 +132,7 @@ def random_case(B, H, d, Lmax, seqlens, seed=0, scale_qkv=1.0) -> dict:
         x = torch.randn(shape, generator=g, dtype=torch.float32)
         if t != "do" and scale_qkv != 1.0:
             x.mul_(scale_qkv)
-        out[t] = x.to(torch.bfloat16)
+        out[t] = x.to(dtype)
     return out
 
 
