@@ -3,13 +3,15 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--precision fast|split|auto]
                     [--sweep] [--no-cpu-baseline] [--cpu-seconds S] [--causal]
                     [--bias seqlen|per_head] [--dtype bf16|fp16] [--layout bhld|blhd]
-                    [--attn sigmoid|softmax] [--compare-softmax] [--layer]
+                    [--attn sigmoid|softmax] [--compare-softmax] [--layer] [--settle-ms MS]
 
 A step is one pass of the whole path over one batch already resident in HBM:
 sigattn_fwd, then sigattn_bwd_dq, then sigattn_bwd_dkdv (one launch each).
-W untimed steps, then exactly K timed steps bracketed by device syncs; HIP
-events recorded on the launch stream around every call give the per-kernel
-durations.  FLOPs are algorithmic and count valid (query, key) pairs only:
+Untimed steps for --settle-ms of wall time (default 500 ms: from cold the
+clocks need about a hundred steps to settle), then W untimed warm-up steps,
+then exactly K timed steps bracketed by device syncs; HIP events recorded on
+the launch stream around every call (created before the timed region) give
+the per-kernel durations and cost about 3 % of the step.  FLOPs are algorithmic and count valid (query, key) pairs only:
 forward 4 n^2 d and backward 10 n^2 d per (sequence, head) — the FlashAttention
 convention; recomputation inside the backward kernels is not counted.
 
@@ -78,8 +80,28 @@ def load_traffic(kernel: str, workload: str, precision: str):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
+SETTLE_MS = 500.0  # default GPU time of untimed steps before the warm-up steps
+
+
+def settle(step, ms):
+    """Run untimed steps for about `ms` milliseconds of wall time (synchronised
+    every few steps), so that clocks and caches reach the steady state of a
+    long training run before warm-up and timing: from cold, the first hundred
+    or so steps of the headline batch run up to 25 % slower.  Returns the
+    number of steps run."""
+    import torch
+
+    done, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step()
+        done += 8
+        torch.cuda.synchronize()
+    return done
+
+
 def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="sigmoid", causal=False,
-                  bias="seqlen", dtype="bf16"):
+                  bias="seqlen", dtype="bf16", settle_ms=SETTLE_MS):
     """Time `steps` passes of forward + backward (HIP events around every
     call, on the launch stream).  attn="softmax" times the softmax comparison
     path on the same inputs and schedule: forward, the delta pass, dQ, dK/dV.
@@ -146,10 +168,14 @@ def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="s
             sa.softmax_bwd_dkdv(q, k, v, do, lse2, delta, n, dk, dv, **kw)
             mark(4)
 
+    settled = settle(step, settle_ms)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    for ev in events:  # create the HIP events now: torch creates them at their first record
+        for e in ev:
+            e.record()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         step(events[i])
@@ -163,7 +189,7 @@ def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="s
     res = {
         "workload": w, "seqlens": n, "step_ms": step_ms, "host_step_ms": host_s * 1e3 / steps,
         "kernel_avg_ms": avg, "kernel_median_ms": med, "kernel_min_ms": {k_: float(np.min(v_)) for k_, v_ in per.items()},
-        "pair_flops": base,
+        "pair_flops": base, "settle_steps": settled,
         "fwd_flops": 4 * base, "bwd_flops": 10 * base,
         "outputs": tuple(t.permute(0, 2, 1, 3) if layout == "blhd" else t for t in (o, dq, dk, dv)),
         "case": case,
@@ -171,7 +197,7 @@ def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="s
     return res
 
 
-def time_layer(attn, steps, warmup, d_model=768, heads=12, mlp=3072, seed=0):
+def time_layer(attn, steps, warmup, d_model=768, heads=12, mlp=3072, seed=0, settle_ms=SETTLE_MS):
     """Forward + backward of one pre-norm bidirectional transformer layer of
     the 160M-parameter class (d_model 768, 12 heads of 64, MLP 3072, bf16,
     random weights) on the headline batch's lengths: LayerNorm, fused QKV
@@ -216,6 +242,7 @@ def time_layer(attn, steps, warmup, d_model=768, heads=12, mlp=3072, seed=0):
     def step():
         layer(x).backward(gy)
 
+    settle(step, settle_ms)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -304,6 +331,8 @@ def main():
                     help="per_head: a learnable per-head bias, with its gradient computed in the backward")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
                     help="element type of the tensors (fp16: the fp16 build of the kernels)")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="wall time of untimed steps run before the warm-up steps (clocks reach steady state)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -336,7 +365,7 @@ def main():
         return
 
     if a.layer:
-        ms = {k_: time_layer(k_, a.steps, a.warmup) for k_ in ("sigmoid", "softmax", "none")}
+        ms = {k_: time_layer(k_, a.steps, a.warmup, settle_ms=a.settle_ms) for k_ in ("sigmoid", "softmax", "none")}
         w = workloads.WORKLOADS[workloads.HEADLINE]
         n = workloads.lengths(workloads.HEADLINE)
         print(json.dumps({
@@ -357,7 +386,7 @@ def main():
     w = workloads.WORKLOADS[name]
     precision = a.precision if a.precision != "auto" else ("split" if w.scale_qkv > 1.0 else "fast")
     r = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn=a.attn, causal=a.causal,
-                      bias=a.bias, dtype=a.dtype)
+                      bias=a.bias, dtype=a.dtype, settle_ms=a.settle_ms)
     n = r["seqlens"]
     total = r["fwd_flops"] + r["bwd_flops"]
     value = tflops(total, r["step_ms"])
@@ -414,6 +443,7 @@ def main():
         "fwd_pct_bf16_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
         "bwd_pct_bf16_peak": round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2),
         "host_ms_per_step": round(r["host_step_ms"], 5),
+        "settle": {"ms": a.settle_ms, "steps": r["settle_steps"]},
         "roofline": roofline,
     }
 
@@ -421,7 +451,7 @@ def main():
         sweep = {}
         base_ms = None
         for sw in ("sweep_b16h16d64_l4096_pad00", "sweep_b16h16d64_l4096_pad25", "sweep_b16h16d64_l4096_pad50"):
-            rs = time_workload(sw, "fast", max(5, a.steps // 2), 2, attn=a.attn)
+            rs = time_workload(sw, "fast", max(5, a.steps // 2), 2, attn=a.attn, settle_ms=a.settle_ms / 2)
             ws = rs["workload"]
             fwd_ms = rs["kernel_avg_ms"]["fwd"]
             step_ms = rs["step_ms"]
@@ -429,7 +459,7 @@ def main():
                 base_ms = (fwd_ms, step_ms)
             dense_pairs = covered_pairs([ws.Lmax] * ws.B, ws.H, 128, 64)
             if a.compare_softmax:
-                rc = time_workload(sw, "fast", max(5, a.steps // 2), 2, attn="softmax")
+                rc = time_workload(sw, "fast", max(5, a.steps // 2), 2, attn="softmax", settle_ms=a.settle_ms / 2)
                 cmp_ = {"softmax_fwd_tflops": round(tflops(rc["fwd_flops"], rc["kernel_avg_ms"]["fwd"]), 2),
                         "softmax_fwd_bwd_tflops": round(tflops(rc["fwd_flops"] + rc["bwd_flops"], rc["step_ms"]), 2),
                         "sigmoid_fwd_speedup": round(rc["kernel_avg_ms"]["fwd"] / fwd_ms, 4),
@@ -453,7 +483,8 @@ def main():
         out["padding_sweep"] = sweep
 
     if a.compare_softmax and a.attn == "sigmoid":
-        rc = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn="softmax", causal=a.causal)
+        rc = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn="softmax", causal=a.causal,
+                           settle_ms=a.settle_ms)
         out["softmax_comparison"] = {
             "value": round(tflops(total, rc["step_ms"]), 2),
             "fwd_tflops": round(tflops(rc["fwd_flops"], rc["kernel_avg_ms"]["fwd"]), 2),
