@@ -3,10 +3,11 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--precision fast|split|auto]
                     [--sweep] [--no-cpu-baseline] [--cpu-seconds S] [--causal]
                     [--bias seqlen|per_head] [--dtype bf16|fp16] [--layout bhld|blhd]
-                    [--attn sigmoid|softmax] [--compare-softmax] [--layer] [--settle-ms MS]
+                    [--attn sigmoid|softmax] [--compare-softmax] [--layer] [--settle-ms MS] [--split-bwd]
 
 A step is one pass of the whole path over one batch already resident in HBM:
-sigattn_fwd, then sigattn_bwd_dq, then sigattn_bwd_dkdv (one launch each).
+sigattn_fwd, then sigattn_bwd (the dQ and dK/dV work in one fused launch;
+with --split-bwd, sigattn_bwd_dq then sigattn_bwd_dkdv, one launch each).
 Untimed steps for --settle-ms of wall time (default 500 ms: from cold the
 clocks need about a hundred steps to settle), then W untimed warm-up steps,
 then exactly K timed steps bracketed by device syncs; HIP events recorded on
@@ -44,7 +45,12 @@ KERNEL_SOURCE = os.path.join(ROOT, "sigmoid_attention_amd", "csrc", "kernels.hip
 # Algorithmic FLOP per valid (query, key) pair and head dim, per kernel:
 # forward: S = QK^T and PV (4); dK/dV kernel: S, dP, dV, dK (8); dQ kernel: dQ (2)
 # (its S and dP recompute what the dK/dV kernel already counts).  Sum: 14 = 4 + 10.
-KERNEL_FLOP_UNITS = {"fwd": 4, "bwd_dq": 2, "bwd_dkdv": 8}
+KERNEL_FLOP_UNITS = {"fwd": 4, "bwd": 10, "bwd_dq": 2, "bwd_dkdv": 8}
+# "bwd" is the fused backward launch (the dK/dV and dQ work of sigattn_bwd).
+# MFMA work the kernels actually issue, same units, (fast, split precision):
+# the backward recomputes S and dP on the dQ side, and split precision doubles
+# the products that take P or dX.
+EXECUTED_UNITS = {"fwd": (4, 6), "bwd": (14, 20), "bwd_dq": (6, 8), "bwd_dkdv": (8, 12)}
 # The softmax comparison path adds a memory pass (delta = rowsum(dO * O)) that
 # counts no FLOPs; its other kernels follow the same convention.
 
@@ -101,7 +107,7 @@ def settle(step, ms):
 
 
 def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="sigmoid", causal=False,
-                  bias="seqlen", dtype="bf16", settle_ms=SETTLE_MS):
+                  bias="seqlen", dtype="bf16", settle_ms=SETTLE_MS, split_bwd=False):
     """Time `steps` passes of forward + backward (HIP events around every
     call, on the launch stream).  attn="softmax" times the softmax comparison
     path on the same inputs and schedule: forward, the delta pass, dQ, dK/dV.
@@ -136,37 +142,49 @@ def time_workload(name, precision, steps, warmup, seed=0, layout="bhld", attn="s
         (B, H, L, _), _ = sa._binding.layout_strides(q, layout)
         lse2 = torch.empty((B, H, L), dtype=torch.float32, device=dev)
         delta = torch.empty_like(lse2)
-    names = ("fwd", "bwd_dq", "bwd_dkdv") if attn == "sigmoid" else ("fwd", "bwd_prep", "bwd_dq", "bwd_dkdv")
+    bwd_names = ("bwd_dq", "bwd_dkdv") if split_bwd else ("bwd",)
+    names = ("fwd",) + (("bwd_prep",) if attn == "softmax" else ()) + bwd_names
     if rows is not None:
         names += ("bwd_bias_grad",)
 
     def step(ev=None):
-        def mark(i):
+        m = iter(range(len(names) + 1))
+
+        def mark():
+            i = next(m)
             if ev is not None:
                 ev[i].record()
-        mark(0)
+        mark()
         if attn == "sigmoid":
             sa.fwd(q, k, v, n, o=o, **kw)
-            mark(1)
-            sa.bwd_dq(q, k, v, do, n, dq=dq, **kw)
-            mark(2)
-            if rows is None:
-                sa.bwd_dkdv(q, k, v, do, n, dk=dk, dv=dv, **kw)
-                mark(3)
+            mark()
+            if not split_bwd:
+                sa.bwd(q, k, v, do, n, dq=dq, dk=dk, dv=dv, dbias=rows, **kw)
+                mark()
             else:
-                sa.bwd_dkdv_dbias(q, k, v, do, n, dk=dk, dv=dv, dbias=rows, **kw)
-                mark(3)
+                sa.bwd_dq(q, k, v, do, n, dq=dq, **kw)
+                mark()
+                if rows is None:
+                    sa.bwd_dkdv(q, k, v, do, n, dk=dk, dv=dv, **kw)
+                else:
+                    sa.bwd_dkdv_dbias(q, k, v, do, n, dk=dk, dv=dv, dbias=rows, **kw)
+                mark()
+            if rows is not None:
                 sa.bias_grad(rows, n, db=db)
-                mark(4)
+                mark()
         else:
             sa.softmax_fwd(q, k, v, n, o=o, lse2=lse2, **kw)
-            mark(1)
+            mark()
             sa.softmax_bwd_prep(o, do, n, delta, precision=precision, layout=layout)
-            mark(2)
-            sa.softmax_bwd_dq(q, k, v, do, lse2, delta, n, dq, **kw)
-            mark(3)
-            sa.softmax_bwd_dkdv(q, k, v, do, lse2, delta, n, dk, dv, **kw)
-            mark(4)
+            mark()
+            if not split_bwd:
+                sa._binding.softmax_bwd_fused(q, k, v, do, lse2, delta, n, dq, dk, dv, **kw)
+                mark()
+            else:
+                sa.softmax_bwd_dq(q, k, v, do, lse2, delta, n, dq, **kw)
+                mark()
+                sa.softmax_bwd_dkdv(q, k, v, do, lse2, delta, n, dk, dv, **kw)
+                mark()
 
     settled = settle(step, settle_ms)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
@@ -333,6 +351,8 @@ def main():
                     help="element type of the tensors (fp16: the fp16 build of the kernels)")
     ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
                     help="wall time of untimed steps run before the warm-up steps (clocks reach steady state)")
+    ap.add_argument("--split-bwd", action="store_true",
+                    help="time the backward as two launches (dQ, then dK/dV) instead of the fused sigattn_bwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -386,14 +406,15 @@ def main():
     w = workloads.WORKLOADS[name]
     precision = a.precision if a.precision != "auto" else ("split" if w.scale_qkv > 1.0 else "fast")
     r = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn=a.attn, causal=a.causal,
-                      bias=a.bias, dtype=a.dtype, settle_ms=a.settle_ms)
+                      bias=a.bias, dtype=a.dtype, settle_ms=a.settle_ms, split_bwd=a.split_bwd)
     n = r["seqlens"]
     total = r["fwd_flops"] + r["bwd_flops"]
     value = tflops(total, r["step_ms"])
     fwd_tf = tflops(r["fwd_flops"], r["kernel_avg_ms"]["fwd"])
     bwd_tf = tflops(r["bwd_flops"], sum(v_ for k_, v_ in r["kernel_avg_ms"].items() if k_.startswith("bwd")))
 
-    dominant = max(KERNEL_FLOP_UNITS, key=r["kernel_avg_ms"].get)
+    timed = [k_ for k_ in KERNEL_FLOP_UNITS if k_ in r["kernel_avg_ms"]]
+    dominant = max(timed, key=r["kernel_avg_ms"].get)
     dom_flops = KERNEL_FLOP_UNITS[dominant] * r["pair_flops"]
     achieved = tflops(dom_flops, r["kernel_avg_ms"][dominant])
     roofline = {
@@ -401,13 +422,15 @@ def main():
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": load_traffic(dominant, name, precision),
         "kernel": dominant, "flop_per_launch": dom_flops,
+        "executed_mfma_frac": round(tflops(EXECUTED_UNITS[dominant][precision == "split"] * r["pair_flops"],
+                                           r["kernel_avg_ms"][dominant]) / PEAK_BF16_TFLOPS, 4),
         "avg_launch_ms": round(r["kernel_avg_ms"][dominant], 5),
         "per_kernel": {
             kname: {"avg_ms": round(r["kernel_avg_ms"][kname], 5), "median_ms": round(r["kernel_median_ms"][kname], 5),
                      "min_ms": round(r["kernel_min_ms"][kname], 5),
                      "algorithmic_tflops": round(tflops(KERNEL_FLOP_UNITS[kname] * r["pair_flops"],
                                                         r["kernel_avg_ms"][kname]), 2)}
-            for kname in KERNEL_FLOP_UNITS},
+            for kname in timed},
     }
     if "bwd_bias_grad" in r["kernel_avg_ms"]:
         roofline["per_kernel"]["bwd_bias_grad"] = {"avg_ms": round(r["kernel_avg_ms"]["bwd_bias_grad"], 5),
@@ -484,7 +507,7 @@ def main():
 
     if a.compare_softmax and a.attn == "sigmoid":
         rc = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn="softmax", causal=a.causal,
-                           settle_ms=a.settle_ms)
+                           settle_ms=a.settle_ms, split_bwd=a.split_bwd)
         out["softmax_comparison"] = {
             "value": round(tflops(total, rc["step_ms"]), 2),
             "fwd_tflops": round(tflops(rc["fwd_flops"], rc["kernel_avg_ms"]["fwd"]), 2),

@@ -179,6 +179,18 @@ sigattn_status sigattn_bwd_dq(const sigattn_args *args, const void *q, const voi
 sigattn_status sigattn_bwd_dkdv(const sigattn_args *args, const void *q, const void *k,
                                 const void *v, const void *dout, void *dk, void *dv);
 
+/* The whole backward in one call: dQ (as sigattn_bwd_dq), dK and dV (as
+ * sigattn_bwd_dkdv) and, if dbias is not NULL, the bias-gradient rows (as
+ * sigattn_bwd_dkdv_dbias).  Results are bitwise those of the separate calls.
+ * Both sides normally run in ONE fused launch: the dK/dV workgroups first,
+ * then the dQ workgroups, which fill the CUs the dK/dV work leaves idle
+ * towards its end (§2C's two backward kernels, scheduled together; still no
+ * atomics: every output row has one writer).  args->strides, if set, has 7
+ * entries: q, k, v, dout, dq, dk, dv.  Same checks and errors as the separate
+ * calls (dq, dk, dv are outputs; dbias is checked like a row output). */
+sigattn_status sigattn_bwd(const sigattn_args *args, const void *q, const void *k, const void *v,
+                           const void *dout, void *dq, void *dk, void *dv, float *dbias);
+
 /* Backward, key side, with the gradient of the bias: as sigattn_bwd_dkdv, and
  * also, per key row, dbias[b, h, j] = sum over valid queries i of dX_ij, where
  * dX = dO V^T * P * (1 - P) is the gradient of the scores X_ij = q_i.k_j /
@@ -226,6 +238,12 @@ sigattn_status sigattn_softmax_bwd_dq(const sigattn_args *args, const void *q, c
 sigattn_status sigattn_softmax_bwd_dkdv(const sigattn_args *args, const void *q, const void *k,
                                         const void *v, const void *dout, const float *lse2,
                                         const float *delta, void *dk, void *dv);
+/* Both softmax backward kernels in one fused launch (after
+ * sigattn_softmax_bwd_prep), as sigattn_bwd does for sigmoid; strides order
+ * q, k, v, dout, dq, dk, dv. */
+sigattn_status sigattn_softmax_bwd(const sigattn_args *args, const void *q, const void *k, const void *v,
+                                   const void *dout, const float *lse2, const float *delta, void *dq,
+                                   void *dk, void *dv);
 
 /* Runs every check the compute call for pass p would run (shape, lengths,
  * bias, precision, null pointers, alignment, strides, aliasing) on the

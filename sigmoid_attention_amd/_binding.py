@@ -34,7 +34,7 @@ LAYOUTS = {"bhld": (0, 1, 2, 3), "blhd": (0, 2, 1, 3)}
 EXPORTED = ("sigattn_fwd", "sigattn_bwd_dq", "sigattn_bwd_dkdv", "sigattn_status_str",
             "sigattn_plan_stats", "sigattn_tile_shape", "sigattn_validate", "sigattn_softmax_fwd",
             "sigattn_softmax_bwd_prep", "sigattn_softmax_bwd_dq", "sigattn_softmax_bwd_dkdv",
-            "sigattn_bwd_dkdv_dbias", "sigattn_bias_grad")
+            "sigattn_bwd_dkdv_dbias", "sigattn_bias_grad", "sigattn_bwd", "sigattn_softmax_bwd")
 
 
 class SigattnStrides(ctypes.Structure):
@@ -97,6 +97,10 @@ def load() -> ctypes.CDLL:
     lib.sigattn_softmax_bwd_dkdv.argtypes = [ap, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bwd_dkdv_dbias.argtypes = [ap, vp, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bias_grad.argtypes = [ap, vp, vp]
+    lib.sigattn_bwd.argtypes = [ap, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sigattn_softmax_bwd.argtypes = [ap, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sigattn_bwd.restype = ctypes.c_int
+    lib.sigattn_softmax_bwd.restype = ctypes.c_int
     for f in (lib.sigattn_softmax_fwd, lib.sigattn_softmax_bwd_prep, lib.sigattn_softmax_bwd_dq,
               lib.sigattn_softmax_bwd_dkdv, lib.sigattn_bwd_dkdv_dbias, lib.sigattn_bias_grad):
         f.restype = ctypes.c_int
@@ -267,6 +271,30 @@ def bwd_dkdv_dbias(q, k, v, dout, seqlens, dk=None, dv=None, dbias=None, bias_mo
     return dk, dv, dbias
 
 
+def bwd(q, k, v, dout, seqlens, dq=None, dk=None, dv=None, dbias=None, bias_rows=False, bias_mode="seqlen",
+        bias_arg=0.0, precision="fast", stream=None, layout: str = "bhld", causal: bool = False):
+    """The whole backward in one call (normally one fused launch): returns
+    (dQ, dK, dV), plus the bias-gradient rows if `bias_rows` or `dbias` is
+    given.  Bitwise the results of bwd_dq and bwd_dkdv(_dbias)."""
+    import torch
+
+    dq = _new_like(q) if dq is None else dq
+    dk = _new_like(k) if dk is None else dk
+    dv = _new_like(v) if dv is None else dv
+    want = bias_rows or dbias is not None
+    if want:
+        dbias = _rows_like(q, layout) if dbias is None else dbias
+        _check_rows(dbias, q, layout)
+    args, keep = _tensor_args((q, k, v, dout, dq, dk, dv), seqlens, bias_mode, bias_arg, precision, stream, layout,
+                              causal)
+    with torch.cuda.device(q.device):
+        _check(load().sigattn_bwd(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dbias.data_ptr() if want else None),
+               "sigattn_bwd")
+    del keep
+    return (dq, dk, dv, dbias) if want else (dq, dk, dv)
+
+
 def bias_grad(dbias, seqlens, db=None, stream=None):
     """db[h] = sum over sequences and rows of dbias[:, h, :] (fp32 [H]), the
     gradient of a per-head bias.  dbias as returned by bwd_dkdv_dbias."""
@@ -375,11 +403,31 @@ def softmax_bwd_dkdv(q, k, v, dout, lse2, delta, seqlens, dk=None, dv=None, prec
 def softmax_bwd(q, k, v, o, dout, lse2, seqlens, dq=None, dk=None, dv=None, delta=None, precision="fast",
                 stream=None, layout="bhld", causal=False):
     """Softmax attention backward: delta = rowsum(dO * O), then the dQ and
-    the dK/dV kernels.  Returns (dQ, dK, dV)."""
-    kw = dict(precision=precision, stream=stream, layout=layout)
-    delta = softmax_bwd_prep(o, dout, seqlens, delta, **kw)
-    dq = softmax_bwd_dq(q, k, v, dout, lse2, delta, seqlens, dq, causal=causal, **kw)
-    dk, dv = softmax_bwd_dkdv(q, k, v, dout, lse2, delta, seqlens, dk, dv, causal=causal, **kw)
+    dK/dV kernels in one fused launch.  Returns (dQ, dK, dV)."""
+    import torch
+
+    delta = softmax_bwd_prep(o, dout, seqlens, delta, precision=precision, stream=stream, layout=layout)
+    return softmax_bwd_fused(q, k, v, dout, lse2, delta, seqlens, dq, dk, dv, precision, stream, layout, causal)
+
+
+def softmax_bwd_fused(q, k, v, dout, lse2, delta, seqlens, dq=None, dk=None, dv=None, precision="fast", stream=None,
+                      layout="bhld", causal=False):
+    """dQ, dK and dV of the softmax path in one fused launch, given lse2 and
+    delta (softmax_bwd_prep).  Returns (dQ, dK, dV)."""
+    import torch
+
+    dq = _new_like(q) if dq is None else dq
+    dk = _new_like(k) if dk is None else dk
+    dv = _new_like(v) if dv is None else dv
+    for x in (lse2, delta):
+        _check_rows(x, q, layout)
+    args, keep = _tensor_args((q, k, v, dout, dq, dk, dv), seqlens, "seqlen", 0.0, precision, stream, layout,
+                              causal)
+    with torch.cuda.device(q.device):
+        _check(load().sigattn_softmax_bwd(ctypes.byref(args), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          dout.data_ptr(), lse2.data_ptr(), delta.data_ptr(), dq.data_ptr(),
+                                          dk.data_ptr(), dv.data_ptr()), "sigattn_softmax_bwd")
+    del keep
     return dq, dk, dv
 
 

@@ -75,14 +75,16 @@ struct View {
 };
 
 // Contiguous [B, H, Lmax, d] unless args->strides says otherwise.
-std::vector<View> views(const sigattn_args* a, const void* const* t, int n) {
+// idx: which args->strides entry each of the n tensors uses (null: entry i).
+std::vector<View> views(const sigattn_args* a, const void* const* t, int n, const int* idx = nullptr) {
   std::vector<View> v(n);
   for (int i = 0; i < n; ++i) {
     v[i].p = (uintptr_t)t[i];
     if (a->strides) {
-      v[i].sb = a->strides[i].b;
-      v[i].sh = a->strides[i].h;
-      v[i].sl = a->strides[i].l;
+      const sigattn_strides& s = a->strides[idx ? idx[i] : i];
+      v[i].sb = s.b;
+      v[i].sh = s.h;
+      v[i].sl = s.l;
     } else {
       v[i].sl = a->d;
       v[i].sh = (int64_t)a->Lmax * a->d;
@@ -221,8 +223,8 @@ sigattn_status check_rows(const sigattn_args* a, const void* const* t, int nt, i
 }
 
 // Strides of the call's tensor arguments, in argument order, into the schedule.
-void set_strides(const sigattn_args* a, const void* const* t, int n, Launch& L) {
-  const std::vector<View> v = views(a, t, n);
+void set_strides(const sigattn_args* a, const void* const* t, int n, Launch& L, const int* idx = nullptr) {
+  const std::vector<View> v = views(a, t, n, idx);
   for (int i = 0; i < n; ++i) {
     L.sched.sb[i] = v[i].sb;
     L.sched.sh[i] = v[i].sh;
@@ -253,6 +255,63 @@ sigattn_status run(const sigattn_args* a, int32_t pass, const void* const* t, in
     set_strides(a, t, n, L);
     L.sched.head_bias = a->bias_mode == SIGATTN_BIAS_PER_HEAD ? a->head_bias : nullptr;
     if (launch_one(L) != hipSuccess) return SIGATTN_ERR_HIP;
+  }
+  return SIGATTN_OK;
+}
+
+// The backward of both sides.  When each side's schedule is one launch (all
+// but batches beyond one launch's piece or zero-fill capacity), both run in
+// one fused launch, the dK/dV blocks first; otherwise the dK/dV launches run,
+// then the dQ launches.  t: q, k, v, dout, dq, dk, dv (args->strides order).
+// lse2/delta: the softmax path; dbias: the sigmoid bias-gradient rows.
+sigattn_status run_bwd(const sigattn_args* a, const void* const* t, const float* lse2, const float* delta,
+                       float* dbias) {
+  static const int kDq[] = {0, 1, 2, 3, 4}, kKv[] = {0, 1, 2, 3, 5, 6};
+  const void* tq[] = {t[0], t[1], t[2], t[3], t[4]};
+  const void* tkv[] = {t[0], t[1], t[2], t[3], t[5], t[6]};
+  std::vector<Launch> pk = sigattn::build_plan(plan_input(a, SIGATTN_PASS_BWD_DKDV), nullptr);
+  std::vector<Launch> pq = sigattn::build_plan(plan_input(a, SIGATTN_PASS_BWD_DQ), nullptr);
+  const float* hb = a->bias_mode == SIGATTN_BIAS_PER_HEAD ? a->head_bias : nullptr;
+  for (Launch& L : pk) {
+    set_strides(a, tkv, 6, L, kKv);
+    L.sched.head_bias = hb;
+  }
+  for (Launch& L : pq) {
+    set_strides(a, tq, 5, L, kDq);
+    L.sched.head_bias = hb;
+  }
+  const bool split = a->precision == SIGATTN_PREC_SPLIT;
+  const hipStream_t st = (hipStream_t)a->stream;
+  const auto impl_fused = f16(a) ? sigattn::f16::launch_bwd_fused : sigattn::bf16::launch_bwd_fused;
+  (void)hipGetLastError();
+  if (pk.size() == 1 && pq.size() == 1) {
+    sigattn::BwdSched P;  // ~7 KB, copied into the launch's kernel arguments
+    P.kv = pk[0].sched;
+    P.dq = pq[0].sched;
+    P.dq_off = (pk[0].blocks + 7) / 8 * 8;
+    const int32_t blocks = P.dq_off + pq[0].blocks;
+    return impl_fused(a->d, split, P, blocks, t[0], t[1], t[2], t[3], const_cast<void*>(t[4]),
+                      const_cast<void*>(t[5]), const_cast<void*>(t[6]), lse2, delta, dbias, st) == hipSuccess
+               ? SIGATTN_OK
+               : SIGATTN_ERR_HIP;
+  }
+  for (const Launch& L : pk) {
+    const hipError_t e =
+        lse2 ? (f16(a) ? sigattn::f16::launch_softmax_dkdv : sigattn::bf16::launch_softmax_dkdv)(
+                   a->d, split, L, t[0], t[1], t[2], t[3], lse2, delta, const_cast<void*>(t[5]),
+                   const_cast<void*>(t[6]), st)
+             : (f16(a) ? sigattn::f16::launch_bwd_dkdv : sigattn::bf16::launch_bwd_dkdv)(
+                   a->d, split, L, t[0], t[1], t[2], t[3], const_cast<void*>(t[5]), const_cast<void*>(t[6]), dbias,
+                   st);
+    if (e != hipSuccess) return SIGATTN_ERR_HIP;
+  }
+  for (const Launch& L : pq) {
+    const hipError_t e =
+        lse2 ? (f16(a) ? sigattn::f16::launch_softmax_dq : sigattn::bf16::launch_softmax_dq)(
+                   a->d, split, L, t[0], t[1], t[2], t[3], lse2, delta, const_cast<void*>(t[4]), st)
+             : (f16(a) ? sigattn::f16::launch_bwd_dq : sigattn::bf16::launch_bwd_dq)(
+                   a->d, split, L, t[0], t[1], t[2], t[3], const_cast<void*>(t[4]), st);
+    if (e != hipSuccess) return SIGATTN_ERR_HIP;
   }
   return SIGATTN_OK;
 }
@@ -320,6 +379,35 @@ sigattn_status sigattn_bwd_dkdv_dbias(const sigattn_args* a, const void* q, cons
   return run(a, SIGATTN_PASS_BWD_DKDV, t, 6, [&](const Launch& L) {
     return (f16(a) ? sigattn::f16::launch_bwd_dkdv : sigattn::bf16::launch_bwd_dkdv)(a->d, split, L, q, k, v, dout, dk, dv, dbias, (hipStream_t)a->stream);
   });
+}
+
+sigattn_status sigattn_bwd(const sigattn_args* a, const void* q, const void* k, const void* v, const void* dout,
+                           void* dq, void* dk, void* dv, float* dbias) {
+  sigattn_status s = check_args(a);
+  if (s != SIGATTN_OK) return s;
+  const void* in[] = {q, k, v, dout};
+  void* out[] = {dq, dk, dv};
+  if ((s = check_ptrs(a, in, 4, out, 3)) != SIGATTN_OK) return s;
+  const void* t[] = {q, k, v, dout, dq, dk, dv};
+  const void* r[] = {dbias};
+  const int nr = dbias ? 1 : 0;
+  if (nr && (s = check_rows(a, t, 7, 4, r, 1, 0)) != SIGATTN_OK) return s;
+  if ((s = check_head_bias(a, t, 7, 4, r, nr)) != SIGATTN_OK) return s;
+  return run_bwd(a, t, nullptr, nullptr, dbias);
+}
+
+sigattn_status sigattn_softmax_bwd(const sigattn_args* a, const void* q, const void* k, const void* v,
+                                   const void* dout, const float* lse2, const float* delta, void* dq, void* dk,
+                                   void* dv) {
+  sigattn_status s = check_args(a);
+  if (s != SIGATTN_OK) return s;
+  const void* in[] = {q, k, v, dout};
+  void* out[] = {dq, dk, dv};
+  if ((s = check_ptrs(a, in, 4, out, 3)) != SIGATTN_OK) return s;
+  const void* t[] = {q, k, v, dout, dq, dk, dv};
+  const void* r[] = {lse2, delta};
+  if ((s = check_rows(a, t, 7, 4, r, 2, 2)) != SIGATTN_OK) return s;
+  return run_bwd(a, t, lse2, delta, nullptr);
 }
 
 sigattn_status sigattn_bias_grad(const sigattn_args* a, const float* dbias, float* db) {

@@ -287,11 +287,12 @@ struct FragAddr {
 // n_b..Lmax-1 of one or two outputs (tensor arguments t1, t2) as 0 with
 // 16-byte stores; the compute workgroups store valid rows only, so no row has
 // two writers.
+// vb: the workgroup's block index within this schedule's part of the grid.
 template <int D>
-__device__ __forceinline__ void zero_padded_rows(const Sched& S, uint16_t* __restrict__ o1, int t1,
+__device__ __forceinline__ void zero_padded_rows(const Sched& S, int vb, uint16_t* __restrict__ o1, int t1,
                                                  uint16_t* __restrict__ o2, int t2,
                                                  float* __restrict__ rows = nullptr) {
-  const int zb = (int)blockIdx.x - S.compute_blocks;
+  const int zb = vb - S.compute_blocks;
   const int bhl = zb / kZeroSplit, part = zb % kZeroSplit;
   const int bl = bhl / S.H;
   if (bl >= S.zero_nseq) return;
@@ -319,10 +320,11 @@ __device__ __forceinline__ float item_c2(const Sched& S, const Item& it) {
   return S.head_bias ? -1.4426950408889634f * S.head_bias[it.bh % S.H] : it.c2;
 }
 
-// Work item of this workgroup (see plan.h); false for idle blocks.  The
-// result is uniform across the workgroup.
-__device__ __forceinline__ bool find_item(const Sched& S, Item& it) {
-  return decode_item(S, (int32_t)(blockIdx.x & 7), (int32_t)(blockIdx.x >> 3), it);
+// Work item of block vb of this schedule's part of the grid (see plan.h);
+// false for idle blocks.  Uniform across the workgroup.  A part starts at a
+// multiple of 8, so vb & 7 is still the block's XCD.
+__device__ __forceinline__ bool find_item(const Sched& S, int vb, Item& it) {
+  return decode_item(S, (int32_t)(vb & 7), (int32_t)(vb >> 3), it);
 }
 
 }  // namespace SIGATTN_ELT

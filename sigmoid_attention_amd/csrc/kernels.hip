@@ -320,11 +320,11 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
   __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
 
   if ((int)blockIdx.x >= S.compute_blocks) {
-    zero_padded_rows<D>(S, O, 3, nullptr, 0);
+    zero_padded_rows<D>(S, (int)blockIdx.x, O, 3, nullptr, 0);
     return;
   }
   Item it;
-  if (!find_item(S, it)) return;
+  if (!find_item(S, (int)blockIdx.x, it)) return;
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -439,11 +439,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd_softmax_kernel(
   __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
 
   if ((int)blockIdx.x >= S.compute_blocks) {
-    zero_padded_rows<D>(S, O, 3, nullptr, 0, LSE);
+    zero_padded_rows<D>(S, (int)blockIdx.x, O, 3, nullptr, 0, LSE);
     return;
   }
   Item it;
-  if (!find_item(S, it)) return;
+  if (!find_item(S, (int)blockIdx.x, it)) return;
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -531,20 +531,25 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd_softmax_kernel(
 // LDS: K in 3 stages (tile j: transposing reads for dQ; tile j+1: scores;
 // tile j+2: loading), V in 2 stages (tile j: dP; tile j+1: loading).
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT, bool SOFTMAX = false>
-__global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, const float* __restrict__ LSE,
-    const float* __restrict__ DELTA, const Sched S) {
-  constexpr int BQ = 128, BK = kInner, TILE = BK * D;
-  __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
+template <int D>
+constexpr int dq_lds_elems() { return 5 * kInner * D; }  // K0 K1 K2 V0 V1
 
-  if ((int)blockIdx.x >= S.compute_blocks) {
-    zero_padded_rows<D>(S, dQ, 4, nullptr, 0);
+// The dQ work of block vb of schedule S (a kernel of its own, or the dQ part
+// of the fused backward launch); lds: dq_lds_elems<D>() 16-bit elements.
+template <int D, bool SPLIT, bool SOFTMAX>
+__device__ __forceinline__ void dq_body(uint16_t* __restrict__ lds, int vb, const uint16_t* __restrict__ Q,
+                                        const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                        const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ,
+                                        const float* __restrict__ LSE, const float* __restrict__ DELTA,
+                                        const Sched& S) {
+  constexpr int BQ = 128, BK = kInner, TILE = BK * D;
+
+  if (vb >= S.compute_blocks) {
+    zero_padded_rows<D>(S, vb, dQ, 4, nullptr, 0);
     return;
   }
   Item it;
-  if (!find_item(S, it)) return;
+  if (!find_item(S, vb, it)) return;
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -624,6 +629,15 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
   }
 }
 
+template <int D, bool SPLIT, bool SOFTMAX = false>
+__global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, const float* __restrict__ LSE,
+    const float* __restrict__ DELTA, const Sched S) {
+  __shared__ __align__(16) uint16_t lds[dq_lds_elems<D>()];
+  dq_body<D, SPLIT, SOFTMAX>(lds, (int)blockIdx.x, Q, K, V, dO, dQ, LSE, DELTA, S);
+}
+
 // ---------------------------------------------------------------------------
 // Backward, dK/dV.  Item = (b, h, 128-key tile).  Inner loop: 64-query tiles j.
 // Per wave (32 keys): S_j = Q_j . K^T (64 queries x 32 keys), dP_j = dO_j . V^T,
@@ -636,22 +650,30 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
 // latency is covered; the next tile's S and dP follow, with the fragments of
 // each K-step read one step ahead.
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT, bool SOFTMAX = false, bool DB = false>
-__global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    const float* __restrict__ LSE, const float* __restrict__ DELTA, float* __restrict__ DBIAS, const Sched S) {
-  constexpr int BKV = 128, BQ = DkdvCfg<D>::BQ, TILE = BQ * D, NMB = BQ / 32, NC = BQ / 16;
-  __shared__ __align__(16) uint16_t lds[6 * TILE];  // Q0 Q1 Q2 G0 G1 G2
-  // softmax: lse2 and delta of each inner tile's rows, 3 stages
-  __shared__ __align__(16) float rowv[SOFTMAX ? 6 * BQ : 4];
+template <int D>
+constexpr int dkdv_lds_elems() { return 6 * DkdvCfg<D>::BQ * D; }  // Q0 Q1 Q2 G0 G1 G2
+// softmax: lse2 and delta of each inner tile's rows, 3 stages
+template <int D, bool SOFTMAX>
+constexpr int dkdv_row_floats() { return SOFTMAX ? 6 * DkdvCfg<D>::BQ : 4; }
 
-  if ((int)blockIdx.x >= S.compute_blocks) {
-    zero_padded_rows<D>(S, dK, 4, dV, 5, DB ? DBIAS : nullptr);
+// The dK/dV work of block vb of schedule S (a kernel of its own, or the dK/dV
+// part of the fused backward launch); lds: dkdv_lds_elems<D>() 16-bit
+// elements, rowv: dkdv_row_floats<D, SOFTMAX>() floats.
+template <int D, bool SPLIT, bool SOFTMAX, bool DB>
+__device__ __forceinline__ void dkdv_body(uint16_t* __restrict__ lds, float* __restrict__ rowv, int vb,
+                                          const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                          const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                                          uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                                          const float* __restrict__ LSE, const float* __restrict__ DELTA,
+                                          float* __restrict__ DBIAS, const Sched& S) {
+  constexpr int BKV = 128, BQ = DkdvCfg<D>::BQ, TILE = BQ * D, NMB = BQ / 32, NC = BQ / 16;
+
+  if (vb >= S.compute_blocks) {
+    zero_padded_rows<D>(S, vb, dK, 4, dV, 5, DB ? DBIAS : nullptr);
     return;
   }
   Item it;
-  if (!find_item(S, it)) return;
+  if (!find_item(S, vb, it)) return;
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -776,6 +798,40 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
   }
 }
 
+template <int D, bool SPLIT, bool SOFTMAX = false, bool DB = false>
+__global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+    const float* __restrict__ LSE, const float* __restrict__ DELTA, float* __restrict__ DBIAS, const Sched S) {
+  __shared__ __align__(16) uint16_t lds[dkdv_lds_elems<D>()];
+  __shared__ __align__(16) float rowv[dkdv_row_floats<D, SOFTMAX>()];
+  dkdv_body<D, SPLIT, SOFTMAX, DB>(lds, rowv, (int)blockIdx.x, Q, K, V, dO, dK, dV, LSE, DELTA, DBIAS, S);
+}
+
+// ---------------------------------------------------------------------------
+// Fused backward: one launch runs the dK/dV work (blocks 0 .. dq_off-1, in
+// the dK/dV schedule's order: its items longest first, then its zero fill)
+// and the dQ work (blocks dq_off .., the same for dQ).  The two parts share
+// nothing but the launch: the dQ items fill the CUs that the dK/dV items
+// leave idle towards their end, and one launch's fixed cost is saved.  Each
+// workgroup takes one role, so LDS is the larger of the two layouts.
+// ---------------------------------------------------------------------------
+template <int D, bool SPLIT, bool SOFTMAX = false, bool DB = false>
+__global__ __launch_bounds__(kThreads, DqCfg<D>::OCC < DkdvCfg<D>::OCC ? DqCfg<D>::OCC : DkdvCfg<D>::OCC) void
+bwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+           const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK,
+           uint16_t* __restrict__ dV, const float* __restrict__ LSE, const float* __restrict__ DELTA,
+           float* __restrict__ DBIAS, const BwdSched P) {
+  constexpr int E = dq_lds_elems<D>() > dkdv_lds_elems<D>() ? dq_lds_elems<D>() : dkdv_lds_elems<D>();
+  __shared__ __align__(16) uint16_t lds[E];
+  __shared__ __align__(16) float rowv[dkdv_row_floats<D, SOFTMAX>()];
+  const int b = (int)blockIdx.x;
+  if (b < P.dq_off)
+    dkdv_body<D, SPLIT, SOFTMAX, DB>(lds, rowv, b, Q, K, V, dO, dK, dV, LSE, DELTA, DBIAS, P.kv);
+  else
+    dq_body<D, SPLIT, SOFTMAX>(lds, b - P.dq_off, Q, K, V, dO, dQ, LSE, DELTA, P.dq);
+}
+
 // delta = rowsum(dO * O) per row for the softmax backward (0 on padded
 // rows); one thread per row, fp32 accumulation of the bf16 products.
 template <int D>
@@ -830,6 +886,25 @@ hipError_t launch_dkdv_t(const Launch& L, const void* q, const void* k, const vo
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dk, (uint16_t*)dv,
                        (const float*)nullptr, (const float*)nullptr, (float*)nullptr, L.sched);
   return hipGetLastError();
+}
+
+template <int D, bool SPLIT, bool SOFTMAX, bool DB>
+hipError_t launch_bwd_fused_t(const BwdSched& P, int32_t blocks, const void* q, const void* k, const void* v,
+                              const void* g, void* dq, void* dk, void* dv, const float* lse, const float* delta,
+                              float* dbias, hipStream_t st) {
+  hipLaunchKernelGGL((bwd_kernel<D, SPLIT, SOFTMAX, DB>), dim3(blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq, (uint16_t*)dk,
+                     (uint16_t*)dv, lse, delta, dbias, P);
+  return hipGetLastError();
+}
+
+template <int D, bool SPLIT>
+hipError_t launch_bwd_fused_d(const BwdSched& P, int32_t blocks, const void* q, const void* k, const void* v,
+                              const void* g, void* dq, void* dk, void* dv, const float* lse, const float* delta,
+                              float* dbias, hipStream_t st) {
+  if (lse) return launch_bwd_fused_t<D, SPLIT, true, false>(P, blocks, q, k, v, g, dq, dk, dv, lse, delta, dbias, st);
+  if (dbias) return launch_bwd_fused_t<D, SPLIT, false, true>(P, blocks, q, k, v, g, dq, dk, dv, lse, delta, dbias, st);
+  return launch_bwd_fused_t<D, SPLIT, false, false>(P, blocks, q, k, v, g, dq, dk, dv, lse, delta, dbias, st);
 }
 
 // db[h] = sum over sequences b and rows j of dbias[b, h, j]: one workgroup of
@@ -928,6 +1003,16 @@ hipError_t launch_bwd_dkdv(int d, bool split, const Launch& L, const void* q, co
                  : launch_dkdv_t<64, false>(L, q, k, v, g, dk, dv, dbias, st);
   return split ? launch_dkdv_t<128, true>(L, q, k, v, g, dk, dv, dbias, st)
                : launch_dkdv_t<128, false>(L, q, k, v, g, dk, dv, dbias, st);
+}
+
+hipError_t launch_bwd_fused(int d, bool split, const BwdSched& P, int32_t blocks, const void* q, const void* k,
+                            const void* v, const void* g, void* dq, void* dk, void* dv, const float* lse2,
+                            const float* delta, float* dbias, hipStream_t st) {
+  if (d == 64)
+    return split ? kern::launch_bwd_fused_d<64, true>(P, blocks, q, k, v, g, dq, dk, dv, lse2, delta, dbias, st)
+                 : kern::launch_bwd_fused_d<64, false>(P, blocks, q, k, v, g, dq, dk, dv, lse2, delta, dbias, st);
+  return split ? kern::launch_bwd_fused_d<128, true>(P, blocks, q, k, v, g, dq, dk, dv, lse2, delta, dbias, st)
+               : kern::launch_bwd_fused_d<128, false>(P, blocks, q, k, v, g, dq, dk, dv, lse2, delta, dbias, st);
 }
 
 hipError_t launch_bias_grad(int32_t B, int32_t H, int32_t Lmax, const float* dbias, float* db, hipStream_t st) {

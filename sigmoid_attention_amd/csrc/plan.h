@@ -101,6 +101,15 @@ struct Launch {
   int32_t blocks;  // grid size: compute blocks + zero-fill blocks
 };
 
+// The fused backward launch: the dK/dV schedule's blocks first, then the dQ
+// schedule's from block dq_off (a multiple of 8, so that each part's block
+// index keeps its XCD; blocks between the two parts are idle).
+struct BwdSched {
+  Sched kv;
+  Sched dq;
+  int32_t dq_off;
+};
+
 struct PlanInput {
   int32_t B, H, Lmax, d;
   const int32_t* seqlens;

@@ -61,12 +61,18 @@ class _SigmoidAttention(torch.autograd.Function):
         kw = dict(bias_mode=bias_mode, bias_arg=arg, precision=precision, layout=layout, causal=causal)
         dq = dk = dv = db = None
         want_db = head_bias is not None and ctx.needs_input_grad[3]
-        if ctx.needs_input_grad[0]:
+        want_kv = ctx.needs_input_grad[1] or ctx.needs_input_grad[2] or want_db
+        if ctx.needs_input_grad[0] and want_kv:  # one fused launch for both sides
+            out = _binding.bwd(q, k, v, do, lens, bias_rows=want_db, **kw)
+            dq, dk, dv = out[:3]
+            if want_db:
+                db = _binding.bias_grad(out[3], lens)
+        elif ctx.needs_input_grad[0]:
             dq = _binding.bwd_dq(q, k, v, do, lens, **kw)
-        if want_db:
+        elif want_db:
             dk, dv, rows = _binding.bwd_dkdv_dbias(q, k, v, do, lens, **kw)
             db = _binding.bias_grad(rows, lens)
-        elif ctx.needs_input_grad[1] or ctx.needs_input_grad[2]:
+        elif want_kv:
             dk, dv = _binding.bwd_dkdv(q, k, v, do, lens, **kw)
         return dq, dk, dv, db, None, None, None, None, None, None
 

@@ -303,3 +303,25 @@ def test_fp16_dtype_validates():
     a, keep = args(dtype="fp16")
     assert validate(a, 0, P[:4]) == OK
     assert validate(a, 2, P[:6]) == OK
+
+
+def bwd_all(a, q=P[0], k=P[1], v=P[2], g=P[3], dq_=P[4], dk=P[5], dv=P[6], db=None):
+    return sa.load().sigattn_bwd(ctypes.byref(a), q, k, v, g, dq_, dk, dv, db)
+
+
+def test_fused_backward_checks():
+    """sigattn_bwd validates like the separate calls before launching."""
+    a, keep = args()
+    assert bwd_all(a, q=None) == NULL
+    assert bwd_all(a, dv=None) == NULL
+    assert bwd_all(a, dk=P[4]) == ALIAS            # dk on top of dq
+    assert bwd_all(a, dq_=P[0]) == ALIAS           # dq on top of q
+    assert bwd_all(a, dv=P[6] + 8) == ALIGN
+    assert bwd_all(a, db=P[7] + 4) == ALIGN
+    assert bwd_all(a, db=P[5] + 64) == ALIAS       # rows inside dk
+    ab, keepb = args(lens=(200, 1))
+    assert bwd_all(ab) == SEQLEN
+    ah, keeph = args(bias_mode=3, head_bias=P[4] + 64)  # bias values inside dq
+    assert bwd_all(ah) == ALIAS
+    lib = sa.load()
+    assert lib.sigattn_softmax_bwd(ctypes.byref(a), P[0], P[1], P[2], P[3], None, P[5], P[6], P[7], 0) == NULL
