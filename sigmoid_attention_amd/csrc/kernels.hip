@@ -9,7 +9,8 @@
 //
 // Design for MI355X (not a translation of the pages' Triton/H100 kernel):
 // * one 256-thread workgroup (4 waves of 64) per output tile; each wave owns
-//   32 output rows, so every product is a 32x32x16 bf16 MFMA;
+//   32 output rows, so every product is a 32x32x16 MFMA (bf16, or fp16 in
+//   the fp16 build of this file);
 // * the tile streamed by the inner loop (K/V in the forward and dQ kernels,
 //   Q/dO in the dK/dV kernel) is loaded straight from global memory into LDS
 //   (buffer_load ... lds), one step ahead, with hardware zero-fill past the
@@ -26,7 +27,13 @@
 // * with no row normaliser (§2A), partial products need no running max or
 //   rescale, and the inner tiles may be visited in any order;
 // * padded output rows are written as 0 by trailing workgroups of the same
-//   launch (dispatched last, they fill the tail), so each call is one launch.
+//   launch (dispatched last, they fill the tail), so each call is one launch;
+// * the two backward kernels can run as one launch (bwd_kernel): the dQ
+//   workgroups fill the CUs that the dK/dV workgroups leave idle at the end;
+// * variants: a causal mask (tiles above the diagonal skipped, the straddling
+//   tile masked in registers), a per-head bias read from device memory with
+//   its gradient (per-key sums of dS), and softmax attention on the same
+//   schedule for comparison.
 #include "device_common.h"
 #include "launch.h"
 #include "plan.h"
@@ -48,8 +55,8 @@ template <int D> struct FwdCfg { static constexpr bool LA = D != 64; static cons
 template <int D> struct DqCfg { static constexpr bool LA = true; static constexpr int OCC = D == 64 ? 2 : 1; };
 template <int D> struct DkdvCfg { static constexpr int BQ = 64; static constexpr int OCC = D == 64 ? 2 : 1; };
 
-// sigma of the eight score values of K-chunk c, rounded to bf16 (hi) and, in
-// split precision, the bf16 remainder (lo).
+// sigma of the eight score values of K-chunk c, rounded to the element type
+// (hi) and, in split precision, the rounded remainder (lo).
 template <int D, bool SPLIT>
 __device__ __forceinline__ void sigmoid_chunk(const f32x16 (&sc)[2], int c, float c2, e16x8& hi, e16x8& lo) {
   f32x8 p = chunk8(sc[c >> 1], c & 1);
@@ -158,7 +165,7 @@ __device__ __forceinline__ void dsoftmax_chunk_row(const f32x16 (&sc)[NB], const
   if (SPLIT) pl = to_e16x8(p8 - to_f32x8(ph));
 }
 
-// Store 4 consecutive fp32 values of an output row as bf16 (8 bytes).
+// Store 4 consecutive fp32 values of an output row in the element type (8 bytes).
 __device__ __forceinline__ void store4(uint16_t* dst, const f32x16& acc, int i, float scale) {
   f32x8 v8;
 #pragma unroll
@@ -833,7 +840,7 @@ bwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const
 }
 
 // delta = rowsum(dO * O) per row for the softmax backward (0 on padded
-// rows); one thread per row, fp32 accumulation of the bf16 products.
+// rows); one thread per row, fp32 accumulation of the 16-bit products.
 template <int D>
 __global__ __launch_bounds__(256) void softmax_prep_kernel(const uint16_t* __restrict__ O,
                                                            const uint16_t* __restrict__ dO,
