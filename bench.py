@@ -25,10 +25,11 @@ Only one GPU is used: --gpus above 1 exits with a message.
 from __future__ import annotations
 
 import argparse
-import math
 import hashlib
 import json
+import math
 import os
+import re
 import sys
 import time
 
@@ -64,11 +65,15 @@ def pair_flops(seqlens, H, d, causal=False):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        h = hashlib.sha256(f.read())
-    for extra in ("device_common.h", "plan.h", "plan.cpp"):
-        with open(os.path.join(ROOT, "sigmoid_attention_amd", "csrc", extra), "rb") as f:
-            h.update(f.read())
+    """Hash of the code that decides what the kernels move: the kernel file,
+    its device header and the planner, with // comments and whitespace
+    removed (so a comment edit does not void measured counters)."""
+    h = hashlib.sha256()
+    for path in (KERNEL_SOURCE, *(os.path.join(ROOT, "sigmoid_attention_amd", "csrc", x)
+                                  for x in ("device_common.h", "plan.h", "plan.cpp"))):
+        with open(path, encoding="utf-8") as f:
+            code = re.sub(r"//[^\n]*", "", f.read())
+        h.update("".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
