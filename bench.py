@@ -426,6 +426,7 @@ def main():
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": load_traffic(dominant, name, precision),
+        "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         "kernel": dominant, "flop_per_launch": dom_flops,
         "executed_mfma_frac": round(tflops(EXECUTED_UNITS[dominant][precision == "split"] * r["pair_flops"],
                                            r["kernel_avg_ms"][dominant]) / PEAK_BF16_TFLOPS, 4),
@@ -437,6 +438,8 @@ def main():
                                                         r["kernel_avg_ms"][kname]), 2)}
             for kname in timed},
     }
+    if roofline["traffic"] is not None:  # achieved HBM rate of the dominant kernel
+        roofline["hbm_gbps"] = round(roofline["traffic"] / (r["kernel_avg_ms"][dominant] * 1e-3) / 1e9, 1)
     if "bwd_bias_grad" in r["kernel_avg_ms"]:
         roofline["per_kernel"]["bwd_bias_grad"] = {"avg_ms": round(r["kernel_avg_ms"]["bwd_bias_grad"], 5),
                                                "median_ms": round(r["kernel_median_ms"]["bwd_bias_grad"], 5)}
