@@ -20,12 +20,17 @@ def to_dev(case):
     return {t: case[t].to(dev) for t in ("q", "k", "v", "do")}
 
 
-def run_all(t, seqlens, precision="fast", bias_mode="seqlen", bias_arg=0.0):
-    """Forward, dQ and dK/dV through the library on the current stream."""
+def run_all(t, seqlens, precision="fast", bias_mode="seqlen", bias_arg=0.0, fused=False):
+    """Forward, dQ and dK/dV through the library on the current stream: the
+    separate backward calls, or (fused=True) the one-launch sigattn_bwd that
+    bench.py times."""
     kw = dict(bias_mode=bias_mode, bias_arg=bias_arg, precision=precision)
     o = sa.fwd(t["q"], t["k"], t["v"], seqlens, **kw)
-    dq = sa.bwd_dq(t["q"], t["k"], t["v"], t["do"], seqlens, **kw)
-    dk, dv = sa.bwd_dkdv(t["q"], t["k"], t["v"], t["do"], seqlens, **kw)
+    if fused:
+        dq, dk, dv = sa.bwd(t["q"], t["k"], t["v"], t["do"], seqlens, **kw)
+    else:
+        dq = sa.bwd_dq(t["q"], t["k"], t["v"], t["do"], seqlens, **kw)
+        dk, dv = sa.bwd_dkdv(t["q"], t["k"], t["v"], t["do"], seqlens, **kw)
     torch.cuda.synchronize()
     return {"o": o, "dq": dq, "dk": dk, "dv": dv}
 
