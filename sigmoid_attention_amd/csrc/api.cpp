@@ -41,7 +41,7 @@ sigattn_status check_args(const sigattn_args* a) {
   // Element count must fit comfortably in 62 bits; B * H must fit the
   // schedule's 32-bit head index; byte offsets within one (sequence, head)
   // slice, up to one tile past Lmax, must fit the kernels' 32-bit buffer
-  // offsets (Lmax <= 4,194,048 at d = 128, 8,388,352 at d = 64).
+  // offsets (Lmax <= 8,388,351 at d = 128, 16,776,959 at d = 64).
   const double elems = (double)a->B * a->H * a->Lmax * a->d;
   if (elems > 4.0e18 || (int64_t)a->B * a->H > INT32_MAX) return SIGATTN_ERR_SHAPE;
   if (((int64_t)a->Lmax + kLmaxSlack) * a->d * 2 > INT32_MAX) return SIGATTN_ERR_SHAPE;
