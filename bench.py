@@ -358,6 +358,8 @@ def main():
                     help="wall time of untimed steps run before the warm-up steps (clocks reach steady state)")
     ap.add_argument("--split-bwd", action="store_true",
                     help="time the backward as two launches (dQ, then dK/dV) instead of the fused sigattn_bwd")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the sustained-MFMA probe reported beside the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -438,6 +440,13 @@ def main():
                                                         r["kernel_avg_ms"][kname]), 2)}
             for kname in timed},
     }
+    if not a.no_probe:  # the chip's sustained MFMA rate and clock, right after the timed region
+        pr = sa.probe_mfma()
+        roofline["measured_mfma_peak"] = {"tflops": round(pr["tflops"], 1),
+                                          "shader_clock_ghz": round(pr["shader_clock_ghz"], 3),
+                                          "kernel": "back-to-back bf16 32x32x16 MFMAs, 4 chains per wave, "
+                                                    "4 waves per SIMD (sigattn_probe_mfma)"}
+        roofline["frac_of_measured_peak"] = round(achieved / pr["tflops"], 4)
     if roofline["traffic"] is not None:  # achieved HBM rate of the dominant kernel
         roofline["hbm_gbps"] = round(roofline["traffic"] / (r["kernel_avg_ms"][dominant] * 1e-3) / 1e9, 1)
     if "bwd_bias_grad" in r["kernel_avg_ms"]:

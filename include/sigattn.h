@@ -253,6 +253,19 @@ sigattn_status sigattn_softmax_bwd(const sigattn_args *args, const void *q, cons
  * tensor pointers.  For callers that want to vet a layout ahead of time. */
 sigattn_status sigattn_validate(const sigattn_args *args, int32_t pass, const void *const *tensors);
 
+/* Measurement helper, not part of the method: runs `blocks` workgroups of
+ * 1024 threads, each wave issuing `iters` x 4 independent bf16 32x32x16 MFMAs
+ * (the product every kernel here uses) on register operands, so that a
+ * caller can time the sustained matrix-core rate of this chip under its
+ * current clocks.  out: device, blocks * 1024 floats (per-thread sums, to
+ * keep the work); clocks: device, 2 values written by block 0: shader-clock
+ * ticks (s_memtime) and 100 MHz ticks (s_memrealtime) over the loop, whose
+ * ratio gives the shader clock.  FLOP = blocks * 16 * iters * 4 * 32768.
+ * SIGATTN_ERR_NULL / _ALIGN (out 4-byte, clocks 8-byte) / _SHAPE (blocks
+ * outside [1, 65536], iters < 1) / _ALIAS before any launch. */
+sigattn_status sigattn_probe_mfma(int32_t blocks, int32_t iters, float *out, uint64_t *clocks,
+                                  void *stream);
+
 /* Static description of a status code; never NULL. */
 const char *sigattn_status_str(sigattn_status status);
 

@@ -15,10 +15,10 @@ HIP kernels; this package only marshals arguments and fails loudly if the
 library is not built.
 """
 from ._binding import (BIAS_MODES, DTYPES, EXPORTED, LAYOUTS, PASSES, PRECISIONS, SigattnError, bias_grad, bwd, bwd_dkdv,
-                       bwd_dkdv_dbias, bwd_dq, fwd, lib_path, load, make_args, plan_stats, softmax_bwd, softmax_bwd_dkdv, softmax_bwd_dq,
+                       bwd_dkdv_dbias, bwd_dq, fwd, lib_path, load, make_args, plan_stats, probe_mfma, softmax_bwd, softmax_bwd_dkdv, softmax_bwd_dq,
                        softmax_bwd_prep, softmax_fwd, status_str, tile_shape, validate)
 from .function import SigmoidAttention, lengths_from_padding_mask, sigmoid_attention, softmax_attention
 
 __all__ = ["BIAS_MODES", "DTYPES", "EXPORTED", "LAYOUTS", "PASSES", "PRECISIONS", "SigattnError", "SigmoidAttention",
            "bias_grad", "bwd", "bwd_dkdv", "bwd_dkdv_dbias", "bwd_dq", "fwd", "lengths_from_padding_mask", "lib_path", "load", "make_args",
-           "plan_stats", "sigmoid_attention", "softmax_attention", "softmax_bwd", "softmax_bwd_dkdv", "softmax_bwd_dq", "softmax_bwd_prep", "softmax_fwd", "status_str", "tile_shape", "validate"]
+           "plan_stats", "probe_mfma", "sigmoid_attention", "softmax_attention", "softmax_bwd", "softmax_bwd_dkdv", "softmax_bwd_dq", "softmax_bwd_prep", "softmax_fwd", "status_str", "tile_shape", "validate"]

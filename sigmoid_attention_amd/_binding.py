@@ -34,7 +34,8 @@ LAYOUTS = {"bhld": (0, 1, 2, 3), "blhd": (0, 2, 1, 3)}
 EXPORTED = ("sigattn_fwd", "sigattn_bwd_dq", "sigattn_bwd_dkdv", "sigattn_status_str",
             "sigattn_plan_stats", "sigattn_tile_shape", "sigattn_validate", "sigattn_softmax_fwd",
             "sigattn_softmax_bwd_prep", "sigattn_softmax_bwd_dq", "sigattn_softmax_bwd_dkdv",
-            "sigattn_bwd_dkdv_dbias", "sigattn_bias_grad", "sigattn_bwd", "sigattn_softmax_bwd")
+            "sigattn_bwd_dkdv_dbias", "sigattn_bias_grad", "sigattn_bwd", "sigattn_softmax_bwd",
+            "sigattn_probe_mfma")
 
 
 class SigattnStrides(ctypes.Structure):
@@ -100,6 +101,8 @@ def load() -> ctypes.CDLL:
     lib.sigattn_bwd.argtypes = [ap, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.sigattn_softmax_bwd.argtypes = [ap, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bwd.restype = ctypes.c_int
+    lib.sigattn_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+    lib.sigattn_probe_mfma.restype = ctypes.c_int
     lib.sigattn_softmax_bwd.restype = ctypes.c_int
     for f in (lib.sigattn_softmax_fwd, lib.sigattn_softmax_bwd_prep, lib.sigattn_softmax_bwd_dq,
               lib.sigattn_softmax_bwd_dkdv, lib.sigattn_bwd_dkdv_dbias, lib.sigattn_bias_grad):
@@ -293,6 +296,36 @@ def bwd(q, k, v, dout, seqlens, dq=None, dk=None, dv=None, dbias=None, bias_rows
                "sigattn_bwd")
     del keep
     return (dq, dk, dv, dbias) if want else (dq, dk, dv)
+
+
+def probe_mfma(blocks=256, iters=20000, repeats=3):
+    """Measurement helper: sustained bf16 MFMA TFLOP/s of this GPU (best of
+    `repeats` timed launches of sigattn_probe_mfma) and the shader clock in
+    GHz during the last one."""
+    import torch
+
+    dev = torch.device("cuda", torch.cuda.current_device())
+    out = torch.empty(blocks * 1024, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    st = torch.cuda.current_stream(dev)
+    lib = load()
+
+    def launch():
+        _check(lib.sigattn_probe_mfma(blocks, iters, out.data_ptr(), clocks.data_ptr(), st.cuda_stream),
+               "sigattn_probe_mfma")
+    launch()
+    best = float("inf")
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        launch()
+        e1.record(st)
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    ticks, real = (int(x) for x in clocks.cpu())
+    flop = blocks * 16 * iters * 4 * 32768.0
+    return {"tflops": flop / (best * 1e-3) / 1e12, "ms": best, "shader_clock_ghz": ticks / real * 0.1 if real else None,
+            "blocks": blocks, "iters": iters}
 
 
 def bias_grad(dbias, seqlens, db=None, stream=None):

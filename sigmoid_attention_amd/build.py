@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libsigattn.so")
 ARCH = "gfx950"
 
 # (source, extra flags): the kernels are compiled once per element type.
-HIP_SOURCES = [("kernels.hip", []), ("kernels.hip", ["-DSIGATTN_FP16"])]
+HIP_SOURCES = [("kernels.hip", []), ("kernels.hip", ["-DSIGATTN_FP16"]), ("probe.hip", [])]
 CXX_SOURCES = ["api.cpp", "plan.cpp"]
 
 

@@ -519,6 +519,20 @@ sigattn_status sigattn_softmax_bwd_dkdv(const sigattn_args* a, const void* q, co
   });
 }
 
+sigattn_status sigattn_probe_mfma(int32_t blocks, int32_t iters, float* out, uint64_t* clocks, void* stream) {
+  if (!out || !clocks) return SIGATTN_ERR_NULL;
+  if ((uintptr_t)out % 4 || (uintptr_t)clocks % 8) return SIGATTN_ERR_ALIGN;
+  if (blocks < 1 || blocks > 65536 || iters < 1) return SIGATTN_ERR_SHAPE;
+  const uintptr_t ol = (uintptr_t)out, oh = ol + (uintptr_t)blocks * 1024 * 4;
+  const uintptr_t cl = (uintptr_t)clocks, ch = cl + 16;
+  if (ol < ch && cl < oh) return SIGATTN_ERR_ALIAS;
+  (void)hipGetLastError();
+  if (sigattn::launch_mfma_probe(blocks, iters, out, (unsigned long long*)clocks, (hipStream_t)stream) !=
+      hipSuccess)
+    return SIGATTN_ERR_HIP;
+  return SIGATTN_OK;
+}
+
 const char* sigattn_status_str(sigattn_status s) {
   switch (s) {
     case SIGATTN_OK: return "ok";

@@ -17,6 +17,10 @@ struct PrepArgs {
   int32_t sl[2];
 };
 
+// Measurement helper: `blocks` x 1024 threads of back-to-back bf16 MFMAs
+// (probe.hip).
+hipError_t launch_mfma_probe(int32_t blocks, int32_t iters, float* out, unsigned long long* clocks, hipStream_t st);
+
 namespace bf16 {
 #include "launch_decls.inc"
 }  // namespace bf16

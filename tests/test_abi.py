@@ -325,3 +325,14 @@ def test_fused_backward_checks():
     assert bwd_all(ah) == ALIAS
     lib = sa.load()
     assert lib.sigattn_softmax_bwd(ctypes.byref(a), P[0], P[1], P[2], P[3], None, P[5], P[6], P[7], 0) == NULL
+
+
+def test_probe_checks():
+    lib = sa.load()
+    assert lib.sigattn_probe_mfma(1, 1, None, P[1], None) == NULL
+    assert lib.sigattn_probe_mfma(1, 1, P[0], None, None) == NULL
+    assert lib.sigattn_probe_mfma(1, 1, P[0] + 2, P[1], None) == ALIGN
+    assert lib.sigattn_probe_mfma(1, 1, P[0], P[1] + 4, None) == ALIGN
+    assert lib.sigattn_probe_mfma(0, 1, P[0], P[1], None) == SHAPE
+    assert lib.sigattn_probe_mfma(1, 0, P[0], P[1], None) == SHAPE
+    assert lib.sigattn_probe_mfma(2, 1, P[0], P[0] + 4096, None) == ALIAS
