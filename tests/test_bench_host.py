@@ -1,0 +1,49 @@
+"""Host-side logic of bench.py (no GPU): the FLOP convention, the covered-tile
+count, the kernel-source hash that guards stored traffic counters, and the
+one-GPU rule."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_pair_flops_closed_forms():
+    # H d n^2 per sequence; causal: H d n (n + 1) / 2
+    assert bench.pair_flops([3, 5], 2, 64) == 2 * 64 * (9 + 25)
+    assert bench.pair_flops([3, 5], 2, 64, causal=True) == 2 * 64 * (6 + 15)
+    assert bench.pair_flops([0, 0], 4, 128) == 0.0
+
+
+def test_flop_units_sum_to_the_convention():
+    u = bench.KERNEL_FLOP_UNITS
+    assert u["fwd"] + u["bwd"] == 14            # 4 n^2 d forward + 10 n^2 d backward
+    assert u["bwd_dq"] + u["bwd_dkdv"] == u["bwd"]
+    for k, (fast, split) in bench.EXECUTED_UNITS.items():
+        assert fast >= u[k] and split >= fast
+
+
+def test_covered_pairs():
+    # 300 rows -> 3 tiles of 128 x 5 tiles of 64; 1 row -> 1 x 1; 0 rows -> none
+    assert bench.covered_pairs([300, 1, 0], 2, 128, 64) == 2 * (15 + 1)
+
+
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("int f() { return 1; }  // one\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(src))
+    h1 = bench.kernel_source_hash()
+    src.write_text("// a new comment\nint f() {\n  return 1;  // two\n}\n")
+    assert bench.kernel_source_hash() == h1
+    src.write_text("int f() { return 2; }\n")
+    assert bench.kernel_source_hash() != h1
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
