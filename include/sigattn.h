@@ -123,7 +123,9 @@ typedef enum sigattn_precision {
 typedef enum sigattn_pass {
   SIGATTN_PASS_FWD = 0,
   SIGATTN_PASS_BWD_DQ = 1,
-  SIGATTN_PASS_BWD_DKDV = 2
+  SIGATTN_PASS_BWD_DKDV = 2,
+  SIGATTN_PASS_BWD = 3       /* both backward sides, as sigattn_bwd runs them
+                                (sigattn_validate and sigattn_plan_stats)       */
 } sigattn_pass;
 
 /* Element strides of one tensor argument seen as [B, H, Lmax, d]: element
@@ -248,9 +250,11 @@ sigattn_status sigattn_softmax_bwd(const sigattn_args *args, const void *q, cons
 /* Runs every check the compute call for pass p would run (shape, lengths,
  * bias, precision, null pointers, alignment, strides, aliasing) on the
  * call's tensor arguments, given in argument order (fwd: q, k, v, o; dq: q,
- * k, v, dout, dq; dkdv: q, k, v, dout, dk, dv), and returns the status that
- * call would return, without enqueuing anything and without dereferencing the
- * tensor pointers.  For callers that want to vet a layout ahead of time. */
+ * k, v, dout, dq; dkdv: q, k, v, dout, dk, dv; SIGATTN_PASS_BWD: q, k, v,
+ * dout, dq, dk, dv, as sigattn_bwd without bias rows), and returns the status
+ * that call would return, without enqueuing anything and without
+ * dereferencing the tensor pointers.  For callers that want to vet a layout
+ * ahead of time. */
 sigattn_status sigattn_validate(const sigattn_args *args, int32_t pass, const void *const *tensors);
 
 /* Measurement helper, not part of the method: runs `blocks` workgroups of
@@ -273,8 +277,10 @@ const char *sigattn_status_str(sigattn_status status);
  * touching the GPU.  For pass p it reports the work items (one output tile
  * each), the (outer tile, inner tile) pairs those items visit — fully padded
  * tiles are not counted because they are never computed — and the number of
- * kernel launches.  Any of the output pointers may be NULL.  Validates
- * args (shape, seqlens, bias, precision) as the compute calls do. */
+ * kernel launches.  For SIGATTN_PASS_BWD: the dK/dV and dQ sides summed,
+ * and 1 launch when both sides fit one (the fused launch of sigattn_bwd).
+ * Any of the output pointers may be NULL.  Validates args (shape, seqlens,
+ * bias, precision) as the compute calls do. */
 sigattn_status sigattn_plan_stats(const sigattn_args *args, int32_t pass, int64_t *work_items,
                                   int64_t *tile_pairs, int32_t *launches);
 

@@ -19,7 +19,7 @@ _lib = None
 BIAS_MODES = {"seqlen": 0, "fixed_n": 1, "const": 2, "per_head": 3}
 PRECISIONS = {"fast": 0, "split": 1}
 DTYPES = {"bf16": 0, "fp16": 1}
-PASSES = {"fwd": 0, "bwd_dq": 1, "bwd_dkdv": 2}
+PASSES = {"fwd": 0, "bwd_dq": 1, "bwd_dkdv": 2, "bwd": 3}
 
 STATUS_NAMES = {
     0: "SIGATTN_OK", 1: "SIGATTN_ERR_NULL", 2: "SIGATTN_ERR_SHAPE", 3: "SIGATTN_ERR_SEQLEN",

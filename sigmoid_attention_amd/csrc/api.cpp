@@ -426,13 +426,14 @@ sigattn_status sigattn_bias_grad(const sigattn_args* a, const float* dbias, floa
 
 sigattn_status sigattn_validate(const sigattn_args* a, int32_t pass, const void* const* t) {
   int32_t o, i;
-  if (tile_rows(pass, &o, &i) != SIGATTN_OK) return SIGATTN_ERR_PASS;
+  if (pass != SIGATTN_PASS_BWD && tile_rows(pass, &o, &i) != SIGATTN_OK) return SIGATTN_ERR_PASS;
   sigattn_status s = check_args(a);
   if (s != SIGATTN_OK) return s;
   if (!t) return SIGATTN_ERR_NULL;
   const int nin = pass == SIGATTN_PASS_FWD ? 3 : 4;
-  const int nout = pass == SIGATTN_PASS_BWD_DKDV ? 2 : 1;
-  void* out[2] = {const_cast<void*>(t[nin]), nout == 2 ? const_cast<void*>(t[nin + 1]) : nullptr};
+  const int nout = pass == SIGATTN_PASS_BWD ? 3 : pass == SIGATTN_PASS_BWD_DKDV ? 2 : 1;
+  void* out[3] = {const_cast<void*>(t[nin]), nout >= 2 ? const_cast<void*>(t[nin + 1]) : nullptr,
+                  nout == 3 ? const_cast<void*>(t[nin + 2]) : nullptr};
   if ((s = check_ptrs(a, t, nin, out, nout)) != SIGATTN_OK) return s;
   return check_head_bias(a, t, nin + nout, nin);
 }
@@ -557,9 +558,18 @@ const char* sigattn_status_str(sigattn_status s) {
 sigattn_status sigattn_plan_stats(const sigattn_args* a, int32_t pass, int64_t* work_items, int64_t* tile_pairs,
                                   int32_t* launches) {
   int32_t o, i;
-  if (tile_rows(pass, &o, &i) != SIGATTN_OK) return SIGATTN_ERR_PASS;
+  if (pass != SIGATTN_PASS_BWD && tile_rows(pass, &o, &i) != SIGATTN_OK) return SIGATTN_ERR_PASS;
   const sigattn_status s = check_args(a);
   if (s != SIGATTN_OK) return s;
+  if (pass == SIGATTN_PASS_BWD) {  // both sides; one fused launch when each side fits one
+    sigattn::PlanStats sk, sq;
+    const size_t lk = sigattn::build_plan(plan_input(a, SIGATTN_PASS_BWD_DKDV), &sk).size();
+    const size_t lq = sigattn::build_plan(plan_input(a, SIGATTN_PASS_BWD_DQ), &sq).size();
+    if (work_items) *work_items = sk.items + sq.items;
+    if (tile_pairs) *tile_pairs = sk.pairs + sq.pairs;
+    if (launches) *launches = (lk == 1 && lq == 1) ? 1 : (int32_t)(lk + lq);
+    return SIGATTN_OK;
+  }
   sigattn::PlanStats st;
   const std::vector<Launch> plan = sigattn::build_plan(plan_input(a, pass), &st);
   if (work_items) *work_items = st.items;

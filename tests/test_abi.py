@@ -336,3 +336,18 @@ def test_probe_checks():
     assert lib.sigattn_probe_mfma(0, 1, P[0], P[1], None) == SHAPE
     assert lib.sigattn_probe_mfma(1, 0, P[0], P[1], None) == SHAPE
     assert lib.sigattn_probe_mfma(2, 1, P[0], P[0] + 4096, None) == ALIAS
+
+
+def test_fused_backward_pass_in_validate_and_plan_stats():
+    lens = (128, 77)
+    a, keep = args(lens=lens)
+    assert validate(a, 3, P[:7]) == OK
+    assert validate(a, 3, P[:4] + [P[4], P[4], P[6]]) == ALIAS     # dk on top of dq
+    assert validate(a, 3, P[:4] + [P[4], P[5], P[0]]) == ALIAS     # dv on top of q
+    kv = sa.plan_stats(2, 2, 128, 64, lens, "bwd_dkdv")
+    q = sa.plan_stats(2, 2, 128, 64, lens, "bwd_dq")
+    both = sa.plan_stats(2, 2, 128, 64, lens, "bwd")
+    assert both[0] == kv[0] + q[0] and both[1] == kv[1] + q[1] and both[2] == 1
+    many = list(np.random.default_rng(5).integers(0, 97, size=300))
+    assert sa.plan_stats(300, 1, 96, 64, many, "bwd")[2] == (sa.plan_stats(300, 1, 96, 64, many, "bwd_dkdv")[2]
+                                                              + sa.plan_stats(300, 1, 96, 64, many, "bwd_dq")[2])
