@@ -1,7 +1,7 @@
 """Benchmark: valid-token TFLOPS of sigmoid attention (forward + backward) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--precision fast|split|auto]
-                    [--sweep] [--no-cpu-baseline] [--cpu-seconds S] [--causal]
+                    [--quick] [--no-cpu-baseline] [--cpu-seconds S] [--causal]
                     [--bias seqlen|per_head] [--dtype bf16|fp16] [--layout bhld|blhd]
                     [--attn sigmoid|softmax] [--compare-softmax] [--layer] [--settle-ms MS] [--split-bwd]
 
@@ -16,9 +16,13 @@ the per-kernel durations and cost about 3 % of the step.  FLOPs are algorithmic 
 forward 4 n^2 d and backward 10 n^2 d per (sequence, head) — the FlashAttention
 convention; recomputation inside the backward kernels is not counted.
 
-Prints ONE JSON line.  With --sweep it also times the three padding-sweep
-workloads (0 / 25 / 50 % padding) and adds their TFLOPS and the time ratio
-against the covered-tile and valid-pair ratios under "padding_sweep".
+Prints ONE JSON line.  Besides the headline workload it carries, from the
+same run: "padding_sweep" (the three padding-sweep workloads at 0 / 25 / 50 %
+padding, forward-only and forward+backward TFLOPS, each time ratio against the
+covered-tile and valid-pair ratios, and the TFLOPS drop from 0 % to 25 %),
+and "workloads" (the dense 8K batch at head dim 128 and the 8K log-normal
+batch with x4 inputs in split precision, each with its roofline fraction and
+its dominant kernel's time).  --quick leaves both out.
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -282,6 +286,30 @@ def tflops(flops, ms):
     return flops / (ms * 1e-3) / 1e12
 
 
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo), the logical CPUs this
+    process may run on, and the threads the BLAS pool uses."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover - not Linux
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        blas = 1
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable, "blas_threads": int(blas)}
+
+
 def cpu_baseline(case, outputs, budget_s):
     """Time the CPU oracle (as it stands) on a bounded sample of the same
     workload: whole heads, cycling through the sequences longest first, until
@@ -290,11 +318,8 @@ def cpu_baseline(case, outputs, budget_s):
     import oracle
     from workloads import as_f64
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        cores = os.cpu_count()
+    hw = host_cpu()
+    cores = hw["blas_threads"]
     w = case["workload"]
     n = case["seqlens"]
     order = [int(b) for b in np.argsort(-np.asarray(n), kind="stable") if n[b] > 0]
@@ -317,6 +342,7 @@ def cpu_baseline(case, outputs, budget_s):
         "value": flops / secs / 1e12 if secs > 0 else None,
         "unit": "TFLOPS",
         "cores": int(cores),
+        **hw,
         "kind": "oracle",
         "sample": f"fp64 oracle forward+backward on {len(done)} of {w.B * w.H} heads of {w.name} "
                   f"(longest sequences first; lengths {sorted({x[2] for x in done}, reverse=True)}), "
@@ -331,6 +357,86 @@ def covered_pairs(seqlens, H, outer, inner):
     return int((H * -(-n // outer) * -(-n // inner)).sum())
 
 
+SWEEP = ("sweep_b16h16d64_l4096_pad00", "sweep_b16h16d64_l4096_pad25", "sweep_b16h16d64_l4096_pad50")
+# Workloads timed beside the headline in the default run: head dim 128 at 8K
+# (dense), and the 8K log-normal batch whose x4 inputs saturate sigma (split
+# precision).
+EXTRA = (("dense_b4h16d128_l8192", "fast"), ("cells8k_b8h12d64_l8192_x4", "split"))
+
+
+def workload_record(r, precision):
+    """Throughput of one timed workload (forward + fused backward) with the
+    roofline fraction of its dominant kernel."""
+    n = r["seqlens"]
+    w = r["workload"]
+    fwd_ms = r["kernel_avg_ms"]["fwd"]
+    bwd_ms = sum(v_ for k_, v_ in r["kernel_avg_ms"].items() if k_.startswith("bwd"))
+    timed = [k_ for k_ in KERNEL_FLOP_UNITS if k_ in r["kernel_avg_ms"]]
+    dom = max(timed, key=r["kernel_avg_ms"].get)
+    achieved = tflops(KERNEL_FLOP_UNITS[dom] * r["pair_flops"], r["kernel_avg_ms"][dom])
+    return {
+        "B": w.B, "H": w.H, "d": w.d, "Lmax": w.Lmax, "seqlens": [int(x) for x in n], "precision": precision,
+        "value": round(tflops(r["fwd_flops"] + r["bwd_flops"], r["step_ms"]), 2),
+        "ms_per_step": round(r["step_ms"], 5),
+        "fwd_tflops": round(tflops(r["fwd_flops"], fwd_ms), 2),
+        "bwd_tflops": round(tflops(r["bwd_flops"], bwd_ms), 2),
+        "kernel_avg_ms": {k_: round(v_, 5) for k_, v_ in r["kernel_avg_ms"].items()},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "avg_launch_ms": round(r["kernel_avg_ms"][dom], 5),
+                     "executed_mfma_frac": round(tflops(EXECUTED_UNITS[dom][precision == "split"] * r["pair_flops"],
+                                                        r["kernel_avg_ms"][dom]) / PEAK_BF16_TFLOPS, 4)},
+    }
+
+
+def padding_sweep(steps, settle_ms, attn="sigmoid", compare_softmax=False):
+    """The padding sweep (B16 H16 d64 Lmax 4096 at 0 / 25 / 50 % padding):
+    forward-only and forward+backward valid-token TFLOPS, the time ratios
+    against 0 % padding beside the covered-tile and valid-pair ratios (the
+    work the schedule skips), and the TFLOPS drop from 0 % to 25 %."""
+    import torch
+
+    sweep = {}
+    base = None
+    for sw in SWEEP:
+        rs = time_workload(sw, "fast", steps, 2, attn=attn, settle_ms=settle_ms)
+        ws = rs["workload"]
+        fwd_ms = rs["kernel_avg_ms"]["fwd"]
+        step_ms = rs["step_ms"]
+        if base is None:
+            base = (fwd_ms, step_ms)
+        dense_pairs = covered_pairs([ws.Lmax] * ws.B, ws.H, 128, 64)
+        cmp_ = {}
+        if compare_softmax:
+            rc = time_workload(sw, "fast", steps, 2, attn="softmax", settle_ms=settle_ms)
+            cmp_ = {"softmax_fwd_tflops": round(tflops(rc["fwd_flops"], rc["kernel_avg_ms"]["fwd"]), 2),
+                    "softmax_fwd_bwd_tflops": round(tflops(rc["fwd_flops"] + rc["bwd_flops"], rc["step_ms"]), 2),
+                    "sigmoid_fwd_speedup": round(rc["kernel_avg_ms"]["fwd"] / fwd_ms, 4),
+                    "sigmoid_step_speedup": round(rc["step_ms"] / step_ms, 4)}
+            del rc
+        sweep[sw] = {**cmp_,
+            "seqlens": [int(x) for x in rs["seqlens"]],
+            "padding": round(1 - float(np.sum(rs["seqlens"])) / (ws.B * ws.Lmax), 4),
+            "fwd_tflops": round(tflops(rs["fwd_flops"], fwd_ms), 2),
+            "fwd_bwd_tflops": round(tflops(rs["fwd_flops"] + rs["bwd_flops"], step_ms), 2),
+            "fwd_ms": round(fwd_ms, 5), "step_ms": round(step_ms, 5),
+            "fwd_time_ratio": round(fwd_ms / base[0], 4),
+            "step_time_ratio": round(step_ms / base[1], 4),
+            "covered_tile_ratio": round(covered_pairs(rs["seqlens"], ws.H, 128, 64) / dense_pairs, 4),
+            "valid_pair_ratio": round(float(np.sum(np.asarray(rs["seqlens"], np.float64) ** 2))
+                                      / (ws.B * ws.Lmax ** 2), 4),
+        }
+        del rs
+        torch.cuda.empty_cache()
+    p0, p25 = sweep[SWEEP[0]], sweep[SWEEP[1]]
+    sweep["tflops_drop_0_to_25"] = {
+        "fwd": round(1 - p25["fwd_tflops"] / p0["fwd_tflops"], 4),
+        "fwd_bwd": round(1 - p25["fwd_bwd_tflops"] / p0["fwd_bwd_tflops"], 4),
+        "tile_granularity_floor": round(1 - p25["valid_pair_ratio"] / p25["covered_tile_ratio"], 4),
+    }
+    return sweep
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,7 +444,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--precision", default="auto", choices=["auto", "fast", "split"])
-    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--quick", action="store_true",
+                    help="time the headline workload only (no padding sweep, no 8K workloads)")
     ap.add_argument("--attn", default="sigmoid", choices=["sigmoid", "softmax"],
                     help="time the softmax comparison path instead of sigmoid attention")
     ap.add_argument("--compare-softmax", action="store_true",
@@ -487,40 +594,18 @@ def main():
         "roofline": roofline,
     }
 
-    if a.sweep:
-        sweep = {}
-        base_ms = None
-        for sw in ("sweep_b16h16d64_l4096_pad00", "sweep_b16h16d64_l4096_pad25", "sweep_b16h16d64_l4096_pad50"):
-            rs = time_workload(sw, "fast", max(5, a.steps // 2), 2, attn=a.attn, settle_ms=a.settle_ms / 2)
-            ws = rs["workload"]
-            fwd_ms = rs["kernel_avg_ms"]["fwd"]
-            step_ms = rs["step_ms"]
-            if base_ms is None:
-                base_ms = (fwd_ms, step_ms)
-            dense_pairs = covered_pairs([ws.Lmax] * ws.B, ws.H, 128, 64)
-            if a.compare_softmax:
-                rc = time_workload(sw, "fast", max(5, a.steps // 2), 2, attn="softmax", settle_ms=a.settle_ms / 2)
-                cmp_ = {"softmax_fwd_tflops": round(tflops(rc["fwd_flops"], rc["kernel_avg_ms"]["fwd"]), 2),
-                        "softmax_fwd_bwd_tflops": round(tflops(rc["fwd_flops"] + rc["bwd_flops"], rc["step_ms"]), 2),
-                        "sigmoid_fwd_speedup": round(rc["kernel_avg_ms"]["fwd"] / fwd_ms, 4),
-                        "sigmoid_step_speedup": round(rc["step_ms"] / step_ms, 4)}
-                del rc
-            else:
-                cmp_ = {}
-            sweep[sw] = {**cmp_,
-                "seqlens": [int(x) for x in rs["seqlens"]],
-                "padding": round(1 - float(np.sum(rs["seqlens"])) / (ws.B * ws.Lmax), 4),
-                "fwd_tflops": round(tflops(rs["fwd_flops"], fwd_ms), 2),
-                "fwd_bwd_tflops": round(tflops(rs["fwd_flops"] + rs["bwd_flops"], step_ms), 2),
-                "fwd_time_ratio": round(fwd_ms / base_ms[0], 4),
-                "step_time_ratio": round(step_ms / base_ms[1], 4),
-                "covered_tile_ratio": round(covered_pairs(rs["seqlens"], ws.H, 128, 64) / dense_pairs, 4),
-                "valid_pair_ratio": round(float(np.sum(np.asarray(rs["seqlens"], np.float64) ** 2))
-                                          / (ws.B * ws.Lmax ** 2), 4),
-            }
-            del rs
-            torch.cuda.empty_cache()
-        out["padding_sweep"] = sweep
+    if not a.quick:
+        sub_steps, sub_settle = max(5, a.steps // 2), min(a.settle_ms, 200.0)
+        out["padding_sweep"] = padding_sweep(sub_steps, sub_settle, attn=a.attn, compare_softmax=a.compare_softmax)
+        if a.attn == "sigmoid" and not a.causal and a.bias == "seqlen" and a.layout == "bhld":
+            out["workloads"] = {}
+            for wn, prec in EXTRA:
+                if wn == name:
+                    continue
+                rx = time_workload(wn, prec, sub_steps, 2, dtype=a.dtype, settle_ms=sub_settle)
+                out["workloads"][wn] = workload_record(rx, prec)
+                del rx
+                torch.cuda.empty_cache()
 
     if a.compare_softmax and a.attn == "sigmoid":
         rc = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn="softmax", causal=a.causal,

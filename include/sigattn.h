@@ -109,14 +109,22 @@ typedef enum sigattn_bias_mode {
                                       sigattn_bwd_dkdv_dbias)                       */
 } sigattn_bias_mode;
 
-/* How P (forward, dV) and dX (dQ, dK) enter the second matrix product (in
- * the tensors' element type, written e16 below: bf16 or fp16). */
+/* Arithmetic of the sigmoid and of the second matrix products (the tensors'
+ * element type is written e16 below: bf16 or fp16).
+ *
+ * FAST is meant for the method's own regime, b = -ln n with scores of order
+ * one, where every weight is about 1/n: P (forward, dV) and dX (dQ, dK) are
+ * rounded once to e16, and the score scale log2(e)/sqrt(d) is folded into the
+ * operand each wave holds for its whole tile (rounded to e16 once), which
+ * saves one instruction per score.  Outside that regime - saturated scores
+ * (|x| >> 10, e.g. inputs scaled x4), or a constant bias near 0 so that many
+ * weights of order one sum - bf16 FAST exceeds |gpu - exact| <= 2e-2 (1 +
+ * |exact|) and SPLIT is required. */
 typedef enum sigattn_precision {
-  SIGATTN_PREC_FAST = 0,  /* rounded once to e16 (round-to-nearest-even)           */
-  SIGATTN_PREC_SPLIT = 1  /* as a pair hi = e16(x), lo = e16(x - hi): two products,
-                             ~16 (bf16) or ~22 (fp16) significant bits; needed with
-                             bf16 when scores saturate the sigmoid (|x| >> 10) and
-                             many small weights sum                               */
+  SIGATTN_PREC_FAST = 0,  /* P and dX rounded once to e16; prescaled scores          */
+  SIGATTN_PREC_SPLIT = 1  /* exact fp32 scores; P and dX as a pair hi = e16(x),
+                             lo = e16(x - hi): two products, ~16 (bf16) or ~22
+                             (fp16) significant bits                             */
 } sigattn_precision;
 
 /* Which pass sigattn_plan_stats describes. */

@@ -67,27 +67,23 @@ def head_forward(q, k, v, causal=False):
     return p @ v, row_logsumexp(x)
 
 
-def head_backward(q, k, v, do, delta=None, causal=False):
+def head_backward(q, k, v, do, causal=False):
     """dQ, dK, dV of l = sum(O * dO) on the valid rows, through the dense row
-    Jacobian of the softmax.  The row term sum_k P_ik dP_ik equals
-    rowsum(dO * O); `delta` (one value per row) replaces it, to model a
-    backward that forms it from a stored, rounded O."""
+    Jacobian of the softmax: dX = P (dP - sum_k P_ik dP_ik)."""
     s = 1.0 / math.sqrt(q.shape[1])
     x = _masked(s * (q @ k.T), causal)
     p = row_softmax(x)
     dv = p.T @ do
     dp = do @ v.T
-    row = np.sum(p * dp, axis=-1, keepdims=True) if delta is None else np.asarray(delta)[:, None]
+    row = np.sum(p * dp, axis=-1, keepdims=True)
     dx = p * (dp - row)
     return s * (dx @ k), s * (dx.T @ q), dv
 
 
-def attention(q, k, v, seqlens, do=None, round_o=None, causal=False):
+def attention(q, k, v, seqlens, do=None, causal=False):
     """Whole padded batch, float64 [B, H, Lmax, d] inputs.  Returns "o" and
     "lse" ([B, H, Lmax]) and, with do, "dq", "dk", "dv"; padded rows 0.
-    round_o: optional function applied to each head's O before the backward
-    forms its row term from it (rowsum(dO * round_o(O))).  causal: query i
-    sees keys 0..i only."""
+    causal: query i sees keys 0..i only."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -108,9 +104,6 @@ def attention(q, k, v, seqlens, do=None, round_o=None, causal=False):
             qv, kv, vv = q[bi, h, :n], k[bi, h, :n], v[bi, h, :n]
             out["o"][bi, h, :n], out["lse"][bi, h, :n] = head_forward(qv, kv, vv, causal)
             if do is not None:
-                delta = None
-                if round_o is not None:
-                    delta = np.sum(do[bi, h, :n] * round_o(out["o"][bi, h, :n]), axis=-1)
-                dq, dk, dv = head_backward(qv, kv, vv, do[bi, h, :n], delta, causal)
+                dq, dk, dv = head_backward(qv, kv, vv, do[bi, h, :n], causal)
                 out["dq"][bi, h, :n], out["dk"][bi, h, :n], out["dv"][bi, h, :n] = dq, dk, dv
     return out

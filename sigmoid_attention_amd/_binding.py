@@ -207,7 +207,11 @@ def fwd(q, k, v, seqlens: Sequence[int], o=None, bias_mode="seqlen", bias_arg=0.
     """O = sigma(Q K^T / sqrt(d) + b) V, padded rows of O zero (causal: query i
     sees keys 0..i).  Enqueued on the
     current stream (or `stream`); returns O (a new O is contiguous in `layout`
-    order)."""
+    order).
+
+    precision "fast" suits b = -ln n with scores of order one; "split" is
+    required when scores saturate the sigmoid (|x| >> 10) or the bias is near
+    0 (see sigattn_precision in include/sigattn.h)."""
     import torch
 
     if o is None:

@@ -78,6 +78,22 @@ __device__ __forceinline__ float sigmoid2(float score, float c1, float c2) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(score, c1, c2)));
 }
 
+// Fast precision folds c1 into the operand a wave holds in registers for its
+// whole item (rounded to the element type once per item), so the score
+// product yields u = c1 * score directly, and the bias enters as the factor
+// m = 2^c2 (e^-b): sigma = 1/(1 + 2^u * m), three VALU instructions per score
+// (exp, fma, rcp) where sigmoid2 needs four.  For u -> +inf the fma gives inf
+// and the reciprocal 0; for u -> -inf it gives 1; m is finite and positive, so
+// no NaN arises.  c2 is clamped to +-126 so that m stays a normal float: that
+// changes sigma only where |b| > 87, and there by less than 2^-126 e^|score|.
+__device__ __forceinline__ float sigmoid_pre(float u, float m) {
+  return __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_amdgcn_exp2f(u), m, 1.0f));
+}
+
+__device__ __forceinline__ float bias_factor(float c2) {
+  return __builtin_amdgcn_exp2f(__builtin_fminf(__builtin_fmaxf(c2, -126.0f), 126.0f));
+}
+
 // Round 8 floats to the element type (round-to-nearest-even,
 // v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
 __device__ __forceinline__ e16x8 to_e16x8(f32x8 x) { return __builtin_convertvector(x, e16x8); }
@@ -224,6 +240,17 @@ template <int D>
 __device__ __forceinline__ void load_bfrag(e16x8 (&f)[D / 16], const Slice& src, int row, int hf) {
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) f[s] = as_e16x8(src.load16(row * src.rs + 16 * s + 8 * hf));
+}
+
+// The same fragments multiplied by `scale` and rounded back to the element
+// type (round-to-nearest-even): the operand of the fast-precision score
+// product (see sigmoid_pre).
+template <int D>
+__device__ __forceinline__ void load_bfrag_scaled(e16x8 (&f)[D / 16], const Slice& src, int row, int hf,
+                                                  float scale) {
+  load_bfrag<D>(f, src, row, hf);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) f[s] = to_e16x8(to_f32x8(f[s]) * scale);
 }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

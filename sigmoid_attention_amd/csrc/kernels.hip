@@ -57,28 +57,38 @@ template <int D> struct FwdCfg { static constexpr bool LA = D != 64; static cons
 template <int D> struct DqCfg { static constexpr bool LA = true; static constexpr int OCC = D == 64 ? 2 : 1; };
 template <int D> struct DkdvCfg { static constexpr int BQ = 64; static constexpr int OCC = D == 64 ? 2 : 1; };
 
+// sigma of one score value: from the raw score with the bias term c2, or
+// (PRE, fast precision) from the prescaled score u with the bias factor m
+// (see sigmoid_pre).
+template <int D, bool PRE>
+__device__ __forceinline__ float sigma_of(float score, float arg) {
+  if constexpr (PRE) return sigmoid_pre(score, arg);
+  else return sigmoid2(score, score_c1<D>(), arg);
+}
+
 // sigma of the eight score values of K-chunk c, rounded to the element type
-// (hi) and, in split precision, the rounded remainder (lo).
-template <int D, bool SPLIT>
-__device__ __forceinline__ void sigmoid_chunk(const f32x16 (&sc)[2], int c, float c2, e16x8& hi, e16x8& lo) {
+// (hi) and, in split precision, the rounded remainder (lo).  arg: c2, or m
+// with PRE.
+template <int D, bool SPLIT, bool PRE>
+__device__ __forceinline__ void sigmoid_chunk(const f32x16 (&sc)[2], int c, float arg, e16x8& hi, e16x8& lo) {
   f32x8 p = chunk8(sc[c >> 1], c & 1);
 #pragma unroll
-  for (int t = 0; t < 8; ++t) p[t] = sigmoid2(p[t], score_c1<D>(), c2);
+  for (int t = 0; t < 8; ++t) p[t] = sigma_of<D, PRE>(p[t], arg);
   hi = to_e16x8(p);
   if (SPLIT) lo = to_e16x8(p - to_f32x8(hi));
 }
 
 // dS = dP * sigma * (1 - sigma) for K-chunk c (and optionally sigma itself;
 // with DSUM, the chunk's eight fp32 dS values are also added to *dsum).
-template <int D, bool SPLIT, bool WANT_P, bool DSUM = false, int NB>
-__device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[NB], const f32x16 (&dp)[NB], int c, float c2,
+template <int D, bool SPLIT, bool PRE, bool WANT_P, bool DSUM = false, int NB>
+__device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[NB], const f32x16 (&dp)[NB], int c, float arg,
                                                e16x8& dh, e16x8& dl, e16x8& ph, e16x8& pl,
                                                float* dsum = nullptr) {
   const f32x8 sv = chunk8(sc[c >> 1], c & 1), gv = chunk8(dp[c >> 1], c & 1);
   f32x8 p8, ds;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const float p = sigmoid2(sv[t], score_c1<D>(), c2);
+    const float p = sigma_of<D, PRE>(sv[t], arg);
     p8[t] = p;
     ds[t] = gv[t] * __builtin_fmaf(-p, p, p);  // dP * p (1 - p)
   }
@@ -93,29 +103,36 @@ __device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[NB], const f32
 }
 
 // Causal mask (query i sees keys 0..i), applied only in tiles that straddle
-// the diagonal; a score of -inf gives sigma = 0 (and dS = 0) and a softmax
-// weight of 0.
+// the diagonal.  `masked` is the score that gives weight 0: -inf for a raw
+// score (sigma = 0, dS = 0; softmax weight 0), +inf for a prescaled one
+// (u = c1 * score with c1 < 0).
 // S^T layout (keys in registers, the query is the lane's column): keys after
 // the lane's query.  key0 = first key of the tile.
-__device__ __forceinline__ void mask_causal_cols(f32x16 (&sc)[2], int key0, int qrow, int hf) {
+__device__ __forceinline__ void mask_causal_cols(f32x16 (&sc)[2], int key0, int qrow, int hf, float masked) {
   const int lim = qrow - key0 - 4 * hf;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (32 * b + 8 * (r >> 2) + (r & 3) > lim) sc[b][r] = -__builtin_inff();
+      if (32 * b + 8 * (r >> 2) + (r & 3) > lim) sc[b][r] = masked;
 }
 
 // S layout (queries in registers, the key is the lane's column): queries
 // before the lane's key.  q0 = first query of the tile.
 template <int NB>
-__device__ __forceinline__ void mask_causal_rows(f32x16 (&sc)[NB], int q0, int krow, int hf) {
+__device__ __forceinline__ void mask_causal_rows(f32x16 (&sc)[NB], int q0, int krow, int hf, float masked) {
   const int lim = krow - q0 - 4 * hf;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (32 * b + 8 * (r >> 2) + (r & 3) < lim) sc[b][r] = -__builtin_inff();
+      if (32 * b + 8 * (r >> 2) + (r & 3) < lim) sc[b][r] = masked;
+}
+
+// The masked score for a raw (PRE = false) or prescaled score.
+template <bool PRE>
+__device__ __forceinline__ constexpr float masked_score() {
+  return PRE ? __builtin_inff() : -__builtin_inff();
 }
 
 // ---------------------------------------------------------------------------
@@ -334,10 +351,12 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
   }
   Item it;
   if (!find_item(S, (int)blockIdx.x, it)) return;
+  constexpr bool PRE = !SPLIT;  // fast precision: prescaled scores (sigmoid_pre)
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c2 = item_c2(S, it);
+  const float sarg = PRE ? bias_factor(c2) : c2;
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BK, D> dma_k(w, lane, S.sl[1]), dma_v(w, lane, S.sl[2]);
@@ -348,7 +367,8 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
 
   const int qrow = it.tile * BQ + 32 * w + l32;
   e16x8 qf[D / 16];
-  load_bfrag<D>(qf, qs, qrow, hf);
+  if (PRE) load_bfrag_scaled<D>(qf, qs, qrow, hf, score_c1<D>());
+  else load_bfrag<D>(qf, qs, qrow, hf);
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
@@ -373,21 +393,21 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
     dma_v.load(vs, (j + 1) * BK, Vb((P + 1) % 2));
     const uint16_t* Kn = Kb(k1);
     const uint16_t* Vc = Vb(P % 2);
-    if (S.causal && j * BK + BK - 1 > q0w) mask_causal_cols(cur, j * BK, qrow, hf);
+    if (S.causal && j * BK + BK - 1 > q0w) mask_causal_cols(cur, j * BK, qrow, hf, masked_score<PRE>());
     zero2(nxt);
     e16x8 ph[4], pl[4];
     if (LA) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         score_steps<D>(nxt, Kn, qf, c * (D / 64), (c + 1) * (D / 64), fa);  // MFMA: tile j+1
-        sigmoid_chunk<D, SPLIT>(cur, c, c2, ph[c], pl[c]);                       // VALU: tile j
+        sigmoid_chunk<D, SPLIT, PRE>(cur, c, sarg, ph[c], pl[c]);              // VALU: tile j
         if (c > 0) value_chunk<D, SPLIT>(acc, tr, Vc, c - 1, ph[c - 1], pl[c - 1]);
       }
       value_chunk<D, SPLIT>(acc, tr, Vc, 3, ph[3], pl[3]);
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        sigmoid_chunk<D, SPLIT>(cur, c, c2, ph[c], pl[c]);
+        sigmoid_chunk<D, SPLIT, PRE>(cur, c, sarg, ph[c], pl[c]);
         if (c > 0) value_chunk<D, SPLIT>(acc, tr, Vc, c - 1, ph[c - 1], pl[c - 1]);
       }
       value_chunk<D, SPLIT>(acc, tr, Vc, 3, ph[3], pl[3]);
@@ -493,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_softmax_kernel(
     const uint16_t* Kn = Kb(k1);
     const uint16_t* Vc = Vb(P % 2);
     zero2(nxt);
-    if (S.causal && j * BK + BK - 1 > q0w) mask_causal_cols(cur, j * BK, qrow, hf);
+    if (S.causal && j * BK + BK - 1 > q0w) mask_causal_cols(cur, j * BK, qrow, hf, -__builtin_inff());
     if (j * BK + BK > n) mask_keys(cur, n - j * BK, hf);
     float mt = cur[0][0];
 #pragma unroll
@@ -559,10 +579,12 @@ __device__ __forceinline__ void dq_body(uint16_t* __restrict__ lds, int vb, cons
   }
   Item it;
   if (!find_item(S, vb, it)) return;
+  constexpr bool PRE = !SPLIT && !SOFTMAX;  // fast precision: prescaled scores (sigmoid_pre)
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c2 = item_c2(S, it);
+  const float sarg = PRE ? bias_factor(c2) : c2;
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BK, D> dma_k(w, lane, S.sl[1]), dma_v(w, lane, S.sl[2]);
@@ -573,7 +595,8 @@ __device__ __forceinline__ void dq_body(uint16_t* __restrict__ lds, int vb, cons
 
   const int qrow = it.tile * BQ + 32 * w + l32;
   e16x8 qf[D / 16], gf[D / 16];
-  load_bfrag<D>(qf, qs, qrow, hf);
+  if (PRE) load_bfrag_scaled<D>(qf, qs, qrow, hf, score_c1<D>());
+  else load_bfrag<D>(qf, qs, qrow, hf);
   load_bfrag<D>(gf, gs, qrow, hf);
   f32x16 acc[D / 32];
 #pragma unroll
@@ -607,7 +630,7 @@ __device__ __forceinline__ void dq_body(uint16_t* __restrict__ lds, int vb, cons
     const uint16_t* Kt = Kb(kc);
     const uint16_t* Kn = Kb(k1);
     const uint16_t* Vc = Vb(P % 2);
-    if (S.causal && j * BK + BK - 1 > q0w) mask_causal_cols(cur, j * BK, qrow, hf);
+    if (S.causal && j * BK + BK - 1 > q0w) mask_causal_cols(cur, j * BK, qrow, hf, masked_score<PRE>());
     f32x16 dp[2];
     zero2(dp);
     zero2(nxt);
@@ -619,7 +642,7 @@ __device__ __forceinline__ void dq_body(uint16_t* __restrict__ lds, int vb, cons
       if constexpr (SOFTMAX)
         dsoftmax_chunk_col<D, SPLIT>(cur, dp, c, lse2, dlt, dh[c], dl[c]);
       else
-        dsigmoid_chunk<D, SPLIT, false>(cur, dp, c, c2, dh[c], dl[c], unused_h, unused_l);
+        dsigmoid_chunk<D, SPLIT, PRE, false>(cur, dp, c, sarg, dh[c], dl[c], unused_h, unused_l);
       if (c > 0) value_chunk<D, SPLIT>(acc, tr, Kt, c - 1, dh[c - 1], dl[c - 1]);
     }
     value_chunk<D, SPLIT>(acc, tr, Kt, 3, dh[3], dl[3]);
@@ -683,10 +706,12 @@ __device__ __forceinline__ void dkdv_body(uint16_t* __restrict__ lds, float* __r
   }
   Item it;
   if (!find_item(S, vb, it)) return;
+  constexpr bool PRE = !SPLIT && !SOFTMAX;  // fast precision: prescaled scores (sigmoid_pre)
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c2 = item_c2(S, it);
+  const float sarg = PRE ? bias_factor(c2) : c2;
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BQ, D> dma_q(w, lane, S.sl[0]), dma_g(w, lane, S.sl[3]);
@@ -697,7 +722,8 @@ __device__ __forceinline__ void dkdv_body(uint16_t* __restrict__ lds, float* __r
 
   const int krow = it.tile * BKV + 32 * w + l32;
   e16x8 kf[D / 16], vf[D / 16];
-  load_bfrag<D>(kf, ks, krow, hf);
+  if (PRE) load_bfrag_scaled<D>(kf, ks, krow, hf, score_c1<D>());
+  else load_bfrag<D>(kf, ks, krow, hf);
   load_bfrag<D>(vf, vs, krow, hf);
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -743,7 +769,7 @@ __device__ __forceinline__ void dkdv_body(uint16_t* __restrict__ lds, float* __r
     dma_q.load(qs, (j + 2) * BQ, Qb(k2));
     dma_g.load(gs, (j + 2) * BQ, Gb(k2));
     row_load((j + 2) * BQ, k2);
-    if (S.causal && j * BQ < k0w + 31) mask_causal_rows(cs, j * BQ, krow, hf);
+    if (S.causal && j * BQ < k0w + 31) mask_causal_rows(cs, j * BQ, krow, hf, masked_score<PRE>());
     const uint16_t* Qn = Qb(k1);
     const uint16_t* Gn = Gb(k1);
     const uint16_t* Qt = Qb(kc);
@@ -768,7 +794,7 @@ __device__ __forceinline__ void dkdv_body(uint16_t* __restrict__ lds, float* __r
           const f32x8 dlt8 = cat8(*(const f32x4*)(lt + BQ + r0), *(const f32x4*)(lt + BQ + r0 + 8));
           dsoftmax_chunk_row<D, SPLIT>(cs, cd, c, lse8, dlt8, dh[c], dl[c], ph[c], pl[c]);
         } else {
-          dsigmoid_chunk<D, SPLIT, true, DB>(cs, cd, c, c2, dh[c], dl[c], ph[c], pl[c], &dsum);
+          dsigmoid_chunk<D, SPLIT, PRE, true, DB>(cs, cd, c, sarg, dh[c], dl[c], ph[c], pl[c], &dsum);
         }
         if (c > 0) {
           value_chunk_pre<D, SPLIT>(dv, ag[(c - 1) & 1], ph[c - 1], pl[c - 1]);

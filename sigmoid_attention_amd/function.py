@@ -88,6 +88,11 @@ def sigmoid_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens
     or beyond a sequence's length are ignored on input and zero on output (and
     in the gradients).  bias_mode / bias_arg / precision as in
     sigmoid_attention_amd.fwd.  causal: query i sees keys 0..i only.
+
+    precision: "fast" (default) suits the method's regime, b = -ln n with
+    scores of order one.  Scores that saturate the sigmoid (|x| >> 10, e.g.
+    large-norm queries and keys) or a bias near 0 need precision="split":
+    there "fast" exceeds the 2e-2 (1 + |exact|) error bound.
     bias_mode "per_head": bias_arg is a float32 tensor of H values on the
     device, b_h = bias_arg[h]; if it requires grad, its gradient (the sum of
     dX over each head's valid (query, key) pairs) is computed by the kernels.
@@ -151,6 +156,10 @@ class SigmoidAttention(torch.nn.Module):
     bias_mode "per_head" makes the bias a trained parameter, one value per
     head (`heads` of them, initialised to `bias_arg`, e.g. -ln of a typical
     length); its gradient comes from the kernels.
+
+    precision "fast" (default) is meant for b = -ln n and scores of order
+    one; use precision="split" when scores saturate the sigmoid (|x| >> 10)
+    or the bias is near 0, where "fast" exceeds the 2e-2 (1 + |exact|) bound.
     """
 
     def __init__(self, layout: str = "blhd", bias_mode: str = "seqlen", bias_arg: float = 0.0,

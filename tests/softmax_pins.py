@@ -148,13 +148,23 @@ ALL_PINS = [pin_unit_values_give_ones, pin_zero_query_is_mean_of_values, pin_sin
 
 
 def pin_row_term_identity(O):
-    """sum_k P_ik dP_ik = rowsum(dO * O): passing the exact O as the rounding
-    function changes no gradient."""
-    q, k, v, do = _rand(11, 1, 2, 6, 4)
-    a = O.attention(q, k, v, [6], do=do)
-    b = O.attention(q, k, v, [6], do=do, round_o=lambda x: x)
-    for key in ("dq", "dk", "dv"):
-        assert np.allclose(a[key], b[key], atol=1e-13), key
+    """sum_k P_ik dP_ik = rowsum(dO_i * O_i) (O_i = sum_k P_ik V_k): the row
+    term of the softmax Jacobian computed by scalar loops from the weights
+    equals the one formed from the oracle's O; and the oracle's dQ row i is
+    s * sum_j P_ij (dP_ij - that term) K_j, also by scalar loops."""
+    q, k, v, do = _rand(11, 1, 1, 6, 4)
+    out = O.attention(q, k, v, [6], do=do)
+    d = 4
+    for i in range(6):
+        s = [sum(q[0, 0, i, c] * k[0, 0, j, c] for c in range(d)) / math.sqrt(d) for j in range(6)]
+        z = sum(math.exp(x) for x in s)
+        p = [math.exp(x) / z for x in s]
+        dp = [sum(do[0, 0, i, c] * v[0, 0, j, c] for c in range(d)) for j in range(6)]
+        row = sum(p[j] * dp[j] for j in range(6))
+        assert abs(row - float(np.sum(do[0, 0, i] * out["o"][0, 0, i]))) < 1e-12
+        for c in range(d):
+            ref = sum(p[j] * (dp[j] - row) * k[0, 0, j, c] for j in range(6)) / math.sqrt(d)
+            assert abs(out["dq"][0, 0, i, c] - ref) < 1e-12
 
 
 ALL_PINS.append(pin_row_term_identity)

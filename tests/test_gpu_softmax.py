@@ -29,17 +29,9 @@ def run(case, precision="fast"):
     return {"o": o, "lse2": lse2, "dq": dq, "dk": dk, "dv": dv}
 
 
-def bf16_round(x):
-    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
-
-
-def compare(case, got, label, stored_o=False):
-    """stored_o: the reference backward forms rowsum(dO * O) from the oracle's
-    own O rounded to bf16, as a backward working from the stored output must
-    (FlashAttention-2's formulation); where scores saturate, the rounding of O
-    dominates dS = P (dP - delta) because P is nearly one-hot and dP ~ delta."""
+def compare(case, got, label):
     ref = softmax_oracle.attention(host(case["q"]), host(case["k"]), host(case["v"]), case["seqlens"],
-                                   do=host(case["do"]), round_o=bf16_round if stored_o else None)
+                                   do=host(case["do"]))
     ref["lse2"] = ref.pop("lse") * LOG2E
     ratios = {k: worst_ratio(host(got[k]), ref[k]) for k in ref}
     print(f"[softmax] {label} ratios={ratios}", flush=True)
@@ -67,8 +59,10 @@ def test_softmax_edge_cases(shape, precision):
     compare(case, run(case, precision), f"{shape} {precision}")
 
 
-def test_softmax_saturated_scores():
-    """x4 inputs: rows dominated by a few keys.  The backward forms
+def test_softmax_saturated_scores_bound_widened_for_stored_o():
+    """x4 inputs: rows dominated by a few keys.  This is the one test held to
+    a bound wider than 2e-2 (1 + |oracle|): dQ and dK add the term below.
+    The backward forms
     delta = rowsum(dO * O) from the stored bf16 O (FlashAttention-2's
     formulation); with P nearly one-hot, dP - delta cancels and that rounding
     dominates dS.  The bound adds its propagation: |d delta_i| <=

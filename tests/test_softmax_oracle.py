@@ -19,10 +19,10 @@ MUTATIONS = {
     "scale_dropped": ("x = _masked((q @ k.T) / math.sqrt(q.shape[1]), causal)", "x = _masked((q @ k.T), causal)"),
     "pv_transposed": ("return p @ v, row_logsumexp(x)", "return p.T @ v, row_logsumexp(x)"),
     "jacobian_row_term_dropped": ("dx = p * (dp - row)", "dx = p * dp"),
-    "jacobian_wrong_axis": ("row = np.sum(p * dp, axis=-1, keepdims=True) if delta",
-                            "row = np.sum(p * dp, axis=0, keepdims=True) if delta"),
-    "row_term_from_dp_only": ("delta = np.sum(do[bi, h, :n] * round_o(out[\"o\"][bi, h, :n]), axis=-1)",
-                              "delta = np.sum(do[bi, h, :n], axis=-1)"),
+    "jacobian_wrong_axis": ("row = np.sum(p * dp, axis=-1, keepdims=True)",
+                            "row = np.sum(p * dp, axis=0, keepdims=True)"),
+    "row_term_from_dp_only": ("row = np.sum(p * dp, axis=-1, keepdims=True)",
+                              "row = np.sum(dp, axis=-1, keepdims=True)"),
     "dv_not_transposed": ("dv = p.T @ do", "dv = p @ do"),
     "dk_uses_k": ("return s * (dx @ k), s * (dx.T @ q), dv", "return s * (dx @ k), s * (dx.T @ k), dv"),
     "causal_mask_transposed": ("np.where(np.tril(np.ones((n, n))) > 0, x, -np.inf)", "np.where(np.triu(np.ones((n, n))) > 0, x, -np.inf)"),
