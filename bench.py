@@ -20,9 +20,11 @@ Prints ONE JSON line.  Besides the headline workload it carries, from the
 same run: "padding_sweep" (the three padding-sweep workloads at 0 / 25 / 50 %
 padding, forward-only and forward+backward TFLOPS, each time ratio against the
 covered-tile and valid-pair ratios, and the TFLOPS drop from 0 % to 25 %),
-and "workloads" (the dense 8K batch at head dim 128 and the 8K log-normal
+"workloads" (the dense 8K batch at head dim 128 and the 8K log-normal
 batch with x4 inputs in split precision, each with its roofline fraction and
-its dominant kernel's time).  --quick leaves both out.
+its dominant kernel's time) and "short_sequences" (equal work as 4 sequences
+of 4096, 1024 of 256 or 4096 of 128, with launches per pass and the slowdown
+of the short cells).  --quick leaves them out.
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -362,6 +364,9 @@ SWEEP = ("sweep_b16h16d64_l4096_pad00", "sweep_b16h16d64_l4096_pad25", "sweep_b1
 # (dense), and the 8K log-normal batch whose x4 inputs saturate sigma (split
 # precision).
 EXTRA = (("dense_b4h16d128_l8192", "fast"), ("cells8k_b8h12d64_l8192_x4", "split"))
+# Equal work per head cut into few long or many short sequences: the schedule
+# keeps every pass one launch, and the TFLOPS ratio shows what short items cost.
+SHORT = ("few_b4h16d64_l4096", "many_b1024h16d64_l256", "many_b4096h16d64_l128")
 
 
 def workload_record(r, precision):
@@ -606,6 +611,21 @@ def main():
                 out["workloads"][wn] = workload_record(rx, prec)
                 del rx
                 torch.cuda.empty_cache()
+            short = {}
+            for wn in SHORT:
+                rx = time_workload(wn, "fast", sub_steps, 2, dtype=a.dtype, settle_ms=sub_settle)
+                rec = workload_record(rx, "fast")
+                ws = rx["workload"]
+                rec.pop("seqlens")
+                rec["launches_per_pass"] = {p_: int(sa.plan_stats(ws.B, ws.H, ws.Lmax, ws.d, rx["seqlens"], p_)[2])
+                                            for p_ in ("fwd", "bwd")}
+                short[wn] = rec
+                del rx
+                torch.cuda.empty_cache()
+            for wn in SHORT[1:]:
+                short[wn]["slowdown_vs_" + SHORT[0]] = {
+                    k_: round(short[SHORT[0]][k_] / short[wn][k_], 4) for k_ in ("value", "fwd_tflops", "bwd_tflops")}
+            out["short_sequences"] = short
 
     if a.compare_softmax and a.attn == "sigmoid":
         rc = time_workload(name, precision, a.steps, a.warmup, layout=a.layout, attn="softmax", causal=a.causal,

@@ -284,8 +284,9 @@ sigattn_status run_bwd(const sigattn_args* a, const void* const* t, const float*
   const hipStream_t st = (hipStream_t)a->stream;
   const auto impl_fused = f16(a) ? sigattn::f16::launch_bwd_fused : sigattn::bf16::launch_bwd_fused;
   (void)hipGetLastError();
-  if (pk.size() == 1 && pq.size() == 1) {
-    sigattn::BwdSched P;  // ~7 KB, copied into the launch's kernel arguments
+  if (pk.size() == 1 && pq.size() == 1 && pk[0].T.b_base == pq[0].T.b_base && pk[0].T.nseq == pq[0].T.nseq) {
+    sigattn::BwdSched P;  // 14.5 KB, copied into the launch's kernel arguments
+    P.T = pk[0].T;
     P.kv = pk[0].sched;
     P.dq = pq[0].sched;
     P.dq_off = (pk[0].blocks + 7) / 8 * 8;

@@ -316,42 +316,96 @@ struct FragAddr {
 // two writers.
 // vb: the workgroup's block index within this schedule's part of the grid.
 template <int D>
-__device__ __forceinline__ void zero_padded_rows(const Sched& S, int vb, uint16_t* __restrict__ o1, int t1,
-                                                 uint16_t* __restrict__ o2, int t2,
-                                                 float* __restrict__ rows = nullptr) {
+__device__ __forceinline__ void zero_padded_rows(const SeqTable& T, const Sched& S, int vb,
+                                                 uint16_t* __restrict__ o1, int t1, uint16_t* __restrict__ o2,
+                                                 int t2, float* __restrict__ rows = nullptr) {
   const int zb = vb - S.compute_blocks;
-  const int bhl = zb / kZeroSplit, part = zb % kZeroSplit;
-  const int bl = bhl / S.H;
-  if (bl >= S.zero_nseq) return;
-  const int n = S.zero_n[bl];
-  const int bh = (S.zero_b0 + bl) * S.H + (bhl - bl * S.H);
+  const int split = S.zero_split;
+  const int shl = zb / split, part = zb - shl * split;
+  const int sl = shl / S.H;
+  if (sl >= S.zero_nseq) return;
+  const int n = table_n(T, sl);
+  const int bh = (T.b_base + sl) * S.H + (shl - sl * S.H);
   uint16_t* p1 = slice_base(o1, S, bh, t1);
   uint16_t* p2 = o2 ? slice_base(o2, S, bh, t2) : nullptr;
   const int rs1 = S.sl[t1], rs2 = o2 ? S.sl[t2] : 0;
   const int chunks = (S.Lmax - n) * (D / 8);
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (int c = part * (int)blockDim.x + (int)threadIdx.x; c < chunks; c += kZeroSplit * (int)blockDim.x) {
+  for (int c = part * (int)blockDim.x + (int)threadIdx.x; c < chunks; c += split * (int)blockDim.x) {
     const int row = n + c / (D / 8), col = 8 * (c % (D / 8));
     *(u32x4*)(p1 + (size_t)row * rs1 + col) = z;
     if (o2) *(u32x4*)(p2 + (size_t)row * rs2 + col) = z;
   }
   // a per-row fp32 output, contiguous [B, H, Lmax] (the softmax lse2)
   if (rows)
-    for (int row = n + part * (int)blockDim.x + (int)threadIdx.x; row < S.Lmax; row += kZeroSplit * (int)blockDim.x)
+    for (int row = n + part * (int)blockDim.x + (int)threadIdx.x; row < S.Lmax; row += split * (int)blockDim.x)
       rows[(size_t)bh * S.Lmax + row] = 0.0f;
 }
 
-// -b log2(e) for the item's (sequence, head): from the schedule, or for a
-// per-head bias from the values in device memory (a uniform scalar load).
+// -b log2(e) for the item's (sequence, head): log2(n) for b = -ln n, the
+// schedule's constant, or from the per-head values in device memory (a
+// uniform scalar load).
 __device__ __forceinline__ float item_c2(const Sched& S, const Item& it) {
-  return S.head_bias ? -1.4426950408889634f * S.head_bias[it.bh % S.H] : it.c2;
+  if (S.bias_kind == 0) return __builtin_amdgcn_logf((float)it.n);
+  if (S.bias_kind == 1) return S.c2_const;
+  return -1.4426950408889634f * S.head_bias[it.bh % S.H];
+}
+
+// The bias factor m = 2^c2 = e^-b of the prescaled sigmoid (sigmoid_pre): for
+// b = -ln n exactly n.
+__device__ __forceinline__ float item_bias_factor(const Sched& S, const Item& it, float c2) {
+  return S.bias_kind == 0 ? (float)it.n : bias_factor(c2);
 }
 
 // Work item of block vb of this schedule's part of the grid (see plan.h);
 // false for idle blocks.  Uniform across the workgroup.  A part starts at a
 // multiple of 8, so vb & 7 is still the block's XCD.
-__device__ __forceinline__ bool find_item(const Sched& S, int vb, Item& it) {
-  return decode_item(S, (int32_t)(vb & 7), (int32_t)(vb >> 3), it);
+// The same result as decode_item; the walk over a piece's sequences reads
+// their lengths eight (or four, for 32-bit lengths) at a time with one
+// 16-byte scalar load, so a piece of 64 short sequences costs 8 dependent
+// loads rather than 64.
+__device__ __forceinline__ bool find_item(const SeqTable& T, const Sched& S, int vb, Item& it) {
+  const int32_t x = vb & 7, j = vb >> 3;
+  if (j >= S.xcd_items[x]) return false;
+  int32_t lo = S.xcd_begin[x], hi = S.xcd_begin[x + 1] - 1;
+  while (lo < hi) {  // last piece whose first list position is <= j
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (S.item0[mid] <= j) lo = mid;
+    else hi = mid - 1;
+  }
+  const int32_t i = j - S.item0[lo];
+  const int32_t ns = S.ns[lo], nh = S.nh[lo];
+  int32_t s = S.s0[lo], nt = S.nt[lo], t0 = S.t0[lo], r = i;
+  if (ns > 1) {
+    const int32_t send = s + ns - 1;
+    const int per = T.wide ? 4 : 8;  // lengths per 16-byte word
+    bool found = false;
+    for (int32_t g = s - s % per; !found; g += per) {
+      const u32x4 w = *(const u32x4*)(T.wide ? (const void*)&T.n32[g] : (const void*)&T.n16[g]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (e >= per) break;
+        const int32_t q = g + e;
+        if (found || q < s) continue;
+        const int32_t nq = T.wide ? (int32_t)w[e] : (int32_t)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        const int32_t tiles = (nq + S.outer_rows - 1) / S.outer_rows;
+        if (r < nh * tiles || q == send) {
+          s = q;
+          nt = tiles;
+          found = true;
+        } else {
+          r -= nh * tiles;
+        }
+      }
+    }
+    t0 = 0;
+  }
+  const int32_t hoff = r / nt;
+  it.s = s;
+  it.n = ns > 1 ? table_n(T, s) : S.n1[lo];
+  it.bh = (T.b_base + s) * S.H + S.h0[lo] + hoff;
+  it.tile = t0 + (r - hoff * nt);
+  return true;
 }
 
 }  // namespace SIGATTN_ELT

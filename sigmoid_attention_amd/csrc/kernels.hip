@@ -54,8 +54,19 @@ constexpr int kInner = 64;  // rows per inner tile
 // d = 128 the forward fits lookahead and two waves per SIMD (1.43x faster
 // than one wave per SIMD on the dense 8K batch).
 template <int D> struct FwdCfg { static constexpr bool LA = D != 64; static constexpr int OCC = D == 64 ? 4 : 2; };
-template <int D> struct DqCfg { static constexpr bool LA = true; static constexpr int OCC = D == 64 ? 2 : 1; };
-template <int D> struct DkdvCfg { static constexpr int BQ = 64; static constexpr int OCC = D == 64 ? 2 : 1; };
+// At d = 128 (one wave per SIMD, no other wave to overlap with) both backward
+// kernels compute the next tile's S and dP inside the chunk loop, with every
+// LDS fragment read issued a chunk ahead: DPLA in dQ, ROLL in dK/dV.
+template <int D> struct DqCfg {
+  static constexpr bool LA = true;
+  static constexpr bool DPLA = D == 128;
+  static constexpr int OCC = D == 64 ? 2 : 1;
+};
+template <int D> struct DkdvCfg {
+  static constexpr int BQ = 64;
+  static constexpr int OCC = D == 64 ? 2 : 1;
+  static constexpr bool ROLL = D == 128;
+};
 
 // sigma of one score value: from the raw score with the bias term c2, or
 // (PRE, fast precision) from the prescaled score u with the bias factor m
@@ -127,6 +138,14 @@ __device__ __forceinline__ void mask_causal_rows(f32x16 (&sc)[NB], int q0, int k
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       if (32 * b + 8 * (r >> 2) + (r & 3) < lim) sc[b][r] = masked;
+}
+
+// The same for one 32-row block of S whose first query is qb0.
+__device__ __forceinline__ void mask_causal_block(f32x16& sc, int qb0, int krow, int hf, float masked) {
+  const int lim = krow - qb0 - 4 * hf;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (8 * (r >> 2) + (r & 3) < lim) sc[r] = masked;
 }
 
 // The masked score for a raw (PRE = false) or prescaled score.
@@ -341,22 +360,22 @@ template <int D, bool SPLIT, bool LA = FwdCfg<D>::LA>
 __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uint16_t* __restrict__ Q,
                                                                         const uint16_t* __restrict__ K,
                                                                         const uint16_t* __restrict__ V,
-                                                                        uint16_t* __restrict__ O, const Sched S) {
+                                                                        uint16_t* __restrict__ O, const SeqTable T, const Sched S) {
   constexpr int BQ = 128, BK = kInner, TILE = BK * D;
   __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
 
   if ((int)blockIdx.x >= S.compute_blocks) {
-    zero_padded_rows<D>(S, (int)blockIdx.x, O, 3, nullptr, 0);
+    zero_padded_rows<D>(T, S, (int)blockIdx.x, O, 3, nullptr, 0);
     return;
   }
   Item it;
-  if (!find_item(S, (int)blockIdx.x, it)) return;
+  if (!find_item(T, S, (int)blockIdx.x, it)) return;
   constexpr bool PRE = !SPLIT;  // fast precision: prescaled scores (sigmoid_pre)
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c2 = item_c2(S, it);
-  const float sarg = PRE ? bias_factor(c2) : c2;
+  const float sarg = PRE ? item_bias_factor(S, it, c2) : c2;
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BK, D> dma_k(w, lane, S.sl[1]), dma_v(w, lane, S.sl[2]);
@@ -463,16 +482,16 @@ __device__ __forceinline__ void mask_keys(f32x16 (&sc)[2], int nv, int hf) {
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_softmax_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, const Sched S) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, const SeqTable T, const Sched S) {
   constexpr int BQ = 128, BK = kInner, TILE = BK * D;
   __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
 
   if ((int)blockIdx.x >= S.compute_blocks) {
-    zero_padded_rows<D>(S, (int)blockIdx.x, O, 3, nullptr, 0, LSE);
+    zero_padded_rows<D>(T, S, (int)blockIdx.x, O, 3, nullptr, 0, LSE);
     return;
   }
   Item it;
-  if (!find_item(S, (int)blockIdx.x, it)) return;
+  if (!find_item(T, S, (int)blockIdx.x, it)) return;
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -570,21 +589,21 @@ __device__ __forceinline__ void dq_body(uint16_t* __restrict__ lds, int vb, cons
                                         const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                         const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ,
                                         const float* __restrict__ LSE, const float* __restrict__ DELTA,
-                                        const Sched& S) {
+                                        const SeqTable& T, const Sched& S) {
   constexpr int BQ = 128, BK = kInner, TILE = BK * D;
 
   if (vb >= S.compute_blocks) {
-    zero_padded_rows<D>(S, vb, dQ, 4, nullptr, 0);
+    zero_padded_rows<D>(T, S, vb, dQ, 4, nullptr, 0);
     return;
   }
   Item it;
-  if (!find_item(S, vb, it)) return;
+  if (!find_item(T, S, vb, it)) return;
   constexpr bool PRE = !SPLIT && !SOFTMAX;  // fast precision: prescaled scores (sigmoid_pre)
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c2 = item_c2(S, it);
-  const float sarg = PRE ? bias_factor(c2) : c2;
+  const float sarg = PRE ? item_bias_factor(S, it, c2) : c2;
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BK, D> dma_k(w, lane, S.sl[1]), dma_v(w, lane, S.sl[2]);
@@ -611,6 +630,78 @@ __device__ __forceinline__ void dq_body(uint16_t* __restrict__ lds, int vb, cons
 
   const int nk = S.causal ? min((n + BK - 1) / BK, causal_inner_end(it.tile, BQ, BK)) : (n + BK - 1) / BK;
   const int q0w = it.tile * BQ + 32 * w;  // this wave's first query
+  if constexpr (DqCfg<D>::DPLA) {
+    // S^T and dP^T of tile j are both computed during step j-1, spread over
+    // its chunks with their A fragments read at the start of each chunk, so
+    // every chunk mixes the next tile's score products, the VALU work on this
+    // tile and this tile's dQ products.  K: 3 stages (tile j for dQ, j+1 for
+    // scores, j+2 loading); V: 2 stages (j+1 for dP, j+2 loading).
+    constexpr int KSQ = D / 64;  // score K-steps per chunk
+    dma_k.load(ks, 0, Kb(0));
+    dma_k.load(ks, BK, Kb(1));
+    dma_v.load(vs, 0, Vb(0));
+    dma_v.load(vs, BK, Vb(1));
+    vm_drain();
+    __syncthreads();
+    f32x16 sA[2], sB[2], gA[2], gB[2];
+    zero2(sA);
+    zero2(gA);
+    score_steps<D>(sA, Kb(0), qf, 0, D / 16, fa);
+    score_steps<D>(gA, Vb(0), gf, 0, D / 16, fa);
+    auto step = [&](auto phase, int j) {
+      constexpr int P = decltype(phase)::value;
+      constexpr int kc = P % 3, k1 = (P + 1) % 3, k2 = (P + 2) % 3;
+      f32x16(&cur)[2] = pick<P>(sA, sB);
+      f32x16(&nxt)[2] = pick<P + 1>(sA, sB);
+      f32x16(&dp)[2] = pick<P>(gA, gB);
+      f32x16(&dnx)[2] = pick<P + 1>(gA, gB);
+      dma_k.load(ks, (j + 2) * BK, Kb(k2));     // stage of K tile j-1 (its dQ reads ended at the last barrier)
+      dma_v.load(vs, (j + 2) * BK, Vb(P % 2));  // stage of V tile j (read during step j-1)
+      const uint16_t* Kt = Kb(kc);
+      const uint16_t* Kn = Kb(k1);
+      const uint16_t* Vn = Vb((P + 1) % 2);
+      if (S.causal && j * BK + BK - 1 > q0w) mask_causal_cols(cur, j * BK, qrow, hf, masked_score<PRE>());
+      e16x8 dh[4], dl[4], unused_h, unused_l;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        e16x8 fs[KSQ][2], fg[KSQ][2], tq[D / 32];
+#pragma unroll
+        for (int k = 0; k < KSQ; ++k)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            fs[k][mb] = fa.read(Kn, mb, c * KSQ + k);
+            fg[k][mb] = fa.read(Vn, mb, c * KSQ + k);
+          }
+        if (c > 0) read_value_frags<D>(tq, tr, Kt, c - 1);
+        sched_fence();
+        if constexpr (SOFTMAX)
+          dsoftmax_chunk_col<D, SPLIT>(cur, dp, c, lse2, dlt, dh[c], dl[c]);
+        else
+          dsigmoid_chunk<D, SPLIT, PRE, false>(cur, dp, c, sarg, dh[c], dl[c], unused_h, unused_l);
+        if (c == 0) {
+          zero2(nxt);
+          zero2(dnx);
+        }
+#pragma unroll
+        for (int k = 0; k < KSQ; ++k)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            nxt[mb] = mfma(fs[k][mb], qf[c * KSQ + k], nxt[mb]);
+            dnx[mb] = mfma(fg[k][mb], gf[c * KSQ + k], dnx[mb]);
+          }
+        if (c > 0) value_chunk_pre<D, SPLIT>(acc, tq, dh[c - 1], dl[c - 1]);
+        sched_fence();
+      }
+      {
+        e16x8 tq[D / 32];
+        read_value_frags<D>(tq, tr, Kt, 3);
+        value_chunk_pre<D, SPLIT>(acc, tq, dh[3], dl[3]);
+      }
+      vm_drain();
+      __syncthreads();
+    };
+    run_steps(nk, step);
+  } else {
   dma_k.load(ks, 0, Kb(0));
   dma_k.load(ks, BK, Kb(1));
   dma_v.load(vs, 0, Vb(0));
@@ -650,6 +741,7 @@ __device__ __forceinline__ void dq_body(uint16_t* __restrict__ lds, int vb, cons
     __syncthreads();
   };
   run_steps(nk, step);
+  }
 
   if (qrow < n) {
     const float scale = S.out_scale;
@@ -665,9 +757,9 @@ template <int D, bool SPLIT, bool SOFTMAX = false>
 __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, const float* __restrict__ LSE,
-    const float* __restrict__ DELTA, const Sched S) {
+    const float* __restrict__ DELTA, const SeqTable T, const Sched S) {
   __shared__ __align__(16) uint16_t lds[dq_lds_elems<D>()];
-  dq_body<D, SPLIT, SOFTMAX>(lds, (int)blockIdx.x, Q, K, V, dO, dQ, LSE, DELTA, S);
+  dq_body<D, SPLIT, SOFTMAX>(lds, (int)blockIdx.x, Q, K, V, dO, dQ, LSE, DELTA, T, S);
 }
 
 // ---------------------------------------------------------------------------
@@ -697,21 +789,21 @@ __device__ __forceinline__ void dkdv_body(uint16_t* __restrict__ lds, float* __r
                                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                                           uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                                           const float* __restrict__ LSE, const float* __restrict__ DELTA,
-                                          float* __restrict__ DBIAS, const Sched& S) {
+                                          float* __restrict__ DBIAS, const SeqTable& T, const Sched& S) {
   constexpr int BKV = 128, BQ = DkdvCfg<D>::BQ, TILE = BQ * D, NMB = BQ / 32, NC = BQ / 16;
 
   if (vb >= S.compute_blocks) {
-    zero_padded_rows<D>(S, vb, dK, 4, dV, 5, DB ? DBIAS : nullptr);
+    zero_padded_rows<D>(T, S, vb, dK, 4, dV, 5, DB ? DBIAS : nullptr);
     return;
   }
   Item it;
-  if (!find_item(S, vb, it)) return;
+  if (!find_item(T, S, vb, it)) return;
   constexpr bool PRE = !SPLIT && !SOFTMAX;  // fast precision: prescaled scores (sigmoid_pre)
   const int n = it.n;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c2 = item_c2(S, it);
-  const float sarg = PRE ? bias_factor(c2) : c2;
+  const float sarg = PRE ? item_bias_factor(S, it, c2) : c2;
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BQ, D> dma_q(w, lane, S.sl[0]), dma_g(w, lane, S.sl[3]);
@@ -751,13 +843,92 @@ __device__ __forceinline__ void dkdv_body(uint16_t* __restrict__ lds, float* __r
   row_load((j0 + 1) * BQ, 1);
   vm_drain();
   __syncthreads();
+  float dsum = 0.0f;  // with DB: sum of this lane's dS values (its key column)
+  if constexpr (DkdvCfg<D>::ROLL) {
+    // S and dP of the current query tile as two 32-row blocks.  Block 0 is
+    // ready when a step starts; block 1 is computed during the step's first
+    // two chunks (while the VALU works on block 0), and block 0 of the next
+    // tile during the last two, with each chunk's A fragments read at its
+    // start: every chunk mixes score products, sigma and dS on the VALU, and
+    // the previous chunk's dV and dK products.
+    static_assert(NMB == 2 && NC == 4, "two 32-row blocks, four 16-row chunks");
+    constexpr int KS = D / 32;  // score K-steps per chunk
+    f32x16 sc[2], gc[2];
+    sc[0] = (f32x16){};
+    gc[0] = (f32x16){};
+    score_block<D>(sc[0], Qb(0), kf, 0, fa);
+    score_block<D>(gc[0], Gb(0), vf, 0, fa);
+    auto step = [&](auto phase, int jr) {
+      const int j = j0 + jr;  // inner (query) tile
+      constexpr int P = decltype(phase)::value;
+      constexpr int kc = P % 3, k1 = (P + 1) % 3, k2 = (P + 2) % 3;
+      dma_q.load(qs, (j + 2) * BQ, Qb(k2));
+      dma_g.load(gs, (j + 2) * BQ, Gb(k2));
+      row_load((j + 2) * BQ, k2);
+      const uint16_t* Qn = Qb(k1);
+      const uint16_t* Gn = Gb(k1);
+      const uint16_t* Qt = Qb(kc);
+      const uint16_t* Gt = Gb(kc);
+      if (S.causal && j * BQ < k0w + 31) mask_causal_block(sc[0], j * BQ, krow, hf, masked_score<PRE>());
+      e16x8 dh[NC], dl[NC], ph[NC], pl[NC];
+      e16x8 ag[2][D / 32], aq[2][D / 32];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        // score products of this chunk: block 1 of tile j (c < 2) or block 0
+        // of tile j+1 (c >= 2), K-steps KS*(c%2) ..
+        const uint16_t* Qs = c < 2 ? Qt : Qn;
+        const uint16_t* Gs = c < 2 ? Gt : Gn;
+        const int mb = c < 2 ? 1 : 0;
+        f32x16& st = sc[c < 2 ? 1 : 0];
+        f32x16& gt = gc[c < 2 ? 1 : 0];
+        read_value_frags<D>(ag[c & 1], tr, Gt, c);
+        read_value_frags<D>(aq[c & 1], tr, Qt, c);
+        e16x8 fs[KS], fg[KS];
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          fs[k] = fa.read(Qs, mb, KS * (c & 1) + k);
+          fg[k] = fa.read(Gs, mb, KS * (c & 1) + k);
+        }
+        sched_fence();
+        if (c == 2 && S.causal && j * BQ + 32 < k0w + 31)
+          mask_causal_block(sc[1], j * BQ + 32, krow, hf, masked_score<PRE>());
+        if constexpr (SOFTMAX) {
+          const float* lt = rowv + 2 * kc * BQ;  // lse2 of stage kc; delta follows
+          const int r0 = 16 * c + 4 * hf;
+          const f32x8 lse8 = cat8(*(const f32x4*)(lt + r0), *(const f32x4*)(lt + r0 + 8));
+          const f32x8 dlt8 = cat8(*(const f32x4*)(lt + BQ + r0), *(const f32x4*)(lt + BQ + r0 + 8));
+          dsoftmax_chunk_row<D, SPLIT>(sc, gc, c, lse8, dlt8, dh[c], dl[c], ph[c], pl[c]);
+        } else {
+          dsigmoid_chunk<D, SPLIT, PRE, true, DB>(sc, gc, c, sarg, dh[c], dl[c], ph[c], pl[c], &dsum);
+        }
+        if ((c & 1) == 0) {
+          st = (f32x16){};
+          gt = (f32x16){};
+        }
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          st = mfma(fs[k], kf[KS * (c & 1) + k], st);
+          gt = mfma(fg[k], vf[KS * (c & 1) + k], gt);
+        }
+        if (c > 0) {
+          value_chunk_pre<D, SPLIT>(dv, ag[(c - 1) & 1], ph[c - 1], pl[c - 1]);
+          value_chunk_pre<D, SPLIT>(dk, aq[(c - 1) & 1], dh[c - 1], dl[c - 1]);
+        }
+        sched_fence();
+      }
+      value_chunk_pre<D, SPLIT>(dv, ag[(NC - 1) & 1], ph[NC - 1], pl[NC - 1]);
+      value_chunk_pre<D, SPLIT>(dk, aq[(NC - 1) & 1], dh[NC - 1], dl[NC - 1]);
+      vm_drain();
+      __syncthreads();
+    };
+    run_steps(nq - j0, step);
+  } else {
   f32x16 sA[NMB], dA[NMB], sB[NMB], dB[NMB];
   zero2(sA);
   zero2(dA);
   score_steps<D>(sA, Qb(0), kf, 0, D / 16, fa);
   score_steps<D>(dA, Gb(0), vf, 0, D / 16, fa);
 
-  float dsum = 0.0f;  // with DB: sum of this lane's dS values (its key column)
   auto step = [&](auto phase, int jr) {
     const int j = j0 + jr;  // inner (query) tile
     constexpr int P = decltype(phase)::value;
@@ -814,6 +985,7 @@ __device__ __forceinline__ void dkdv_body(uint16_t* __restrict__ lds, float* __r
     __syncthreads();
   };
   run_steps(nq - j0, step);
+  }
 
   if constexpr (DB) {
     dsum += __shfl_xor(dsum, 32);  // the other half of the column's query rows
@@ -837,10 +1009,11 @@ template <int D, bool SPLIT, bool SOFTMAX = false, bool DB = false>
 __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    const float* __restrict__ LSE, const float* __restrict__ DELTA, float* __restrict__ DBIAS, const Sched S) {
+    const float* __restrict__ LSE, const float* __restrict__ DELTA, float* __restrict__ DBIAS, const SeqTable T,
+    const Sched S) {
   __shared__ __align__(16) uint16_t lds[dkdv_lds_elems<D>()];
   __shared__ __align__(16) float rowv[dkdv_row_floats<D, SOFTMAX>()];
-  dkdv_body<D, SPLIT, SOFTMAX, DB>(lds, rowv, (int)blockIdx.x, Q, K, V, dO, dK, dV, LSE, DELTA, DBIAS, S);
+  dkdv_body<D, SPLIT, SOFTMAX, DB>(lds, rowv, (int)blockIdx.x, Q, K, V, dO, dK, dV, LSE, DELTA, DBIAS, T, S);
 }
 
 // ---------------------------------------------------------------------------
@@ -862,9 +1035,9 @@ bwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const
   __shared__ __align__(16) float rowv[dkdv_row_floats<D, SOFTMAX>()];
   const int b = (int)blockIdx.x;
   if (b < P.dq_off)
-    dkdv_body<D, SPLIT, SOFTMAX, DB>(lds, rowv, b, Q, K, V, dO, dK, dV, LSE, DELTA, DBIAS, P.kv);
+    dkdv_body<D, SPLIT, SOFTMAX, DB>(lds, rowv, b, Q, K, V, dO, dK, dV, LSE, DELTA, DBIAS, P.T, P.kv);
   else
-    dq_body<D, SPLIT, SOFTMAX>(lds, b - P.dq_off, Q, K, V, dO, dQ, LSE, DELTA, P.dq);
+    dq_body<D, SPLIT, SOFTMAX>(lds, b - P.dq_off, Q, K, V, dO, dQ, LSE, DELTA, P.T, P.dq);
 }
 
 // delta = rowsum(dO * O) per row for the softmax backward (0 on padded
@@ -896,7 +1069,7 @@ __global__ __launch_bounds__(256) void softmax_prep_kernel(const uint16_t* __res
 template <int D, bool SPLIT>
 hipError_t launch_fwd_t(const Launch& L, const void* q, const void* k, const void* v, void* o, hipStream_t st) {
   hipLaunchKernelGGL((fwd_kernel<D, SPLIT>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, L.sched);
+                     (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, L.T, L.sched);
   return hipGetLastError();
 }
 
@@ -905,7 +1078,7 @@ hipError_t launch_dq_t(const Launch& L, const void* q, const void* k, const void
                        hipStream_t st) {
   hipLaunchKernelGGL((dq_kernel<D, SPLIT>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq, (const float*)nullptr,
-                     (const float*)nullptr, L.sched);
+                     (const float*)nullptr, L.T, L.sched);
   return hipGetLastError();
 }
 
@@ -915,11 +1088,11 @@ hipError_t launch_dkdv_t(const Launch& L, const void* q, const void* k, const vo
   if (dbias)
     hipLaunchKernelGGL((dkdv_kernel<D, SPLIT, false, true>), dim3(L.blocks), dim3(kThreads), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dk,
-                       (uint16_t*)dv, (const float*)nullptr, (const float*)nullptr, dbias, L.sched);
+                       (uint16_t*)dv, (const float*)nullptr, (const float*)nullptr, dbias, L.T, L.sched);
   else
     hipLaunchKernelGGL((dkdv_kernel<D, SPLIT>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dk, (uint16_t*)dv,
-                       (const float*)nullptr, (const float*)nullptr, (float*)nullptr, L.sched);
+                       (const float*)nullptr, (const float*)nullptr, (float*)nullptr, L.T, L.sched);
   return hipGetLastError();
 }
 
@@ -983,7 +1156,7 @@ template <int D, bool SPLIT>
 hipError_t launch_softmax_fwd_t(const Launch& L, const void* q, const void* k, const void* v, void* o, float* lse,
                                 hipStream_t st) {
   hipLaunchKernelGGL((fwd_softmax_kernel<D, SPLIT>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, L.sched);
+                     (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, L.T, L.sched);
   return hipGetLastError();
 }
 
@@ -991,7 +1164,7 @@ template <int D, bool SPLIT>
 hipError_t launch_softmax_dq_t(const Launch& L, const void* q, const void* k, const void* v, const void* g,
                                const float* lse, const float* delta, void* dq, hipStream_t st) {
   hipLaunchKernelGGL((dq_kernel<D, SPLIT, true>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq, lse, delta, L.sched);
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq, lse, delta, L.T, L.sched);
   return hipGetLastError();
 }
 
@@ -1000,7 +1173,7 @@ hipError_t launch_softmax_dkdv_t(const Launch& L, const void* q, const void* k, 
                                  const float* lse, const float* delta, void* dk, void* dv, hipStream_t st) {
   hipLaunchKernelGGL((dkdv_kernel<D, SPLIT, true>), dim3(L.blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dk, (uint16_t*)dv, lse,
-                     delta, (float*)nullptr, L.sched);
+                     delta, (float*)nullptr, L.T, L.sched);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // Host-side tile schedule: which output tiles exist, how they are grouped into
-// pieces, and which XCD list each piece goes to.  Pure C++; no HIP calls.
+// pieces, which XCD list each piece goes to, and which sequences each launch
+// covers.  Pure C++; no HIP calls.
 #include "plan.h"
 
 #include <algorithm>
@@ -11,11 +12,10 @@ namespace sigattn {
 namespace {
 
 struct Piece {
-  int32_t b, h0, nh, t0, nt;
-  int32_t n;
-  int64_t item_cost;   // inner tiles of the piece's longest item
-  int64_t total;       // inner tiles over all its items
-  int64_t cost() const { return total; }
+  int32_t s0, ns, h0, nh, t0, nt;  // see Sched; s0 is launch-local
+  int64_t item_cost;               // inner tiles of the piece's longest item
+  int64_t total;                   // inner tiles over all its items
+  int64_t items;                   // work items
 };
 
 int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
@@ -28,39 +28,173 @@ int64_t item_inner(const PlanInput& in, int32_t n, int32_t t) {
   return std::min(inner, causal_inner_end(t, in.outer_rows, in.inner_rows));
 }
 
-Piece make_piece(const PlanInput& in, int32_t b, int32_t h0, int32_t nh, int32_t t0, int32_t nt, int32_t n) {
+// Tiles t0 .. t0+nt-1 of nh heads of one sequence (launch-local index s).
+Piece seq_piece(const PlanInput& in, int32_t s, int32_t n, int32_t h0, int32_t nh, int32_t t0, int32_t nt) {
   int64_t sum = 0, mx = 0;
   for (int32_t t = t0; t < t0 + nt; ++t) {
     const int64_t c = item_inner(in, n, t);
     sum += c;
     mx = std::max(mx, c);
   }
-  return {b, h0, nh, t0, nt, n, mx, sum * nh};
+  return {s, 1, h0, nh, t0, nt, mx, sum * nh, (int64_t)nt * nh};
 }
 
-// Pieces of at most about `target` tile pairs, cut evenly: whole sequences
-// (all heads) when small, else runs of heads, else runs of tiles of one head.
-std::vector<Piece> make_pieces(const PlanInput& in, int64_t target) {
+// Pieces of at most about `target` tile pairs over the sequences
+// [b_lo, b_hi), cut evenly: runs of consecutive short sequences (all heads,
+// at most kPieceSeqs sequences), whole sequences, runs of heads, or runs of
+// tiles of one head.
+std::vector<Piece> make_pieces(const PlanInput& in, int32_t b_lo, int32_t b_hi, int64_t target) {
   std::vector<Piece> pieces;
-  for (int32_t b = 0; b < in.B; ++b) {
-    const int32_t n = in.seqlens[b];
-    if (n <= 0) continue;
-    const int32_t items = ceil_div(n, in.outer_rows);
-    const int64_t head_cost = make_piece(in, b, 0, 1, 0, items, n).total;
-    if (head_cost * in.H <= target) {
-      pieces.push_back(make_piece(in, b, 0, in.H, 0, items, n));
-    } else if (head_cost <= target) {
-      const int32_t parts = (int32_t)((head_cost * in.H + target - 1) / target);
-      const int32_t k = ceil_div(in.H, parts);
-      for (int32_t h = 0; h < in.H; h += k) pieces.push_back(make_piece(in, b, h, std::min(k, in.H - h), 0, items, n));
+  Piece group{};
+  bool open = false;
+  auto close = [&]() {
+    if (!open) return;
+    if (group.ns == 1) {  // a group of one is a plain whole-sequence piece
+      const int32_t n = in.seqlens[b_lo + group.s0];
+      pieces.push_back(seq_piece(in, group.s0, n, 0, in.H, 0, ceil_div(n, in.outer_rows)));
     } else {
-      const int32_t parts = (int32_t)std::min<int64_t>(items, (head_cost + target - 1) / target);
+      pieces.push_back(group);
+    }
+    open = false;
+  };
+  for (int32_t b = b_lo; b < b_hi; ++b) {
+    const int32_t n = in.seqlens[b];
+    if (n <= 0) continue;  // no items; inside a group it is skipped by the decode
+    const int32_t s = b - b_lo;
+    const int32_t items = ceil_div(n, in.outer_rows);
+    const Piece one = seq_piece(in, s, n, 0, 1, 0, items);
+    const int64_t whole = one.total * in.H;
+    if (whole <= target) {
+      if (open && (group.total + whole > target || s - group.s0 + 1 > kPieceSeqs)) close();
+      if (!open) {
+        group = {s, 0, 0, in.H, 0, 0, 0, 0, 0};
+        open = true;
+      }
+      group.ns = s - group.s0 + 1;
+      group.total += whole;
+      group.items += (int64_t)items * in.H;
+      group.item_cost = std::max(group.item_cost, one.item_cost);
+      continue;
+    }
+    close();
+    if (one.total <= target) {
+      const int32_t parts = (int32_t)((whole + target - 1) / target);
+      const int32_t k = ceil_div(in.H, parts);
+      for (int32_t h = 0; h < in.H; h += k) pieces.push_back(seq_piece(in, s, n, h, std::min(k, in.H - h), 0, items));
+    } else {
+      const int32_t parts = (int32_t)std::min<int64_t>(items, (one.total + target - 1) / target);
       const int32_t m = ceil_div(items, parts);
       for (int32_t h = 0; h < in.H; ++h)
-        for (int32_t t = 0; t < items; t += m) pieces.push_back(make_piece(in, b, h, 1, t, std::min(m, items - t), n));
+        for (int32_t t = 0; t < items; t += m) pieces.push_back(seq_piece(in, s, n, h, 1, t, std::min(m, items - t)));
     }
   }
+  close();
   return pieces;
+}
+
+// Pieces for the sequences [b_lo, b_hi) that fit one launch, cut as finely as
+// the piece limit allows (about 1/64 of the work each, else 1/32 .. 1/8), or
+// an empty optional when even the coarsest cut needs more than kMaxPieces.
+bool plan_pieces(const PlanInput& in, int32_t b_lo, int32_t b_hi, std::vector<Piece>& out) {
+  int64_t total = 0;
+  for (int32_t b = b_lo; b < b_hi; ++b)
+    if (in.seqlens[b] > 0) total += seq_piece(in, 0, in.seqlens[b], 0, in.H, 0, ceil_div(in.seqlens[b], in.outer_rows)).total;
+  out.clear();
+  if (total == 0) return true;
+  // No piece larger than about 1/64 of the launch's work (1/8 of one XCD's
+  // share): longest-first assignment then evens out the 8 XCD lists to within
+  // a few percent on ragged batches.  If that needs more pieces than one
+  // launch holds, cut coarser (1/32, 1/16, 1/8).
+  for (int64_t parts_per_xcd = 8; parts_per_xcd >= 1; parts_per_xcd /= 2) {
+    out = make_pieces(in, b_lo, b_hi, std::max<int64_t>(1, (total + parts_per_xcd * kXcds - 1) / (parts_per_xcd * kXcds)));
+    if (out.size() <= (size_t)kMaxPieces) return true;
+  }
+  return false;
+}
+
+// One launch over the sequences [b_lo, b_hi) with the given pieces.
+Launch make_launch(const PlanInput& in, int32_t b_lo, int32_t b_hi, std::vector<Piece> pieces) {
+  const double log2e = 1.4426950408889634;
+  Launch L;
+  std::memset(&L, 0, sizeof(L));
+  L.T.b_base = b_lo;
+  L.T.nseq = b_hi - b_lo;
+  L.T.wide = in.Lmax > 65535;
+  for (int32_t s = 0; s < L.T.nseq; ++s) {
+    if (L.T.wide) L.T.n32[s] = (uint32_t)in.seqlens[b_lo + s];
+    else L.T.n16[s] = (uint16_t)in.seqlens[b_lo + s];
+  }
+  Sched& S = L.sched;
+  S.H = in.H;
+  S.Lmax = in.Lmax;
+  S.outer_rows = in.outer_rows;
+  S.out_scale = (float)(1.0 / std::sqrt((double)in.d));
+  S.causal = in.causal;
+  S.bias_kind = in.bias_mode == 0 ? 0 : in.bias_mode == 3 ? 2 : 1;
+  S.c2_const = S.bias_kind == 1 ? (float)(-bias_value(1, in.bias_mode, in.bias_arg) * log2e) : 0.0f;
+
+  // Longest first (ties: lower sequence, head, tile first, so plans are deterministic).
+  std::stable_sort(pieces.begin(), pieces.end(), [](const Piece& a, const Piece& b) { return a.total > b.total; });
+  // Longest-processing-time-first over the 8 XCD lists.
+  std::vector<std::vector<Piece>> lists(kXcds);
+  int64_t load[kXcds] = {0};
+  for (const Piece& pc : pieces) {
+    int best = 0;
+    for (int x = 1; x < kXcds; ++x)
+      if (load[x] < load[best]) best = x;
+    lists[best].push_back(pc);
+    load[best] += pc.total;
+  }
+  int32_t g = 0, max_items = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    // Within a list, items with the most inner tiles start first.
+    std::stable_sort(lists[x].begin(), lists[x].end(),
+                     [](const Piece& a, const Piece& b) { return a.item_cost > b.item_cost; });
+    S.xcd_begin[x] = g;
+    int32_t item = 0;
+    for (const Piece& pc : lists[x]) {
+      S.s0[g] = pc.s0;
+      S.ns[g] = pc.ns;
+      S.h0[g] = pc.h0;
+      S.nh[g] = pc.nh;
+      S.t0[g] = pc.t0;
+      S.nt[g] = pc.nt;
+      S.item0[g] = item;
+      S.n1[g] = pc.ns == 1 ? in.seqlens[b_lo + pc.s0] : 0;
+      item += (int32_t)pc.items;
+      ++g;
+    }
+    S.xcd_items[x] = item;
+    max_items = std::max(max_items, item);
+  }
+  S.xcd_begin[kXcds] = g;
+  S.compute_blocks = kXcds * max_items;
+  L.blocks = S.compute_blocks;
+  bool pad = false;
+  for (int32_t b = b_lo; b < b_hi; ++b) pad |= in.seqlens[b] < in.Lmax;
+  if (pad) {
+    S.zero_nseq = L.T.nseq;
+    S.zero_split = (int64_t)L.T.nseq * in.H <= 2048 ? 4 : 1;
+    L.blocks += S.zero_nseq * in.H * S.zero_split;
+  }
+  return L;
+}
+
+// Launches for the sequences [b_lo, b_hi): one if its pieces fit, else the
+// two halves in turn.
+void plan_range(const PlanInput& in, int32_t b_lo, int32_t b_hi, std::vector<Launch>& out) {
+  std::vector<Piece> pieces;
+  if (b_hi - b_lo > 1 && !plan_pieces(in, b_lo, b_hi, pieces)) {
+    const int32_t mid = b_lo + (b_hi - b_lo) / 2;
+    plan_range(in, b_lo, mid, out);
+    plan_range(in, mid, b_hi, out);
+    return;
+  }
+  if (b_hi - b_lo == 1) plan_pieces(in, b_lo, b_hi, pieces);  // one sequence always fits
+  bool pad = false;
+  for (int32_t b = b_lo; b < b_hi; ++b) pad |= in.seqlens[b] < in.Lmax;
+  if (pieces.empty() && !pad) return;  // nothing to compute or clear
+  out.push_back(make_launch(in, b_lo, b_hi, std::move(pieces)));
 }
 
 }  // namespace
@@ -74,98 +208,22 @@ double bias_value(int32_t n, int32_t mode, float arg) {
 }
 
 std::vector<Launch> build_plan(const PlanInput& in, PlanStats* stats) {
-  const double log2e = 1.4426950408889634;
-  std::vector<Piece> pieces;
-  int64_t total_cost = 0, total_items = 0;
-  for (int32_t b = 0; b < in.B; ++b) {
-    const int32_t n = in.seqlens[b];
-    if (n <= 0) continue;
-    const int32_t items = ceil_div(n, in.outer_rows);
-    total_items += (int64_t)items * in.H;
-    total_cost += make_piece(in, b, 0, in.H, 0, items, n).total;
-  }
   if (stats) {
-    stats->items = total_items;
-    stats->pairs = total_cost;
+    int64_t items = 0, pairs = 0;
+    for (int32_t b = 0; b < in.B; ++b) {
+      const int32_t n = in.seqlens[b];
+      if (n <= 0) continue;
+      const Piece p = seq_piece(in, 0, n, 0, in.H, 0, ceil_div(n, in.outer_rows));
+      items += p.items;
+      pairs += p.total;
+    }
+    stats->items = items;
+    stats->pairs = pairs;
   }
-
-  // Cut work so that no piece is larger than about 1/64 of the total (1/8 of
-  // one XCD's share): longest-first assignment then evens out the 8 XCD lists
-  // to within a few percent on ragged batches.  If that needs more pieces than
-  // one launch holds, cut coarser (1/32, 1/16, 1/8) before resorting to
-  // several launches.
-  for (int64_t parts_per_xcd = 8; parts_per_xcd >= 1; parts_per_xcd /= 2) {
-    pieces = make_pieces(in, std::max<int64_t>(1, (total_cost + parts_per_xcd * kXcds - 1) / (parts_per_xcd * kXcds)));
-    if (pieces.size() <= (size_t)kMaxPieces) break;
-  }
-  // Longest first (ties: lower sequence, head, tile first, so plans are deterministic).
-  std::stable_sort(pieces.begin(), pieces.end(), [](const Piece& a, const Piece& b) {
-    return a.cost() > b.cost();
-  });
-
-  // Zero-fill chunks: sequences [256c, 256c + 256) that have padding.
-  std::vector<int32_t> zero_chunks;
-  for (int32_t b0 = 0; b0 < in.B; b0 += kZeroSeqs) {
-    bool any = false;
-    for (int32_t b = b0; b < std::min(in.B, b0 + kZeroSeqs); ++b) any |= in.seqlens[b] < in.Lmax;
-    if (any) zero_chunks.push_back(b0);
-  }
-  const size_t piece_chunks = (pieces.size() + kMaxPieces - 1) / kMaxPieces;
-  const size_t nlaunch = std::max(piece_chunks, zero_chunks.size());
-
+  // Sequences per launch: what one length table holds.
+  const int32_t cap = in.Lmax > 65535 ? kMaxSeqsWide : kMaxSeqs;
   std::vector<Launch> launches;
-  for (size_t li = 0; li < nlaunch; ++li) {
-    const size_t p0 = std::min(pieces.size(), li * kMaxPieces);
-    const size_t p1 = std::min(pieces.size(), p0 + kMaxPieces);
-    // Longest-processing-time-first over the 8 XCD lists.
-    std::vector<std::vector<Piece>> lists(kXcds);
-    int64_t load[kXcds] = {0};
-    for (size_t p = p0; p < p1; ++p) {
-      int best = 0;
-      for (int x = 1; x < kXcds; ++x)
-        if (load[x] < load[best]) best = x;
-      lists[best].push_back(pieces[p]);
-      load[best] += pieces[p].cost();
-    }
-    Launch L;
-    std::memset(&L.sched, 0, sizeof(L.sched));
-    L.sched.H = in.H;
-    L.sched.Lmax = in.Lmax;
-    L.sched.out_scale = (float)(1.0 / std::sqrt((double)in.d));
-    L.sched.causal = in.causal;
-    int32_t g = 0, max_items = 0;
-    for (int x = 0; x < kXcds; ++x) {
-      // Within a list, items with the most inner tiles start first.
-      std::stable_sort(lists[x].begin(), lists[x].end(), [](const Piece& a, const Piece& b) {
-        return a.item_cost > b.item_cost;
-      });
-      L.sched.xcd_begin[x] = g;
-      int32_t item = 0;
-      for (const Piece& pc : lists[x]) {
-        L.sched.bh0[g] = pc.b * in.H + pc.h0;
-        L.sched.n[g] = pc.n;
-        L.sched.item0[g] = item;
-        L.sched.t0[g] = pc.t0;
-        L.sched.nt[g] = pc.nt;
-        L.sched.c2[g] = (float)(-bias_value(pc.n, in.bias_mode, in.bias_arg) * log2e);
-        item += pc.nh * pc.nt;
-        ++g;
-      }
-      L.sched.xcd_items[x] = item;
-      max_items = std::max(max_items, item);
-    }
-    L.sched.xcd_begin[kXcds] = g;
-    L.sched.compute_blocks = kXcds * max_items;
-    L.blocks = L.sched.compute_blocks;
-    if (li < zero_chunks.size()) {
-      const int32_t b0 = zero_chunks[li];
-      L.sched.zero_b0 = b0;
-      L.sched.zero_nseq = std::min(kZeroSeqs, in.B - b0);
-      for (int32_t i = 0; i < L.sched.zero_nseq; ++i) L.sched.zero_n[i] = in.seqlens[b0 + i];
-      L.blocks += L.sched.zero_nseq * in.H * kZeroSplit;
-    }
-    launches.push_back(L);
-  }
+  for (int32_t b0 = 0; b0 < in.B; b0 += cap) plan_range(in, b0, std::min(in.B, b0 + cap), launches);
   return launches;
 }
 

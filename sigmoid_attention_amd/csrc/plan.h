@@ -18,44 +18,74 @@
 // cost, so long items start first.
 #pragma once
 
+#include <cstddef>
 #include <cstdint>
 #include <vector>
 
 namespace sigattn {
 
 constexpr int kXcds = 8;
-// Pieces per launch and sequences zero-filled per launch: six 4-byte arrays of
-// kMaxPieces, one of kZeroSeqs and a small header keep the kernel-argument
-// block near 3.4 KB, under the 4 KB limit.
+// Pieces per launch (seven 4-byte arrays of kMaxPieces: 2.7 KB of kernel
+// arguments per schedule).
 constexpr int kMaxPieces = 96;
-constexpr int kZeroSeqs = 256;
-// Workgroups that share the zero fill of one (sequence, head).
-constexpr int kZeroSplit = 4;
+// Sequences per launch: their lengths travel in a table of 16-bit values
+// (8 KB), or of 32-bit values for Lmax > 65535 (then half as many).  One
+// table serves both schedules of the fused backward, whose kernel-argument
+// block (BwdSched) is then 14.5 KB; the largest block the kernels take must
+// stay within kKernargBudget, the size checked to launch on MI355X with
+// ROCm 7 (static_assert below the structures).
+constexpr int kMaxSeqs = 4096;
+constexpr int kMaxSeqsWide = 2048;
+// Sequences one piece may span (bounds the decode's scan over them).
+constexpr int kPieceSeqs = 64;
 
-// Kernel-argument block.  Plain data; copied by value into every launch.
+// Lengths of the sequences b_base .. b_base + nseq - 1 of one launch.  The
+// table is 16-byte aligned so that the kernels read it in 16-byte words.
+struct alignas(16) SeqTable {
+  int32_t b_base;
+  int32_t nseq;
+  int32_t wide;  // 1: the lengths are 32-bit (Lmax > 65535)
+  int32_t pad_;
+  union {
+    uint16_t n16[kMaxSeqs];
+    uint32_t n32[kMaxSeqsWide];
+  };
+};
+
+// Kernel-argument block of one pass.  Plain data; copied by value into every
+// launch together with the launch's SeqTable.
 struct Sched {
   int32_t H;
   int32_t Lmax;
+  int32_t outer_rows;            // rows per output tile (work item)
   float out_scale;               // 1 / sqrt(d) (gradient epilogues)
   int32_t xcd_begin[kXcds + 1];  // piece range of each XCD list
   int32_t xcd_items[kXcds];      // work items in each XCD list
-  // A piece is nh consecutive heads h0..h0+nh-1 of one sequence b times nt
-  // consecutive outer tiles t0..t0+nt-1; its items are enumerated head-major.
-  int32_t bh0[kMaxPieces];       // b * H + h0
-  int32_t n[kMaxPieces];         // valid length n_b
+  // Piece p covers the launch-local sequences s0 .. s0+ns-1 (indices into the
+  // SeqTable) and heads h0 .. h0+nh-1; with ns = 1, outer tiles t0 .. t0+nt-1
+  // of that sequence (items head-major, tile fastest); with ns > 1, every
+  // outer tile of each sequence (items sequence-major, then head, then tile).
+  int32_t s0[kMaxPieces];
+  int32_t ns[kMaxPieces];
+  int32_t h0[kMaxPieces];
+  int32_t nh[kMaxPieces];
+  int32_t t0[kMaxPieces];
+  int32_t nt[kMaxPieces];
   int32_t item0[kMaxPieces];     // first list position (within its XCD list) of the piece
-  int32_t t0[kMaxPieces];        // first outer tile of the piece
-  int32_t nt[kMaxPieces];        // outer tiles per head in the piece
-  float c2[kMaxPieces];          // -bias * log2(e)
+  int32_t n1[kMaxPieces];        // length of the piece's sequence when ns = 1 (saves a table read)
+  // The bias term c2 = -b log2(e) of an item: from the sequence length
+  // (bias_kind 0: b = -ln n, c2 = log2 n), the constant c2_const (1), or the
+  // per-head values at head_bias (2).
+  int32_t bias_kind;
+  float c2_const;
   // Padded rows n_b..Lmax-1 of the outputs are written as 0 by trailing
-  // workgroups: block compute_blocks + (bl * H + h) * kZeroSplit + part clears
-  // part `part` of those rows of sequence zero_b0 + bl, head h.
+  // workgroups: block compute_blocks + (s * H + h) * zero_split + part clears
+  // part `part` of those rows of table sequence s, head h.
   int32_t compute_blocks;        // 8 * max(xcd_items)
-  int32_t zero_b0;               // first sequence zero-filled by this launch
-  int32_t zero_nseq;             // sequences zero-filled by this launch (0: none)
-  int32_t zero_n[kZeroSeqs];     // their valid lengths
+  int32_t zero_nseq;             // table sequences zero-filled by this launch (0 or the table's nseq)
+  int32_t zero_split;            // workgroups per (sequence, head) of the zero fill
   int32_t causal;                // causal mask (see PlanInput)
-  const float* head_bias;        // device: one bias per head (replaces c2), or null
+  const float* head_bias;        // device: one bias per head (bias_kind 2), or null
   // Element strides (sequence, head, row) of each tensor argument of the
   // launch, in argument order; the head dimension is contiguous.
   int64_t sb[6];
@@ -70,15 +100,16 @@ struct Sched {
 #define SIGATTN_HD
 #endif
 
-// One work item: outer tile `tile` of head bh = b * H + h.
+inline SIGATTN_HD int32_t table_n(const SeqTable& T, int32_t s) { return T.wide ? (int32_t)T.n32[s] : (int32_t)T.n16[s]; }
+
+// One work item: outer tile `tile` of head bh = b * H + h, b = T.b_base + s.
 struct Item {
-  int32_t bh, n, tile;
-  float c2;
+  int32_t bh, n, tile, s;
 };
 
 // The item of list position j in XCD list x, or false for an idle block
 // (j beyond the list).  Workgroup i runs x = i % 8, j = i / 8.
-inline SIGATTN_HD bool decode_item(const Sched& S, int32_t x, int32_t j, Item& it) {
+inline SIGATTN_HD bool decode_item(const SeqTable& T, const Sched& S, int32_t x, int32_t j, Item& it) {
   if (j >= S.xcd_items[x]) return false;
   int32_t lo = S.xcd_begin[x], hi = S.xcd_begin[x + 1] - 1;
   while (lo < hi) {  // last piece whose first list position is <= j
@@ -86,29 +117,49 @@ inline SIGATTN_HD bool decode_item(const Sched& S, int32_t x, int32_t j, Item& i
     if (S.item0[mid] <= j) lo = mid;
     else hi = mid - 1;
   }
-  const int32_t i = j - S.item0[lo];
-  const int32_t nt = S.nt[lo];
+  int32_t i = j - S.item0[lo];
+  int32_t s = S.s0[lo], nt = S.nt[lo], t0 = S.t0[lo];
+  if (S.ns[lo] > 1) {  // walk the piece's sequences (at most kPieceSeqs)
+    const int32_t send = s + S.ns[lo] - 1;
+    for (;; ++s) {
+      nt = (table_n(T, s) + S.outer_rows - 1) / S.outer_rows;
+      const int32_t cnt = S.nh[lo] * nt;
+      if (i < cnt || s == send) break;
+      i -= cnt;
+    }
+    t0 = 0;
+  }
   const int32_t hoff = i / nt;
-  it.bh = S.bh0[lo] + hoff;
-  it.tile = S.t0[lo] + (i - hoff * nt);
-  it.n = S.n[lo];
-  it.c2 = S.c2[lo];
+  it.s = s;
+  it.n = S.ns[lo] > 1 ? table_n(T, s) : S.n1[lo];
+  it.bh = (T.b_base + s) * S.H + S.h0[lo] + hoff;
+  it.tile = t0 + (i - hoff * nt);
   return true;
 }
 
 struct Launch {
+  SeqTable T;
   Sched sched;
   int32_t blocks;  // grid size: compute blocks + zero-fill blocks
 };
 
 // The fused backward launch: the dK/dV schedule's blocks first, then the dQ
 // schedule's from block dq_off (a multiple of 8, so that each part's block
-// index keeps its XCD; blocks between the two parts are idle).
+// index keeps its XCD; blocks between the two parts are idle).  Both
+// schedules cover the sequences of the one table.
 struct BwdSched {
+  SeqTable T;
   Sched kv;
   Sched dq;
   int32_t dq_off;
 };
+
+// Kernel-argument bytes a launch may carry (blocks of 16 KB were checked on
+// MI355X); the fused backward's ten pointers come before its BwdSched.
+constexpr size_t kKernargBudget = 16384;
+static_assert(sizeof(BwdSched) + 10 * sizeof(void*) <= kKernargBudget, "fused backward arguments exceed the budget");
+static_assert(sizeof(SeqTable) + sizeof(Sched) + 10 * sizeof(void*) <= kKernargBudget,
+              "single-pass arguments exceed the budget");
 
 struct PlanInput {
   int32_t B, H, Lmax, d;

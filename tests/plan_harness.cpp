@@ -3,7 +3,8 @@
 // same decode_item() the kernels use.  Verifies that each non-padded output
 // tile is visited exactly once and that no fully padded tile appears; prints
 // a one-line JSON summary.  Also checks that every sequence with padding is
-// zero-filled by exactly one launch.
+// zero-filled by exactly one launch, that each launch's length table holds
+// its sequences, and that no piece spans more sequences than allowed.
 //
 // usage: plan_harness B H Lmax d outer_rows inner_rows n_0 ... n_{B-1}
 #include <cstdio>
@@ -36,25 +37,35 @@ int main(int argc, char** argv) {
   std::vector<int> zeroed(in.B, 0);
   long long blocks = 0, idle = 0, bad = 0, pairs = 0;
   double worst_imbalance = 0.0;
+  int max_piece_seqs = 0;
   for (const auto& L : plan) {
     if (L.sched.compute_blocks % sigattn::kXcds) ++bad;
-    if (L.blocks != L.sched.compute_blocks + L.sched.zero_nseq * in.H * sigattn::kZeroSplit) ++bad;
-    for (int32_t i = 0; i < L.sched.zero_nseq; ++i) {
-      const int b = L.sched.zero_b0 + i;
-      if (b >= in.B || L.sched.zero_n[i] != lens[b]) ++bad;
-      else zeroed[b]++;
+    if (L.blocks != L.sched.compute_blocks + L.sched.zero_nseq * in.H * L.sched.zero_split) ++bad;
+    // the length table holds this launch's sequences exactly
+    const int cap = L.T.wide ? sigattn::kMaxSeqsWide : sigattn::kMaxSeqs;
+    if (L.T.nseq < 1 || L.T.nseq > cap || L.T.b_base < 0 || L.T.b_base + L.T.nseq > in.B) ++bad;
+    else
+      for (int32_t s = 0; s < L.T.nseq; ++s)
+        if (sigattn::table_n(L.T, s) != lens[L.T.b_base + s]) ++bad;
+    if (L.sched.zero_nseq != 0 && L.sched.zero_nseq != L.T.nseq) ++bad;
+    for (int32_t i = 0; i < L.sched.zero_nseq; ++i) zeroed[L.T.b_base + i]++;
+    for (int32_t p = 0; p < L.sched.xcd_begin[sigattn::kXcds]; ++p) {
+      if (L.sched.ns[p] < 1 || L.sched.ns[p] > sigattn::kPieceSeqs || L.sched.s0[p] < 0 ||
+          L.sched.s0[p] + L.sched.ns[p] > L.T.nseq)
+        ++bad;
+      max_piece_seqs = L.sched.ns[p] > max_piece_seqs ? L.sched.ns[p] : max_piece_seqs;
     }
     long long xload[sigattn::kXcds] = {0};
     for (int32_t i = 0; i < L.sched.compute_blocks; ++i) {
       sigattn::Item it;
       ++blocks;
-      if (!sigattn::decode_item(L.sched, i % sigattn::kXcds, i / sigattn::kXcds, it)) {
+      if (!sigattn::decode_item(L.T, L.sched, i % sigattn::kXcds, i / sigattn::kXcds, it)) {
         ++idle;
         continue;
       }
       const int b = it.bh / in.H;
       const int ntiles = (lens[b] + in.outer_rows - 1) / in.outer_rows;
-      if (b < 0 || b >= in.B || it.n != lens[b] || it.tile < 0 || it.tile >= ntiles) ++bad;
+      if (b < 0 || b >= in.B || b != L.T.b_base + it.s || it.n != lens[b] || it.tile < 0 || it.tile >= ntiles) ++bad;
       seen[{it.bh, it.tile}]++;
       const long long inner = (lens[b] + in.inner_rows - 1) / in.inner_rows;
       pairs += inner;
@@ -87,8 +98,9 @@ int main(int argc, char** argv) {
     if (lens[b] < in.Lmax ? zeroed[b] != 1 : zeroed[b] > 1) ++zero_bad;
   printf("{\"launches\": %zu, \"blocks\": %lld, \"idle\": %lld, \"items\": %lld, \"expect\": %lld, "
          "\"missing\": %lld, \"dup\": %lld, \"extra\": %lld, \"bad\": %lld, \"pairs\": %lld, "
-         "\"stats_items\": %lld, \"stats_pairs\": %lld, \"xcd_imbalance\": %.4f, \"zero_bad\": %lld}\n",
+         "\"stats_items\": %lld, \"stats_pairs\": %lld, \"xcd_imbalance\": %.4f, \"zero_bad\": %lld, "
+         "\"max_piece_seqs\": %d}\n",
          plan.size(), blocks, idle, blocks - idle, expect, missing, dup, extra, bad, pairs, (long long)st.items,
-         (long long)st.pairs, worst_imbalance, zero_bad);
+         (long long)st.pairs, worst_imbalance, zero_bad, max_piece_seqs);
   return 0;
 }

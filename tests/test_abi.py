@@ -348,6 +348,31 @@ def test_fused_backward_pass_in_validate_and_plan_stats():
     q = sa.plan_stats(2, 2, 128, 64, lens, "bwd_dq")
     both = sa.plan_stats(2, 2, 128, 64, lens, "bwd")
     assert both[0] == kv[0] + q[0] and both[1] == kv[1] + q[1] and both[2] == 1
-    many = list(np.random.default_rng(5).integers(0, 97, size=300))
-    assert sa.plan_stats(300, 1, 96, 64, many, "bwd")[2] == (sa.plan_stats(300, 1, 96, 64, many, "bwd_dkdv")[2]
-                                                              + sa.plan_stats(300, 1, 96, 64, many, "bwd_dq")[2])
+    # beyond one launch's length table (4096 sequences): each side runs two
+    # launches and the backward runs them in turn instead of one fused launch
+    many = [64] * 5000
+    assert sa.plan_stats(5000, 1, 96, 64, many, "bwd_dkdv")[2] == 2
+    assert sa.plan_stats(5000, 1, 96, 64, many, "bwd")[2] == (sa.plan_stats(5000, 1, 96, 64, many, "bwd_dkdv")[2]
+                                                               + sa.plan_stats(5000, 1, 96, 64, many, "bwd_dq")[2])
+
+
+@pytest.mark.parametrize("B,n,Lmax", [(1024, 256, 256), (4096, 128, 128), (1024, 200, 256), (300, None, 96)])
+def test_many_short_sequences_one_launch(B, n, Lmax):
+    """Batches of many short sequences (single cells of a few hundred genes)
+    run every pass as one launch: pieces span many sequences and the lengths
+    travel in a table of the kernel arguments."""
+    lens = [n] * B if n is not None else list(np.random.default_rng(5).integers(0, Lmax + 1, size=B))
+    for pass_ in ("fwd", "bwd_dq", "bwd_dkdv", "bwd"):
+        items, pairs, launches = sa.plan_stats(B, 16, Lmax, 64, lens, pass_)
+        assert launches == 1, (pass_, launches)
+    items, pairs, _ = sa.plan_stats(B, 16, Lmax, 64, lens, "fwd")
+    ln = np.asarray(lens, dtype=np.int64)
+    assert items == int((16 * -(-ln // 128)).sum()) and pairs == int((16 * -(-ln // 128) * -(-ln // 64)).sum())
+
+
+def test_long_padded_length_uses_wide_table():
+    """Lmax above 65535 needs 32-bit lengths: a launch then holds 2048 sequences."""
+    lens = [100] * 2500
+    assert sa.plan_stats(2500, 1, 70000, 64, lens, "fwd")[2] == 2
+    assert sa.plan_stats(2048, 1, 70000, 64, lens[:2048], "fwd")[2] == 1
+    assert sa.plan_stats(2500, 1, 65535, 64, lens, "fwd")[2] == 1

@@ -95,12 +95,14 @@ def test_fused_softmax_equals_separate_and_oracle():
 
 
 def test_multi_launch_route():
-    """300 sequences exceed one launch's zero-fill capacity (256 sequences),
-    so the schedule has several launches per side and sigattn_bwd runs them
-    in turn; results still equal the separate calls and the oracle."""
-    B, H, d, L = 300, 1, 64, 96
+    """4500 sequences exceed one launch's length table (4096 sequences), so
+    the schedule has two launches per side (and per forward) and sigattn_bwd
+    runs them in turn; results still equal the separate calls and the
+    oracle."""
+    B, H, d, L = 4500, 1, 64, 96
     lens = list(np.random.default_rng(5).integers(0, L + 1, size=B))
-    assert sa.plan_stats(B, H, L, d, lens, "bwd_dq")[2] > 1
+    assert sa.plan_stats(B, H, L, d, lens, "bwd_dq")[2] == 2
+    assert sa.plan_stats(B, H, L, d, lens, "fwd")[2] == 2
     c = workloads.random_case(B, H, d, L, lens, seed=65)
     t = {x: c[x].to(DEV) for x in ("q", "k", "v", "do")}
     n = c["seqlens"]
@@ -109,6 +111,8 @@ def test_multi_launch_route():
     dk0, dv0 = sa.bwd_dkdv(t["q"], t["k"], t["v"], t["do"], n)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq0) and torch.equal(dk, dk0) and torch.equal(dv, dv0)
+    o = sa.fwd(t["q"], t["k"], t["v"], n)
+    torch.cuda.synchronize()
     ref = oracle.attention(host(c["q"]), host(c["k"]), host(c["v"]), n, do=host(c["do"]))
-    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+    for name, g in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
         assert worst_ratio(host(g), ref[name]) <= 1.0, name

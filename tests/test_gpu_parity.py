@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import sigmoid_attention_amd as sa
 import workloads
 from gpu_util import host, padded_rows_zero, run_all, to_dev, worst_ratio
 
@@ -79,3 +80,24 @@ def test_saturated_scores_split_every_element():
     the many small saturated weights accurate."""
     case = workloads.random_case(2, 2, 64, 700, [700, 333], seed=9, scale_qkv=4.0)
     check_full(case, "split", label="x4 ragged")
+
+
+@pytest.mark.parametrize("B,H,Lmax,lo", [(1024, 2, 256, 1), (4096, 1, 128, 100)], ids=["B1024", "B4096"])
+def test_many_short_sequences_every_element(B, H, Lmax, lo):
+    """Single-cell batches of many short cells: every pass is one launch
+    (pieces span many sequences; the lengths travel in the kernel arguments),
+    and the fused backward is the call the bench times."""
+    rng = np.random.default_rng(B)
+    lens = rng.integers(lo, Lmax + 1, size=B)
+    lens[: B // 8] = Lmax  # some full-length cells: no padding to zero there
+    for pass_ in ("fwd", "bwd"):
+        assert sa.plan_stats(B, H, Lmax, 64, lens, pass_)[2] == 1, pass_
+    case = workloads.random_case(B, H, 64, Lmax, lens, seed=B + 1)
+    t = to_dev(case)
+    got = run_all(t, lens, "fast", fused=True)
+    ref = oracle.attention(host(case["q"]), host(case["k"]), host(case["v"]), lens, do=host(case["do"]))
+    ratios = {k: worst_ratio(host(got[k]), ref[k]) for k in OUTS}
+    print(f"[parity] many short B={B} H={H} Lmax={Lmax} ratios={ratios}", flush=True)
+    for k in OUTS:
+        assert ratios[k] <= 1.0, (k, ratios)
+        assert padded_rows_zero(got[k], lens), f"{k}: padded rows not zero"

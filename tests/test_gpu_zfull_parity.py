@@ -12,8 +12,10 @@ covered, since every head is.
 Workloads (seeded synthetic single-cell-like batches, see workloads.py):
 the headline padded batch (B8 H16 d64 Lmax 2048), the padding sweep at 0 / 25
 / 50 % (B16 H16 d64 Lmax 4096), dense 8K at d = 128 (B4 H16) and the 8K
-log-normal batch with x4 inputs (B8 H12 d64).  The tiny workload is compared
-in test_gpu_parity.py.  Host time: about 2 minutes with 15 workers."""
+log-normal batch with x4 inputs (B8 H12 d64); and one sum of n^2 per head
+cut three ways (4 sequences of 4096, 1024 cells of 256, 4096 cells of 128).
+The tiny workload is compared in test_gpu_parity.py.  Host time: a few
+minutes with 15 workers."""
 import multiprocessing as mp
 import time
 
@@ -36,6 +38,9 @@ FULL = [
     ("sweep_b16h16d64_l4096_pad50", "fast"),
     ("dense_b4h16d128_l8192", "fast"),
     ("cells8k_b8h12d64_l8192_x4", "split"),
+    ("few_b4h16d64_l4096", "fast"),
+    ("many_b1024h16d64_l256", "fast"),
+    ("many_b4096h16d64_l128", "fast"),
 ]
 
 _POOL = None

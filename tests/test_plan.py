@@ -56,6 +56,11 @@ CASES = [
     ("few_heads_long", 1, 4, 8192, [8192]),
     ("many_sequences", 300, 8, 512, list(np.random.default_rng(1).integers(0, 513, 300))),
     ("many_full_sequences", 600, 2, 256, [256] * 599 + [255]),
+    ("short_cells_1024", 1024, 16, 256, [256] * 1024),
+    ("short_cells_4096", 4096, 4, 128, [128] * 4096),
+    ("ragged_cells_3000", 3000, 2, 512, list(np.random.default_rng(2).integers(0, 513, 3000))),
+    ("beyond_one_table", 4500, 1, 64, list(np.random.default_rng(3).integers(0, 65, 4500))),
+    ("wide_lengths", 2100, 1, 70000, [1] * 2099 + [70000]),
 ]
 
 
@@ -72,6 +77,9 @@ def test_schedule_covers_every_tile_once(harness, case, pass_):
     assert r["pairs"] == pairs == r["stats_pairs"], r
     if items == 0 and all(n == L for n in lens):
         assert r["launches"] == 0
+    if B <= (2048 if L > 65535 else 4096) and items > 0:
+        assert r["launches"] == 1, r  # one launch per pass up to a length table's capacity
+    assert r["max_piece_seqs"] <= 64, r
 
 
 @pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))

@@ -61,6 +61,14 @@ WORKLOADS = {
         Workload("cells8k_b8h12d64_l8192_x4", 8, 12, 64, 8192, "lognormal_2000", scale_qkv=4.0,
                  note="160M-class layer shape (12 heads of 64) at 8K; log-normal lengths (median 2000, sigma 0.8) "
                       "clipped to [200, 8192]; Q/K/V scaled by 4 so sigmoid arguments saturate"),
+        # Equal work (sum of n^2 per head) cut three ways: few long sequences,
+        # and many short cells as single-cell batches hold them.
+        Workload("few_b4h16d64_l4096", 4, 16, 64, 4096, "full",
+                 note="4 sequences of 4096 (the long-sequence reference for the two short-cell batches)"),
+        Workload("many_b1024h16d64_l256", 1024, 16, 64, 256, "full",
+                 note="1024 cells of 256 genes: the same sum of n^2 as 4 x 4096"),
+        Workload("many_b4096h16d64_l128", 4096, 16, 64, 128, "full",
+                 note="4096 cells of 128 genes: the same sum of n^2 as 4 x 4096"),
     )
 }
 
