@@ -44,6 +44,27 @@ namespace SIGATTN_ELT {
 namespace kern {
 
 constexpr int kThreads = 256;
+
+// The LDS tile ring of a workgroup: up to six tiles of `elems` 16-bit
+// elements.  A load into one stage is issued while other stages are read.
+// With SEP each stage is a __shared__ array of its own: the compiler can then
+// tell that those reads do not touch the stage being filled and does not make
+// them wait for the load (global -> LDS loads count as outstanding LDS writes
+// until they land).  Without SEP the stages are slices of one array and every
+// LDS read after a load waits for it; the scheduler then keeps fewer values
+// live, which the head-dim-128 backward (one wave per SIMD, at the register
+// limit) needs.  Stages are always named by compile-time indices, so with SEP
+// every access resolves to one array.
+struct Ring {
+  uint16_t* p[6];
+};
+#define SIGATTN_RING(name, n, elems, sep)                                                                  \
+  __shared__ __align__(16) uint16_t name##0[(sep) ? (elems) : (n) * (elems)], name##1[(sep) ? (elems) : 8], \
+      name##2[(sep) ? (elems) : 8], name##3[(sep) ? (elems) : 8], name##4[(sep) ? (elems) : 8],             \
+      name##5[(sep) && (n) > 5 ? (elems) : 8];                                                                \
+  const Ring name = (sep) ? Ring{{name##0, name##1, name##2, name##3, name##4, (n) > 5 ? name##5 : nullptr}}  \
+                          : Ring{{name##0, name##0 + (elems), name##0 + 2 * (elems), name##0 + 3 * (elems),    \
+                                  name##0 + 4 * (elems), (n) > 5 ? name##0 + 5 * (elems) : nullptr}}
 constexpr int kInner = 64;  // rows per inner tile
 
 // Schedule per kernel and head dim (measured on MI355X, same-run A/B):
@@ -95,6 +116,10 @@ template <int D, bool SPLIT, bool PRE, bool WANT_P, bool DSUM = false, int NB>
 __device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[NB], const f32x16 (&dp)[NB], int c, float arg,
                                                e16x8& dh, e16x8& dl, e16x8& ph, e16x8& pl,
                                                float* dsum = nullptr) {
+  // No contraction of dP * p (1 - p) into the sum below: the sum then rounds
+  // the same in every kernel that inlines this, whatever else is scheduled
+  // around it.
+#pragma clang fp contract(off)
   const f32x8 sv = chunk8(sc[c >> 1], c & 1), gv = chunk8(dp[c >> 1], c & 1);
   f32x8 p8, ds;
 #pragma unroll
@@ -362,7 +387,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
                                                                         const uint16_t* __restrict__ V,
                                                                         uint16_t* __restrict__ O, const SeqTable T, const Sched S) {
   constexpr int BQ = 128, BK = kInner, TILE = BK * D;
-  __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
+  SIGATTN_RING(lds, 5, TILE, false);  // K0 K1 K2 V0 V1
 
   if ((int)blockIdx.x >= S.compute_blocks) {
     zero_padded_rows<D>(T, S, (int)blockIdx.x, O, 3, nullptr, 0);
@@ -379,8 +404,8 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uin
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BK, D> dma_k(w, lane, S.sl[1]), dma_v(w, lane, S.sl[2]);
-  auto Kb = [&](int i) { return lds + i * TILE; };
-  auto Vb = [&](int i) { return lds + (3 + i) * TILE; };
+  auto Kb = [&](int i) { return lds.p[i]; };
+  auto Vb = [&](int i) { return lds.p[3 + i]; };
   const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]);
 
@@ -484,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_softmax_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, const SeqTable T, const Sched S) {
   constexpr int BQ = 128, BK = kInner, TILE = BK * D;
-  __shared__ __align__(16) uint16_t lds[5 * TILE];  // K0 K1 K2 V0 V1
+  SIGATTN_RING(lds, 5, TILE, false);  // K0 K1 K2 V0 V1
 
   if ((int)blockIdx.x >= S.compute_blocks) {
     zero_padded_rows<D>(T, S, (int)blockIdx.x, O, 3, nullptr, 0, LSE);
@@ -498,8 +523,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_softmax_kernel(
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BK, D> dma_k(w, lane, S.sl[1]), dma_v(w, lane, S.sl[2]);
-  auto Kb = [&](int i) { return lds + i * TILE; };
-  auto Vb = [&](int i) { return lds + (3 + i) * TILE; };
+  auto Kb = [&](int i) { return lds.p[i]; };
+  auto Vb = [&](int i) { return lds.p[3 + i]; };
   const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]);
 
@@ -579,18 +604,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_softmax_kernel(
 // LDS: K in 3 stages (tile j: transposing reads for dQ; tile j+1: scores;
 // tile j+2: loading), V in 2 stages (tile j: dP; tile j+1: loading).
 // ---------------------------------------------------------------------------
-template <int D>
-constexpr int dq_lds_elems() { return 5 * kInner * D; }  // K0 K1 K2 V0 V1
-
 // The dQ work of block vb of schedule S (a kernel of its own, or the dQ part
-// of the fused backward launch); lds: dq_lds_elems<D>() 16-bit elements.
+// of the fused backward launch); lds: five stages of kInner x D elements.
 template <int D, bool SPLIT, bool SOFTMAX>
-__device__ __forceinline__ void dq_body(uint16_t* __restrict__ lds, int vb, const uint16_t* __restrict__ Q,
+__device__ __forceinline__ void dq_body(const Ring& lds, int vb, const uint16_t* __restrict__ Q,
                                         const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                         const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ,
                                         const float* __restrict__ LSE, const float* __restrict__ DELTA,
                                         const SeqTable& T, const Sched& S) {
-  constexpr int BQ = 128, BK = kInner, TILE = BK * D;
+  constexpr int BQ = 128, BK = kInner;
 
   if (vb >= S.compute_blocks) {
     zero_padded_rows<D>(T, S, vb, dQ, 4, nullptr, 0);
@@ -607,8 +629,8 @@ __device__ __forceinline__ void dq_body(uint16_t* __restrict__ lds, int vb, cons
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BK, D> dma_k(w, lane, S.sl[1]), dma_v(w, lane, S.sl[2]);
-  auto Kb = [&](int i) { return lds + i * TILE; };
-  auto Vb = [&](int i) { return lds + (3 + i) * TILE; };
+  auto Kb = [&](int i) { return lds.p[i]; };
+  auto Vb = [&](int i) { return lds.p[3 + i]; };
   const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]), gs(slice_base(dO, S, it.bh, 3), n, S.sl[3]);
 
@@ -758,7 +780,7 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, const float* __restrict__ LSE,
     const float* __restrict__ DELTA, const SeqTable T, const Sched S) {
-  __shared__ __align__(16) uint16_t lds[dq_lds_elems<D>()];
+  SIGATTN_RING(lds, 5, kInner * D, D == 64);  // K0 K1 K2 V0 V1
   dq_body<D, SPLIT, SOFTMAX>(lds, (int)blockIdx.x, Q, K, V, dO, dQ, LSE, DELTA, T, S);
 }
 
@@ -774,23 +796,21 @@ __global__ __launch_bounds__(kThreads, DqCfg<D>::OCC) void dq_kernel(
 // latency is covered; the next tile's S and dP follow, with the fragments of
 // each K-step read one step ahead.
 // ---------------------------------------------------------------------------
-template <int D>
-constexpr int dkdv_lds_elems() { return 6 * DkdvCfg<D>::BQ * D; }  // Q0 Q1 Q2 G0 G1 G2
 // softmax: lse2 and delta of each inner tile's rows, 3 stages
 template <int D, bool SOFTMAX>
 constexpr int dkdv_row_floats() { return SOFTMAX ? 6 * DkdvCfg<D>::BQ : 4; }
 
 // The dK/dV work of block vb of schedule S (a kernel of its own, or the dK/dV
-// part of the fused backward launch); lds: dkdv_lds_elems<D>() 16-bit
-// elements, rowv: dkdv_row_floats<D, SOFTMAX>() floats.
+// part of the fused backward launch); lds: six stages of BQ x D elements,
+// rowv: dkdv_row_floats<D, SOFTMAX>() floats.
 template <int D, bool SPLIT, bool SOFTMAX, bool DB>
-__device__ __forceinline__ void dkdv_body(uint16_t* __restrict__ lds, float* __restrict__ rowv, int vb,
+__device__ __forceinline__ void dkdv_body(const Ring& lds, float* __restrict__ rowv, int vb,
                                           const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                                           uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                                           const float* __restrict__ LSE, const float* __restrict__ DELTA,
                                           float* __restrict__ DBIAS, const SeqTable& T, const Sched& S) {
-  constexpr int BKV = 128, BQ = DkdvCfg<D>::BQ, TILE = BQ * D, NMB = BQ / 32, NC = BQ / 16;
+  constexpr int BKV = 128, BQ = DkdvCfg<D>::BQ, NMB = BQ / 32, NC = BQ / 16;
 
   if (vb >= S.compute_blocks) {
     zero_padded_rows<D>(T, S, vb, dK, 4, dV, 5, DB ? DBIAS : nullptr);
@@ -807,8 +827,8 @@ __device__ __forceinline__ void dkdv_body(uint16_t* __restrict__ lds, float* __r
   const TrFrag<D> tr(lane);
   const FragAddr<D> fa(l32, hf);
   const TileDma<BQ, D> dma_q(w, lane, S.sl[0]), dma_g(w, lane, S.sl[3]);
-  auto Qb = [&](int i) { return lds + i * TILE; };
-  auto Gb = [&](int i) { return lds + (3 + i) * TILE; };
+  auto Qb = [&](int i) { return lds.p[i]; };
+  auto Gb = [&](int i) { return lds.p[3 + i]; };
   const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]), gs(slice_base(dO, S, it.bh, 3), n, S.sl[3]);
 
@@ -1011,7 +1031,7 @@ __global__ __launch_bounds__(kThreads, DkdvCfg<D>::OCC) void dkdv_kernel(
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     const float* __restrict__ LSE, const float* __restrict__ DELTA, float* __restrict__ DBIAS, const SeqTable T,
     const Sched S) {
-  __shared__ __align__(16) uint16_t lds[dkdv_lds_elems<D>()];
+  SIGATTN_RING(lds, 6, DkdvCfg<D>::BQ * D, D == 64);  // Q0 Q1 Q2 G0 G1 G2
   __shared__ __align__(16) float rowv[dkdv_row_floats<D, SOFTMAX>()];
   dkdv_body<D, SPLIT, SOFTMAX, DB>(lds, rowv, (int)blockIdx.x, Q, K, V, dO, dK, dV, LSE, DELTA, DBIAS, T, S);
 }
@@ -1030,8 +1050,10 @@ bwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const
            const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK,
            uint16_t* __restrict__ dV, const float* __restrict__ LSE, const float* __restrict__ DELTA,
            float* __restrict__ DBIAS, const BwdSched P) {
-  constexpr int E = dq_lds_elems<D>() > dkdv_lds_elems<D>() ? dq_lds_elems<D>() : dkdv_lds_elems<D>();
-  __shared__ __align__(16) uint16_t lds[E];
+  // the two roles use the same stages: dQ items K0 K1 K2 V0 V1, dK/dV items
+  // Q0 Q1 Q2 G0 G1 G2
+  static_assert(kInner == DkdvCfg<D>::BQ, "one stage size for both roles");
+  SIGATTN_RING(lds, 6, kInner * D, D == 64);
   __shared__ __align__(16) float rowv[dkdv_row_floats<D, SOFTMAX>()];
   const int b = (int)blockIdx.x;
   if (b < P.dq_off)
