@@ -670,6 +670,7 @@ __device__ __forceinline__ void dq_body(const Ring& lds, int vb, const uint16_t*
     zero2(gA);
     score_steps<D>(sA, Kb(0), qf, 0, D / 16, fa);
     score_steps<D>(gA, Vb(0), gf, 0, D / 16, fa);
+    __syncthreads();  // V tile 0 is read by every wave before step 0 refills its stage
     auto step = [&](auto phase, int j) {
       constexpr int P = decltype(phase)::value;
       constexpr int kc = P % 3, k1 = (P + 1) % 3, k2 = (P + 2) % 3;
