@@ -390,7 +390,8 @@ def workload_record(r, precision):
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "avg_launch_ms": round(r["kernel_avg_ms"][dom], 5),
                      "executed_mfma_frac": round(tflops(EXECUTED_UNITS[dom][precision == "split"] * r["pair_flops"],
-                                                        r["kernel_avg_ms"][dom]) / PEAK_BF16_TFLOPS, 4)},
+                                                        r["kernel_avg_ms"][dom]) / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic(dom, w.name, precision)},
     }
 
 
