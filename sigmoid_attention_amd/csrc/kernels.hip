@@ -74,7 +74,12 @@ constexpr int kInner = 64;  // rows per inner tile
 // for the forward and dK/dV; dQ keeps the lookahead of its scores.  At
 // d = 128 the forward fits lookahead and two waves per SIMD (1.43x faster
 // than one wave per SIMD on the dense 8K batch).
-template <int D> struct FwdCfg { static constexpr bool LA = D != 64; static constexpr int OCC = D == 64 ? 4 : 2; };
+// Forward waves per SIMD: 4 at d = 64 (3 in split precision, whose hi + lo
+// packs do not fit 128 registers without spilling), 2 at d = 128.
+template <int D, bool SPLIT = false> struct FwdCfg {
+  static constexpr bool LA = D != 64;
+  static constexpr int OCC = D == 64 ? (SPLIT ? 3 : 4) : 2;
+};
 // At d = 128 (one wave per SIMD, no other wave to overlap with) both backward
 // kernels compute the next tile's S and dP inside the chunk loop, with every
 // LDS fragment read issued a chunk ahead: DPLA in dQ, ROLL in dK/dV.
@@ -382,7 +387,7 @@ __device__ __forceinline__ void run_steps(int n, Step&& step) {
 // products on such tiles are unused).
 // ---------------------------------------------------------------------------
 template <int D, bool SPLIT, bool LA = FwdCfg<D>::LA>
-__global__ __launch_bounds__(kThreads, FwdCfg<D>::OCC) void fwd_kernel(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(kThreads, (FwdCfg<D, SPLIT>::OCC)) void fwd_kernel(const uint16_t* __restrict__ Q,
                                                                         const uint16_t* __restrict__ K,
                                                                         const uint16_t* __restrict__ V,
                                                                         uint16_t* __restrict__ O, const SeqTable T, const Sched S) {
