@@ -13,10 +13,15 @@
 //   the fp16 build of this file);
 // * the tile streamed by the inner loop (K/V in the forward and dQ kernels,
 //   Q/dO in the dK/dV kernel) is loaded straight from global memory into LDS
-//   (buffer_load ... lds), one step ahead, with hardware zero-fill past the
+//   (buffer_load ... lds), two steps ahead, with hardware zero-fill past the
 //   sequence end; one LDS copy per tile serves both the 16-byte fragment
 //   reads and the transposing reads (see device_common.h): one barrier per
-//   inner step and no VALU work for staging;
+//   inner step and no VALU work for staging; in the d = 64 backward each
+//   stage of the tile ring is an LDS array of its own (SIGATTN_RING), so the
+//   step's reads do not wait for the load in flight;
+// * fast precision folds the score scale into the operand a wave holds in
+//   registers for its whole item, so sigma costs three VALU instructions per
+//   score (exp, fma, rcp; see sigmoid_pre);
 // * the score product's output registers are directly the B operand of the
 //   second product (see device_common.h): P and dS never leave registers and
 //   are never stored; the transposed A operand is read with ds_read_b64_tr_b16
