@@ -192,10 +192,12 @@ sigattn_status sigattn_bwd_dkdv(const sigattn_args *args, const void *q, const v
 /* The whole backward in one call: dQ (as sigattn_bwd_dq), dK and dV (as
  * sigattn_bwd_dkdv) and, if dbias is not NULL, the bias-gradient rows (as
  * sigattn_bwd_dkdv_dbias).  Results are bitwise those of the separate calls.
- * Both sides normally run in ONE fused launch: the dK/dV workgroups first,
- * then the dQ workgroups, which fill the CUs the dK/dV work leaves idle
- * towards its end (§2C's two backward kernels, scheduled together; still no
- * atomics: every output row has one writer).  args->strides, if set, has 7
+ * At d = 64 both sides normally run in ONE fused launch: the dK/dV
+ * workgroups first, then the dQ workgroups, which fill the CUs the dK/dV work
+ * leaves idle towards its end (§2C's two backward kernels, scheduled
+ * together; still no atomics: every output row has one writer).  At d = 128
+ * the two kernels run at different occupancies, and the dK/dV and dQ
+ * launches run in turn on args->stream.  args->strides, if set, has 7
  * entries: q, k, v, dout, dq, dk, dv.  Same checks and errors as the separate
  * calls (dq, dk, dv are outputs; dbias is checked like a row output). */
 sigattn_status sigattn_bwd(const sigattn_args *args, const void *q, const void *k, const void *v,
@@ -248,8 +250,8 @@ sigattn_status sigattn_softmax_bwd_dq(const sigattn_args *args, const void *q, c
 sigattn_status sigattn_softmax_bwd_dkdv(const sigattn_args *args, const void *q, const void *k,
                                         const void *v, const void *dout, const float *lse2,
                                         const float *delta, void *dk, void *dv);
-/* Both softmax backward kernels in one fused launch (after
- * sigattn_softmax_bwd_prep), as sigattn_bwd does for sigmoid; strides order
+/* Both softmax backward kernels (after sigattn_softmax_bwd_prep), in one
+ * fused launch at d = 64 as sigattn_bwd does for sigmoid; strides order
  * q, k, v, dout, dq, dk, dv. */
 sigattn_status sigattn_softmax_bwd(const sigattn_args *args, const void *q, const void *k, const void *v,
                                    const void *dout, const float *lse2, const float *delta, void *dq,
@@ -286,7 +288,8 @@ const char *sigattn_status_str(sigattn_status status);
  * each), the (outer tile, inner tile) pairs those items visit — fully padded
  * tiles are not counted because they are never computed — and the number of
  * kernel launches.  For SIGATTN_PASS_BWD: the dK/dV and dQ sides summed,
- * and 1 launch when both sides fit one (the fused launch of sigattn_bwd).
+ * and 1 launch when sigattn_bwd fuses them (d = 64, both sides fitting one
+ * launch each).
  * Any of the output pointers may be NULL.  Validates args (shape, seqlens,
  * bias, precision) as the compute calls do. */
 sigattn_status sigattn_plan_stats(const sigattn_args *args, int32_t pass, int64_t *work_items,

@@ -280,7 +280,7 @@ def bwd_dkdv_dbias(q, k, v, dout, seqlens, dk=None, dv=None, dbias=None, bias_mo
 
 def bwd(q, k, v, dout, seqlens, dq=None, dk=None, dv=None, dbias=None, bias_rows=False, bias_mode="seqlen",
         bias_arg=0.0, precision="fast", stream=None, layout: str = "bhld", causal: bool = False):
-    """The whole backward in one call (normally one fused launch): returns
+    """The whole backward in one call (one fused launch at d = 64): returns
     (dQ, dK, dV), plus the bias-gradient rows if `bias_rows` or `dbias` is
     given.  Bitwise the results of bwd_dq and bwd_dkdv(_dbias)."""
     import torch
@@ -440,7 +440,7 @@ def softmax_bwd_dkdv(q, k, v, dout, lse2, delta, seqlens, dk=None, dv=None, prec
 def softmax_bwd(q, k, v, o, dout, lse2, seqlens, dq=None, dk=None, dv=None, delta=None, precision="fast",
                 stream=None, layout="bhld", causal=False):
     """Softmax attention backward: delta = rowsum(dO * O), then the dQ and
-    dK/dV kernels in one fused launch.  Returns (dQ, dK, dV)."""
+    dK/dV kernels (one fused launch at d = 64).  Returns (dQ, dK, dV)."""
     import torch
 
     delta = softmax_bwd_prep(o, dout, seqlens, delta, precision=precision, stream=stream, layout=layout)
@@ -449,7 +449,7 @@ def softmax_bwd(q, k, v, o, dout, lse2, seqlens, dq=None, dk=None, dv=None, delt
 
 def softmax_bwd_fused(q, k, v, dout, lse2, delta, seqlens, dq=None, dk=None, dv=None, precision="fast", stream=None,
                       layout="bhld", causal=False):
-    """dQ, dK and dV of the softmax path in one fused launch, given lse2 and
+    """dQ, dK and dV of the softmax path (one fused launch at d = 64), given lse2 and
     delta (softmax_bwd_prep).  Returns (dQ, dK, dV)."""
     import torch
 

@@ -259,10 +259,17 @@ sigattn_status run(const sigattn_args* a, int32_t pass, const void* const* t, in
   return SIGATTN_OK;
 }
 
-// The backward of both sides.  When each side's schedule is one launch (all
-// but batches beyond one launch's piece or zero-fill capacity), both run in
-// one fused launch, the dK/dV blocks first; otherwise the dK/dV launches run,
-// then the dQ launches.  t: q, k, v, dout, dq, dk, dv (args->strides order).
+// Whether the backward of both sides runs as one fused launch: at head dim 64
+// when each side's schedule is one launch (all but batches beyond one
+// launch's length table).  At head dim 128 the dK/dV kernel runs one wave per
+// SIMD and the dQ kernel two, so they run as their own launches.
+bool fused_bwd(int32_t d, size_t dkdv_launches, size_t dq_launches) {
+  return d == 64 && dkdv_launches == 1 && dq_launches == 1;
+}
+
+// The backward of both sides: one fused launch (fused_bwd), the dK/dV
+// blocks first; otherwise the dK/dV launches run, then the dQ launches.
+// t: q, k, v, dout, dq, dk, dv (args->strides order).
 // lse2/delta: the softmax path; dbias: the sigmoid bias-gradient rows.
 sigattn_status run_bwd(const sigattn_args* a, const void* const* t, const float* lse2, const float* delta,
                        float* dbias) {
@@ -284,7 +291,7 @@ sigattn_status run_bwd(const sigattn_args* a, const void* const* t, const float*
   const hipStream_t st = (hipStream_t)a->stream;
   const auto impl_fused = f16(a) ? sigattn::f16::launch_bwd_fused : sigattn::bf16::launch_bwd_fused;
   (void)hipGetLastError();
-  if (pk.size() == 1 && pq.size() == 1 && pk[0].T.b_base == pq[0].T.b_base && pk[0].T.nseq == pq[0].T.nseq) {
+  if (fused_bwd(a->d, pk.size(), pq.size()) && pk[0].T.b_base == pq[0].T.b_base && pk[0].T.nseq == pq[0].T.nseq) {
     sigattn::BwdSched P;  // 14.5 KB, copied into the launch's kernel arguments
     P.T = pk[0].T;
     P.kv = pk[0].sched;
@@ -562,13 +569,13 @@ sigattn_status sigattn_plan_stats(const sigattn_args* a, int32_t pass, int64_t* 
   if (pass != SIGATTN_PASS_BWD && tile_rows(pass, &o, &i) != SIGATTN_OK) return SIGATTN_ERR_PASS;
   const sigattn_status s = check_args(a);
   if (s != SIGATTN_OK) return s;
-  if (pass == SIGATTN_PASS_BWD) {  // both sides; one fused launch when each side fits one
+  if (pass == SIGATTN_PASS_BWD) {  // both sides; one launch when run_bwd fuses them
     sigattn::PlanStats sk, sq;
     const size_t lk = sigattn::build_plan(plan_input(a, SIGATTN_PASS_BWD_DKDV), &sk).size();
     const size_t lq = sigattn::build_plan(plan_input(a, SIGATTN_PASS_BWD_DQ), &sq).size();
     if (work_items) *work_items = sk.items + sq.items;
     if (tile_pairs) *tile_pairs = sk.pairs + sq.pairs;
-    if (launches) *launches = (lk == 1 && lq == 1) ? 1 : (int32_t)(lk + lq);
+    if (launches) *launches = fused_bwd(a->d, lk, lq) ? 1 : (int32_t)(lk + lq);
     return SIGATTN_OK;
   }
   sigattn::PlanStats st;

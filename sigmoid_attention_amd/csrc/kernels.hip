@@ -33,8 +33,9 @@
 //   rescale, and the inner tiles may be visited in any order;
 // * padded output rows are written as 0 by trailing workgroups of the same
 //   launch (dispatched last, they fill the tail), so each call is one launch;
-// * the two backward kernels can run as one launch (bwd_kernel): the dQ
-//   workgroups fill the CUs that the dK/dV workgroups leave idle at the end;
+// * at d = 64 the two backward kernels run as one launch (bwd_kernel): the
+//   dQ workgroups fill the CUs that the dK/dV workgroups leave idle at the
+//   end;
 // * variants: a causal mask (tiles above the diagonal skipped, the straddling
 //   tile masked in registers), a per-head bias read from device memory with
 //   its gradient (per-key sums of dS), and softmax attention on the same
@@ -85,13 +86,15 @@ template <int D, bool SPLIT = false> struct FwdCfg {
   static constexpr bool LA = D != 64;
   static constexpr int OCC = D == 64 ? (SPLIT ? 3 : 4) : 2;
 };
-// At d = 128 (one wave per SIMD, no other wave to overlap with) both backward
-// kernels compute the next tile's S and dP inside the chunk loop, with every
-// LDS fragment read issued a chunk ahead: DPLA in dQ, ROLL in dK/dV.
+// The dQ kernel runs two waves per SIMD at either head dim (at d = 128 one
+// 16-byte value is spilled and reloaded once per step).  The dK/dV kernel
+// runs one wave per SIMD at d = 128 (its accumulators alone take 128
+// registers); with no other wave to overlap with, it computes the next
+// tile's S and dP inside the chunk loop, with every LDS fragment read issued
+// a chunk ahead (ROLL).  Their occupancies differ there, so at d = 128 the
+// backward runs as two launches rather than the fused one.
 template <int D> struct DqCfg {
-  static constexpr bool LA = true;
-  static constexpr bool DPLA = D == 128;
-  static constexpr int OCC = D == 64 ? 2 : 1;
+  static constexpr int OCC = 2;
 };
 template <int D> struct DkdvCfg {
   static constexpr int BQ = 64;
@@ -662,79 +665,6 @@ __device__ __forceinline__ void dq_body(const Ring& lds, int vb, const uint16_t*
 
   const int nk = S.causal ? min((n + BK - 1) / BK, causal_inner_end(it.tile, BQ, BK)) : (n + BK - 1) / BK;
   const int q0w = it.tile * BQ + 32 * w;  // this wave's first query
-  if constexpr (DqCfg<D>::DPLA) {
-    // S^T and dP^T of tile j are both computed during step j-1, spread over
-    // its chunks with their A fragments read at the start of each chunk, so
-    // every chunk mixes the next tile's score products, the VALU work on this
-    // tile and this tile's dQ products.  K: 3 stages (tile j for dQ, j+1 for
-    // scores, j+2 loading); V: 2 stages (j+1 for dP, j+2 loading).
-    constexpr int KSQ = D / 64;  // score K-steps per chunk
-    dma_k.load(ks, 0, Kb(0));
-    dma_k.load(ks, BK, Kb(1));
-    dma_v.load(vs, 0, Vb(0));
-    dma_v.load(vs, BK, Vb(1));
-    vm_drain();
-    __syncthreads();
-    f32x16 sA[2], sB[2], gA[2], gB[2];
-    zero2(sA);
-    zero2(gA);
-    score_steps<D>(sA, Kb(0), qf, 0, D / 16, fa);
-    score_steps<D>(gA, Vb(0), gf, 0, D / 16, fa);
-    __syncthreads();  // V tile 0 is read by every wave before step 0 refills its stage
-    auto step = [&](auto phase, int j) {
-      constexpr int P = decltype(phase)::value;
-      constexpr int kc = P % 3, k1 = (P + 1) % 3, k2 = (P + 2) % 3;
-      f32x16(&cur)[2] = pick<P>(sA, sB);
-      f32x16(&nxt)[2] = pick<P + 1>(sA, sB);
-      f32x16(&dp)[2] = pick<P>(gA, gB);
-      f32x16(&dnx)[2] = pick<P + 1>(gA, gB);
-      dma_k.load(ks, (j + 2) * BK, Kb(k2));     // stage of K tile j-1 (its dQ reads ended at the last barrier)
-      dma_v.load(vs, (j + 2) * BK, Vb(P % 2));  // stage of V tile j (read during step j-1)
-      const uint16_t* Kt = Kb(kc);
-      const uint16_t* Kn = Kb(k1);
-      const uint16_t* Vn = Vb((P + 1) % 2);
-      if (S.causal && j * BK + BK - 1 > q0w) mask_causal_cols(cur, j * BK, qrow, hf, masked_score<PRE>());
-      e16x8 dh[4], dl[4], unused_h, unused_l;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        e16x8 fs[KSQ][2], fg[KSQ][2], tq[D / 32];
-#pragma unroll
-        for (int k = 0; k < KSQ; ++k)
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            fs[k][mb] = fa.read(Kn, mb, c * KSQ + k);
-            fg[k][mb] = fa.read(Vn, mb, c * KSQ + k);
-          }
-        if (c > 0) read_value_frags<D>(tq, tr, Kt, c - 1);
-        sched_fence();
-        if constexpr (SOFTMAX)
-          dsoftmax_chunk_col<D, SPLIT>(cur, dp, c, lse2, dlt, dh[c], dl[c]);
-        else
-          dsigmoid_chunk<D, SPLIT, PRE, false>(cur, dp, c, sarg, dh[c], dl[c], unused_h, unused_l);
-        if (c == 0) {
-          zero2(nxt);
-          zero2(dnx);
-        }
-#pragma unroll
-        for (int k = 0; k < KSQ; ++k)
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            nxt[mb] = mfma(fs[k][mb], qf[c * KSQ + k], nxt[mb]);
-            dnx[mb] = mfma(fg[k][mb], gf[c * KSQ + k], dnx[mb]);
-          }
-        if (c > 0) value_chunk_pre<D, SPLIT>(acc, tq, dh[c - 1], dl[c - 1]);
-        sched_fence();
-      }
-      {
-        e16x8 tq[D / 32];
-        read_value_frags<D>(tq, tr, Kt, 3);
-        value_chunk_pre<D, SPLIT>(acc, tq, dh[3], dl[3]);
-      }
-      vm_drain();
-      __syncthreads();
-    };
-    run_steps(nk, step);
-  } else {
   dma_k.load(ks, 0, Kb(0));
   dma_k.load(ks, BK, Kb(1));
   dma_v.load(vs, 0, Vb(0));
@@ -774,7 +704,6 @@ __device__ __forceinline__ void dq_body(const Ring& lds, int vb, const uint16_t*
     __syncthreads();
   };
   run_steps(nk, step);
-  }
 
   if (qrow < n) {
     const float scale = S.out_scale;
@@ -1249,11 +1178,9 @@ hipError_t launch_bwd_dkdv(int d, bool split, const Launch& L, const void* q, co
 hipError_t launch_bwd_fused(int d, bool split, const BwdSched& P, int32_t blocks, const void* q, const void* k,
                             const void* v, const void* g, void* dq, void* dk, void* dv, const float* lse2,
                             const float* delta, float* dbias, hipStream_t st) {
-  if (d == 64)
-    return split ? kern::launch_bwd_fused_d<64, true>(P, blocks, q, k, v, g, dq, dk, dv, lse2, delta, dbias, st)
-                 : kern::launch_bwd_fused_d<64, false>(P, blocks, q, k, v, g, dq, dk, dv, lse2, delta, dbias, st);
-  return split ? kern::launch_bwd_fused_d<128, true>(P, blocks, q, k, v, g, dq, dk, dv, lse2, delta, dbias, st)
-               : kern::launch_bwd_fused_d<128, false>(P, blocks, q, k, v, g, dq, dk, dv, lse2, delta, dbias, st);
+  if (d != 64) return hipErrorInvalidValue;  // d = 128 runs the two launches (see DqCfg)
+  return split ? kern::launch_bwd_fused_d<64, true>(P, blocks, q, k, v, g, dq, dk, dv, lse2, delta, dbias, st)
+               : kern::launch_bwd_fused_d<64, false>(P, blocks, q, k, v, g, dq, dk, dv, lse2, delta, dbias, st);
 }
 
 hipError_t launch_bias_grad(int32_t B, int32_t H, int32_t Lmax, const float* dbias, float* db, hipStream_t st) {

@@ -62,7 +62,7 @@ class _SigmoidAttention(torch.autograd.Function):
         dq = dk = dv = db = None
         want_db = head_bias is not None and ctx.needs_input_grad[3]
         want_kv = ctx.needs_input_grad[1] or ctx.needs_input_grad[2] or want_db
-        if ctx.needs_input_grad[0] and want_kv:  # one fused launch for both sides
+        if ctx.needs_input_grad[0] and want_kv:  # both sides in one call (one fused launch at d = 64)
             out = _binding.bwd(q, k, v, do, lens, bias_rows=want_db, **kw)
             dq, dk, dv = out[:3]
             if want_db:

@@ -348,6 +348,8 @@ def test_fused_backward_pass_in_validate_and_plan_stats():
     q = sa.plan_stats(2, 2, 128, 64, lens, "bwd_dq")
     both = sa.plan_stats(2, 2, 128, 64, lens, "bwd")
     assert both[0] == kv[0] + q[0] and both[1] == kv[1] + q[1] and both[2] == 1
+    # at d = 128 the two sides run at different occupancies: two launches
+    assert sa.plan_stats(2, 2, 128, 128, lens, "bwd")[2] == 2
     # beyond one launch's length table (4096 sequences): each side runs two
     # launches and the backward runs them in turn instead of one fused launch
     many = [64] * 5000
