@@ -357,47 +357,49 @@ __device__ __forceinline__ float item_bias_factor(const Sched& S, const Item& it
   return S.bias_kind == 0 ? (float)it.n : bias_factor(c2);
 }
 
-// Work item of block vb of this schedule's part of the grid (see plan.h);
-// false for idle blocks.  Uniform across the workgroup.  A part starts at a
-// multiple of 8, so vb & 7 is still the block's XCD.
-// The same result as decode_item; the walk over a piece's sequences reads
-// their lengths eight (or four, for 32-bit lengths) at a time with one
-// 16-byte scalar load, so a piece of 64 short sequences costs 8 dependent
-// loads rather than 64.
+// The work item of block vb (list x = vb % 8, position j = vb / 8), as the
+// host's decode_item computes it, or false for an idle block; uniform across
+// the workgroup.  The piece comes from a binary search over the list's first
+// positions.  In a piece of several short sequences (at most 64) the search
+// for the sequence is spread over the wave instead of walked: one lane per
+// sequence reads its length, the lanes' item counts are summed up to each
+// lane, and the first lane whose sum passes the item's offset names the
+// sequence: one round of independent loads where the walk chained up to
+// eight, which cost 13-16 % of the time of a batch of 4096 sequences of 128.
 __device__ __forceinline__ bool find_item(const SeqTable& T, const Sched& S, int vb, Item& it) {
   const int32_t x = vb & 7, j = vb >> 3;
   if (j >= S.xcd_items[x]) return false;
+  const int32_t lane = (int32_t)(threadIdx.x & 63);
   int32_t lo = S.xcd_begin[x], hi = S.xcd_begin[x + 1] - 1;
   while (lo < hi) {  // last piece whose first list position is <= j
     const int32_t mid = (lo + hi + 1) >> 1;
     if (S.item0[mid] <= j) lo = mid;
     else hi = mid - 1;
   }
-  const int32_t i = j - S.item0[lo];
   const int32_t ns = S.ns[lo], nh = S.nh[lo];
-  int32_t s = S.s0[lo], nt = S.nt[lo], t0 = S.t0[lo], r = i;
+  int32_t s = S.s0[lo], nt = S.nt[lo], t0 = S.t0[lo], r = j - S.item0[lo];
   if (ns > 1) {
-    const int32_t send = s + ns - 1;
-    const int per = T.wide ? 4 : 8;  // lengths per 16-byte word
-    bool found = false;
-    for (int32_t g = s - s % per; !found; g += per) {
-      const u32x4 w = *(const u32x4*)(T.wide ? (const void*)&T.n32[g] : (const void*)&T.n16[g]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (e >= per) break;
-        const int32_t q = g + e;
-        if (found || q < s) continue;
-        const int32_t nq = T.wide ? (int32_t)w[e] : (int32_t)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        const int32_t tiles = (nq + S.outer_rows - 1) / S.outer_rows;
-        if (r < nh * tiles || q == send) {
-          s = q;
-          nt = tiles;
-          found = true;
-        } else {
-          r -= nh * tiles;
-        }
-      }
+    const int32_t q = s + (lane < ns ? lane : ns - 1);  // a sequence of the piece
+    int32_t nq;
+    if (T.wide) nq = (int32_t)T.n32[q];
+    else nq = (int32_t)T.n16[q];
+    const int32_t tiles = lane < ns ? (nq + S.outer_rows - 1) / S.outer_rows : 0;
+    const int32_t cnt = nh * tiles;
+    // items of sequences s .. s + lane: each bit plane of cnt as a ballot,
+    // counted over the lanes up to this one (as many planes as the largest
+    // count has bits)
+    const uint64_t upto = lane == 63 ? ~0ull : (2ull << lane) - 1;
+    int32_t incl = 0;
+    for (int b = 0;; ++b) {
+      const uint64_t plane = __ballot((cnt >> b) & 1);
+      if (__ballot((cnt >> b) != 0) == 0) break;
+      incl += __popcll(plane & upto) << b;
     }
+    const uint64_t m = __ballot(lane < ns && incl > r);
+    const int32_t k = __builtin_amdgcn_readfirstlane(m ? __ffsll((long long)m) - 1 : ns - 1);
+    r -= __builtin_amdgcn_readfirstlane(__shfl(incl - cnt, k, 64));
+    nt = __builtin_amdgcn_readfirstlane(__shfl(tiles, k, 64));
+    s += k;
     t0 = 0;
   }
   const int32_t hoff = r / nt;
