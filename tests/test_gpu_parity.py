@@ -82,11 +82,15 @@ def test_saturated_scores_split_every_element():
     check_full(case, "split", label="x4 ragged")
 
 
-@pytest.mark.parametrize("B,H,Lmax,lo", [(1024, 2, 256, 1), (4096, 1, 128, 100)], ids=["B1024", "B4096"])
+@pytest.mark.parametrize("B,H,Lmax,lo", [(1024, 2, 256, 1), (4096, 1, 128, 100), (1536, 3, 512, 1)],
+                         ids=["B1024", "B4096", "B1536-mixed"])
 def test_many_short_sequences_every_element(B, H, Lmax, lo):
     """Single-cell batches of many short cells: every pass is one launch
     (pieces span many sequences; the lengths travel in the kernel arguments),
-    and the fused backward is the call the bench times."""
+    and the fused backward is the call the bench times.  The mixed batch has
+    1 to 4 tiles per sequence and 3 heads, so the sequences of one piece
+    carry different item counts (up to 12) for the kernels' wave-wide
+    search."""
     rng = np.random.default_rng(B)
     lens = rng.integers(lo, Lmax + 1, size=B)
     lens[: B // 8] = Lmax  # some full-length cells: no padding to zero there
