@@ -47,6 +47,7 @@ if ROOT not in sys.path:
 
 METRIC = "valid-token TFLOPS fwd/bwd, sigmoid attn d=64 L≤8K padded; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published (no sparsity)
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "sigmoid_attention_amd", "csrc", "kernels.hip")
 # Algorithmic FLOP per valid (query, key) pair and head dim, per kernel:
@@ -58,6 +59,13 @@ KERNEL_FLOP_UNITS = {"fwd": 4, "bwd": 10, "bwd_dq": 2, "bwd_dkdv": 8}
 # the backward recomputes S and dP on the dQ side, and split precision doubles
 # the products that take P or dX.
 EXECUTED_UNITS = {"fwd": (4, 6), "bwd": (14, 20), "bwd_dq": (6, 8), "bwd_dkdv": (8, 12)}
+# ... except where sigattn_bwd runs the one-tile backward (every sequence
+# within one 128-row tile, head dim 64, fast precision, no mask): S and dP
+# once, so it issues exactly the algorithmic 10.
+ONE_TILE_EXECUTED = 10
+# Algorithmic HBM bytes per launch: each input's valid rows read once, each
+# output written whole (padded rows as zeros), as (inputs, outputs) counts.
+KERNEL_TENSORS = {"fwd": (3, 1), "bwd": (4, 3), "bwd_dq": (4, 1), "bwd_dkdv": (4, 2)}
 # The softmax comparison path adds a memory pass (delta = rowsum(dO * O)) that
 # counts no FLOPs; its other kernels follow the same convention.
 
@@ -68,6 +76,38 @@ def pair_flops(seqlens, H, d, causal=False):
     n = np.asarray(seqlens, dtype=np.float64)
     pairs = n * (n + 1) / 2 if causal else n * n
     return float(H * d * pairs.sum())
+
+
+def one_tile_bwd(w, precision, causal=False) -> bool:
+    """Whether sigattn_bwd runs the one-tile backward for this workload."""
+    return w.d == 64 and precision == "fast" and not causal and w.Lmax <= 128
+
+
+def executed_units(kname, w, precision, causal=False):
+    if kname == "bwd" and one_tile_bwd(w, precision, causal):
+        return ONE_TILE_EXECUTED
+    return EXECUTED_UNITS[kname][precision == "split"]
+
+
+def kernel_bytes(kname, seqlens, w) -> float:
+    """Algorithmic HBM bytes of one launch (16-bit elements)."""
+    ins, outs = KERNEL_TENSORS[kname]
+    valid = float(np.sum(np.asarray(seqlens, dtype=np.float64))) * w.H * w.d * 2
+    return ins * valid + outs * float(w.B) * w.H * w.Lmax * w.d * 2
+
+
+def roofline_bound(flops, nbytes, ms):
+    """The roofline that bounds a launch of `flops` and `nbytes` (the lower of
+    the MFMA and HBM times) and the fraction of each peak achieved."""
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    hbm = flops / nbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    return {"bound": "hbm" if hbm else "mfma",
+            "achieved": round(gbs if hbm else tf, 2), "peak": PEAK_HBM_GBS if hbm else PEAK_BF16_TFLOPS,
+            "unit": "GB/s" if hbm else "TFLOP/s",
+            "frac": round(gbs / PEAK_HBM_GBS if hbm else tf / PEAK_BF16_TFLOPS, 4),
+            "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "bytes_per_launch": nbytes, "flop_per_launch": flops}
 
 
 def kernel_source_hash() -> str:
@@ -378,7 +418,11 @@ def workload_record(r, precision):
     bwd_ms = sum(v_ for k_, v_ in r["kernel_avg_ms"].items() if k_.startswith("bwd"))
     timed = [k_ for k_ in KERNEL_FLOP_UNITS if k_ in r["kernel_avg_ms"]]
     dom = max(timed, key=r["kernel_avg_ms"].get)
-    achieved = tflops(KERNEL_FLOP_UNITS[dom] * r["pair_flops"], r["kernel_avg_ms"][dom])
+    roof = roofline_bound(KERNEL_FLOP_UNITS[dom] * r["pair_flops"], kernel_bytes(dom, n, w), r["kernel_avg_ms"][dom])
+    roof.update({"kernel": dom, "avg_launch_ms": round(r["kernel_avg_ms"][dom], 5),
+                 "executed_mfma_frac": round(tflops(executed_units(dom, w, precision) * r["pair_flops"],
+                                                    r["kernel_avg_ms"][dom]) / PEAK_BF16_TFLOPS, 4),
+                 "traffic": load_traffic(dom, w.name, precision)})
     return {
         "B": w.B, "H": w.H, "d": w.d, "Lmax": w.Lmax, "seqlens": [int(x) for x in n], "precision": precision,
         "value": round(tflops(r["fwd_flops"] + r["bwd_flops"], r["step_ms"]), 2),
@@ -386,12 +430,7 @@ def workload_record(r, precision):
         "fwd_tflops": round(tflops(r["fwd_flops"], fwd_ms), 2),
         "bwd_tflops": round(tflops(r["bwd_flops"], bwd_ms), 2),
         "kernel_avg_ms": {k_: round(v_, 5) for k_, v_ in r["kernel_avg_ms"].items()},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "avg_launch_ms": round(r["kernel_avg_ms"][dom], 5),
-                     "executed_mfma_frac": round(tflops(EXECUTED_UNITS[dom][precision == "split"] * r["pair_flops"],
-                                                        r["kernel_avg_ms"][dom]) / PEAK_BF16_TFLOPS, 4),
-                     "traffic": load_traffic(dom, w.name, precision)},
+        "roofline": roof,
     }
 
 
@@ -537,13 +576,12 @@ def main():
     dominant = max(timed, key=r["kernel_avg_ms"].get)
     dom_flops = KERNEL_FLOP_UNITS[dominant] * r["pair_flops"]
     achieved = tflops(dom_flops, r["kernel_avg_ms"][dominant])
-    roofline = {
-        "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+    roofline = roofline_bound(dom_flops, kernel_bytes(dominant, n, w), r["kernel_avg_ms"][dominant])
+    roofline.update({
         "traffic": load_traffic(dominant, name, precision),
         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-        "kernel": dominant, "flop_per_launch": dom_flops,
-        "executed_mfma_frac": round(tflops(EXECUTED_UNITS[dominant][precision == "split"] * r["pair_flops"],
+        "kernel": dominant,
+        "executed_mfma_frac": round(tflops(executed_units(dominant, w, precision, a.causal) * r["pair_flops"],
                                            r["kernel_avg_ms"][dominant]) / PEAK_BF16_TFLOPS, 4),
         "avg_launch_ms": round(r["kernel_avg_ms"][dominant], 5),
         "per_kernel": {
@@ -552,7 +590,7 @@ def main():
                      "algorithmic_tflops": round(tflops(KERNEL_FLOP_UNITS[kname] * r["pair_flops"],
                                                         r["kernel_avg_ms"][kname]), 2)}
             for kname in timed},
-    }
+    })
     if not a.no_probe:  # the chip's sustained MFMA rate and clock, right after the timed region
         pr = sa.probe_mfma()
         roofline["measured_mfma_peak"] = {"tflops": round(pr["tflops"], 1),

@@ -267,6 +267,15 @@ bool fused_bwd(int32_t d, size_t dkdv_launches, size_t dq_launches) {
   return d == 64 && dkdv_launches == 1 && dq_launches == 1;
 }
 
+// Whether the sigmoid backward runs as the one-tile kernel (launch_bwd_small):
+// head dim 64, fast precision, no mask, no bias gradient, every sequence
+// within one 128-row tile.
+bool small_bwd(const sigattn_args* a, bool softmax, bool dbias) {
+  static_assert(kDkdvOuter == 128, "the one-tile kernel's rows are the dK/dV schedule's tiles");
+  return a->d == 64 && a->precision == SIGATTN_PREC_FAST && a->mask != SIGATTN_MASK_CAUSAL && !softmax && !dbias &&
+         a->Lmax <= kDkdvOuter;
+}
+
 // The backward of both sides: one fused launch (fused_bwd), the dK/dV
 // blocks first; otherwise the dK/dV launches run, then the dQ launches.
 // t: q, k, v, dout, dq, dk, dv (args->strides order).
@@ -291,6 +300,15 @@ sigattn_status run_bwd(const sigattn_args* a, const void* const* t, const float*
   const hipStream_t st = (hipStream_t)a->stream;
   const auto impl_fused = f16(a) ? sigattn::f16::launch_bwd_fused : sigattn::bf16::launch_bwd_fused;
   (void)hipGetLastError();
+  if (small_bwd(a, lse2 != nullptr, dbias != nullptr)) {
+    const View vq = views(a, tq, 5, kDq)[4];
+    for (const Launch& L : pk)
+      if ((f16(a) ? sigattn::f16::launch_bwd_small : sigattn::bf16::launch_bwd_small)(
+              L, t[0], t[1], t[2], t[3], const_cast<void*>(t[4]), const_cast<void*>(t[5]), const_cast<void*>(t[6]),
+              vq.sb, vq.sh, (int32_t)vq.sl, st) != hipSuccess)
+        return SIGATTN_ERR_HIP;
+    return SIGATTN_OK;
+  }
   if (fused_bwd(a->d, pk.size(), pq.size()) && pk[0].T.b_base == pq[0].T.b_base && pk[0].T.nseq == pq[0].T.nseq) {
     sigattn::BwdSched P;  // 14.5 KB, copied into the launch's kernel arguments
     P.T = pk[0].T;
@@ -575,7 +593,8 @@ sigattn_status sigattn_plan_stats(const sigattn_args* a, int32_t pass, int64_t* 
     const size_t lq = sigattn::build_plan(plan_input(a, SIGATTN_PASS_BWD_DQ), &sq).size();
     if (work_items) *work_items = sk.items + sq.items;
     if (tile_pairs) *tile_pairs = sk.pairs + sq.pairs;
-    if (launches) *launches = fused_bwd(a->d, lk, lq) ? 1 : (int32_t)(lk + lq);
+    if (launches)
+      *launches = small_bwd(a, false, false) ? (int32_t)lk : fused_bwd(a->d, lk, lq) ? 1 : (int32_t)(lk + lq);
     return SIGATTN_OK;
   }
   sigattn::PlanStats st;

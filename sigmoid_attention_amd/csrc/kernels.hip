@@ -35,7 +35,9 @@
 //   launch (dispatched last, they fill the tail), so each call is one launch;
 // * at d = 64 the two backward kernels run as one launch (bwd_kernel): the
 //   dQ workgroups fill the CUs that the dK/dV workgroups leave idle at the
-//   end;
+//   end; when every sequence fits one 128-row tile, one workgroup per
+//   (sequence, head) computes S and dP once for dQ, dK and dV
+//   (bwd_small_kernel);
 // * variants: a causal mask (tiles above the diagonal skipped, the straddling
 //   tile masked in registers), a per-head bias read from device memory with
 //   its gradient (per-key sums of dS), and softmax attention on the same
@@ -1002,6 +1004,187 @@ bwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const
     dq_body<D, SPLIT, SOFTMAX>(lds, b - P.dq_off, Q, K, V, dO, dQ, LSE, DELTA, P.T, P.dq);
 }
 
+// ---------------------------------------------------------------------------
+// Backward of sequences that fit one 128-row tile (Lmax <= 128; sigmoid, fast
+// precision, no mask, head dim 64).  The two-kernel split of the pages (§2C)
+// recomputes S and dP on each side; for long sequences that costs 2/5 more
+// matrix work but keeps every workgroup's output private.  When a whole
+// (sequence, head) is one tile, one workgroup owns all of its dQ, dK and dV
+// rows, so the split buys nothing: this kernel computes S, dP and dS once.
+// Workgroup = (sequence, head); wave w owns keys 32w .. 32w+31 and, in the
+// second phase, queries 32w .. 32w+31.
+// Phase 1 (as the dK/dV kernel, two 64-query halves): S = Q K^T and
+// dP = dO V^T with the key as the lane's column, dS = dP sigma (1 - sigma),
+// dV^T += dO^T P, dK^T += Q^T dS; each dS chunk is also stored to LDS as dS^T
+// (keys x queries).  Phase 2: dQ^T (d x 32 queries) += K^T dS^T over the 128
+// keys, with both operands read from LDS by transposing reads.
+// The dS^T buffer keeps each key row's 4-query (8-byte) groups in order up
+// to an XOR of the group index by Y(r) = (r % 4) * 8 + (r / 4) % 8: the phase-1
+// stores (32 keys, one group) and the phase-2 transposing reads (4 keys x 8
+// groups) each hit 32 distinct groups, all 64 banks.
+// Rows of dQ, dK and dV from n_b to Lmax - 1 are written as 0 here.
+// ---------------------------------------------------------------------------
+constexpr int kSmallRows = 128;
+
+__device__ __forceinline__ int ds_group(int r, int g) { return g ^ (((r & 3) << 3) | ((r >> 2) & 7)); }
+
+// Rows n .. Lmax-1 of a slice as 0 (16-byte stores, all threads).
+template <int D>
+__device__ __forceinline__ void zero_rows(uint16_t* p, int rs, int n, int lmax) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int c = (int)threadIdx.x; c < (lmax - n) * (D / 8); c += kThreads)
+    *(u32x4*)(p + (size_t)(n + c / (D / 8)) * rs + 8 * (c % (D / 8))) = z;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_small_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+    const SeqTable T, const Sched S, const int64_t dq_sb, const int64_t dq_sh, const int32_t dq_sl) {
+  static_assert(D == 64, "head dim 64");
+  constexpr int R = kSmallRows;
+  __shared__ __align__(16) uint16_t qt[R * D], gt[R * D], kt[R * D], dst[R * R];
+
+  const int s = (int)blockIdx.x / S.H, h = (int)blockIdx.x - s * S.H;
+  Item it;
+  it.s = s;
+  it.n = table_n(T, s);
+  it.bh = (T.b_base + s) * S.H + h;
+  it.tile = 0;
+  const int n = it.n;
+  uint16_t* const dqp = dQ + (size_t)(T.b_base + s) * dq_sb + (size_t)h * dq_sh;
+  uint16_t* const dkp = slice_base(dK, S, it.bh, 4);
+  uint16_t* const dvp = slice_base(dV, S, it.bh, 5);
+  if (n == 0) {
+    zero_rows<D>(dqp, dq_sl, 0, S.Lmax);
+    zero_rows<D>(dkp, S.sl[4], 0, S.Lmax);
+    zero_rows<D>(dvp, S.sl[5], 0, S.Lmax);
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
+      vs(slice_base(V, S, it.bh, 2), n, S.sl[2]), gs(slice_base(dO, S, it.bh, 3), n, S.sl[3]);
+  {
+    const TileDma<R, D> dma_q(w, lane, S.sl[0]), dma_g(w, lane, S.sl[3]), dma_k(w, lane, S.sl[1]);
+    dma_q.load(qs, 0, qt);
+    dma_g.load(gs, 0, gt);
+    dma_k.load(ks, 0, kt);
+  }
+  const int krow = 32 * w + l32;
+  e16x8 kf[D / 16], vf[D / 16];
+  load_bfrag_scaled<D>(kf, ks, krow, hf, score_c1<D>());
+  load_bfrag<D>(vf, vs, krow, hf);
+  const float m = item_bias_factor(S, it, item_c2(S, it));
+  const TrFrag<D> tr(lane);
+  const FragAddr<D> fa(l32, hf);
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dk[i] = (f32x16){};
+    dv[i] = (f32x16){};
+  }
+  vm_drain();
+  __syncthreads();
+
+  // Phase 1: the two 64-query halves.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint16_t* Qj = qt + 64 * j * D;
+    const uint16_t* Gj = gt + 64 * j * D;
+    f32x16 sc[2], gc[2];
+    zero2(sc);
+    zero2(gc);
+    score_pipelined<D>(sc, Qj, kf, fa);
+    score_pipelined<D>(gc, Gj, vf, fa);
+    e16x8 dh[4], dl[4], ph[4], pl[4];
+    e16x8 ag[2][D / 32], aq[2][D / 32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      read_value_frags<D>(ag[c & 1], tr, Gj, c);
+      read_value_frags<D>(aq[c & 1], tr, Qj, c);
+      sched_fence();
+      dsigmoid_chunk<D, false, true, true>(sc, gc, c, m, dh[c], dl[c], ph[c], pl[c]);
+      // dS^T rows: this lane's key; queries 64j + 16c + 4hf + {0..3} and + 8
+      const u32x4 pk = as_u32x4(dh[c]);
+      const int g0 = 16 * j + 4 * c + hf;
+      *(uint2*)(dst + krow * R + 4 * ds_group(krow, g0)) = (uint2){pk[0], pk[1]};
+      *(uint2*)(dst + krow * R + 4 * ds_group(krow, g0 + 2)) = (uint2){pk[2], pk[3]};
+      if (c > 0) {
+        value_chunk_pre<D, false>(dv, ag[(c - 1) & 1], ph[c - 1], pl[c - 1]);
+        value_chunk_pre<D, false>(dk, aq[(c - 1) & 1], dh[c - 1], dl[c - 1]);
+        interleave<2 * (D / 32), 64 / (2 * (D / 32))>();
+      }
+      sched_fence();
+    }
+    value_chunk_pre<D, false>(dv, ag[1], ph[3], pl[3]);
+    value_chunk_pre<D, false>(dk, aq[1], dh[3], dl[3]);
+  }
+  {
+    const float scale = S.out_scale;
+    if (krow < n) {
+      uint16_t* rk = dkp + (size_t)krow * S.sl[4];
+      uint16_t* rv = dvp + (size_t)krow * S.sl[5];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          store4(rk + 32 * db + 8 * i + 4 * hf, dk[db], i, scale);
+          store4(rv + 32 * db + 8 * i + 4 * hf, dv[db], i, 1.0f);
+        }
+    } else if (krow < S.Lmax) {
+      uint16_t* rk = dkp + (size_t)krow * S.sl[4];
+      uint16_t* rv = dvp + (size_t)krow * S.sl[5];
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        *(uint2*)(rk + 8 * i + 4 * hf) = (uint2){0u, 0u};
+        *(uint2*)(rv + 8 * i + 4 * hf) = (uint2){0u, 0u};
+      }
+    }
+  }
+  __syncthreads();
+
+  // Phase 2: dQ^T += K^T dS^T, eight 16-key chunks.  The B fragment of chunk
+  // cc is read as dS^T rows (keys) 16cc + 4hf + j/4 (+ 8), queries
+  // 32w + 16gq + 4(j%4) .. +3 (lane j of each 16, gq = lane / 16 % 2): the
+  // key order of TrFrag's reads of K.  Y(16cc + x) = Y(x) ^ 4 (cc % 2).
+  const int j16 = lane & 15, gq = (lane >> 4) & 1;
+  const int rl = 4 * hf + (j16 >> 2), grp = 8 * w + 4 * gq + (j16 & 3);
+  int boff[2][2];  // [cc % 2][first / second read]
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = rl + 8 * hh;
+      boff[par][hh] = r * R + 4 * (ds_group(r, grp) ^ (4 * par));
+    }
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+#pragma unroll
+  for (int cc = 0; cc < R / 16; ++cc) {
+    e16x8 a[D / 32];
+    read_value_frags<D>(a, tr, kt, cc);
+    const bf16x4 lo = lds_tr4(dst + 16 * cc * R + boff[cc & 1][0]);
+    const bf16x4 hi = lds_tr4(dst + 16 * cc * R + boff[cc & 1][1]);
+    const e16x8 b = __builtin_bit_cast(e16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] = mfma(a[db], b, acc[db]);
+  }
+  const int qrow = 32 * w + l32;
+  if (qrow < n) {
+    uint16_t* rq = dqp + (size_t)qrow * dq_sl;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store4(rq + 32 * db + 8 * i + 4 * hf, acc[db], i, S.out_scale);
+  } else if (qrow < S.Lmax) {
+    uint16_t* rq = dqp + (size_t)qrow * dq_sl;
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) *(uint2*)(rq + 8 * i + 4 * hf) = (uint2){0u, 0u};
+  }
+}
+
 // delta = rowsum(dO * O) per row for the softmax backward (0 on padded
 // rows); one thread per row, fp32 accumulation of the 16-bit products.
 template <int D>
@@ -1075,6 +1258,16 @@ hipError_t launch_bwd_fused_d(const BwdSched& P, int32_t blocks, const void* q, 
   if (lse) return launch_bwd_fused_t<D, SPLIT, true, false>(P, blocks, q, k, v, g, dq, dk, dv, lse, delta, dbias, st);
   if (dbias) return launch_bwd_fused_t<D, SPLIT, false, true>(P, blocks, q, k, v, g, dq, dk, dv, lse, delta, dbias, st);
   return launch_bwd_fused_t<D, SPLIT, false, false>(P, blocks, q, k, v, g, dq, dk, dv, lse, delta, dbias, st);
+}
+
+hipError_t launch_bwd_small_t(const Launch& L, const void* q, const void* k, const void* v, const void* g, void* dq,
+                              void* dk, void* dv, int64_t dq_sb, int64_t dq_sh, int32_t dq_sl, hipStream_t st) {
+  const int64_t blocks = (int64_t)L.T.nseq * L.sched.H;
+  if (L.sched.Lmax > kSmallRows || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((bwd_small_kernel<64>), dim3((unsigned)blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq, (uint16_t*)dk,
+                     (uint16_t*)dv, L.T, L.sched, dq_sb, dq_sh, dq_sl);
+  return hipGetLastError();
 }
 
 // db[h] = sum over sequences b and rows j of dbias[b, h, j]: one workgroup of
@@ -1181,6 +1374,11 @@ hipError_t launch_bwd_fused(int d, bool split, const BwdSched& P, int32_t blocks
   if (d != 64) return hipErrorInvalidValue;  // d = 128 runs the two launches (see DqCfg)
   return split ? kern::launch_bwd_fused_d<64, true>(P, blocks, q, k, v, g, dq, dk, dv, lse2, delta, dbias, st)
                : kern::launch_bwd_fused_d<64, false>(P, blocks, q, k, v, g, dq, dk, dv, lse2, delta, dbias, st);
+}
+
+hipError_t launch_bwd_small(const Launch& L, const void* q, const void* k, const void* v, const void* g, void* dq,
+                            void* dk, void* dv, int64_t dq_sb, int64_t dq_sh, int32_t dq_sl, hipStream_t st) {
+  return kern::launch_bwd_small_t(L, q, k, v, g, dq, dk, dv, dq_sb, dq_sh, dq_sl, st);
 }
 
 hipError_t launch_bias_grad(int32_t B, int32_t H, int32_t Lmax, const float* dbias, float* db, hipStream_t st) {
