@@ -409,7 +409,28 @@ EXTRA = (("dense_b4h16d128_l8192", "fast"), ("cells8k_b8h12d64_l8192_x4", "split
 SHORT = ("few_b4h16d64_l4096", "many_b1024h16d64_l256", "many_b4096h16d64_l128")
 
 
-def workload_record(r, precision):
+def measure_copy_gbs(reps=10) -> float:
+    """HBM rate of a plain device copy of 1 GiB (bytes read + written per
+    second), timed with HIP events: the rate a streaming kernel reaches on
+    this chip, beside the published 8 TB/s."""
+    import torch
+
+    x = torch.empty(1 << 29, dtype=torch.int16, device="cuda:0").fill_(1)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = reps * 2 * x.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def workload_record(r, precision, copy_gbs=None):
     """Throughput of one timed workload (forward + fused backward) with the
     roofline fraction of its dominant kernel."""
     n = r["seqlens"]
@@ -423,6 +444,8 @@ def workload_record(r, precision):
                  "executed_mfma_frac": round(tflops(executed_units(dom, w, precision) * r["pair_flops"],
                                                     r["kernel_avg_ms"][dom]) / PEAK_BF16_TFLOPS, 4),
                  "traffic": load_traffic(dom, w.name, precision)})
+    if copy_gbs and roof["bound"] == "hbm":
+        roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbs, 4)
     return {
         "B": w.B, "H": w.H, "d": w.d, "Lmax": w.Lmax, "seqlens": [int(x) for x in n], "precision": precision,
         "value": round(tflops(r["fwd_flops"] + r["bwd_flops"], r["step_ms"]), 2),
@@ -598,6 +621,13 @@ def main():
                                           "kernel": "back-to-back bf16 32x32x16 MFMAs, 4 chains per wave, "
                                                     "4 waves per SIMD (sigattn_probe_mfma)"}
         roofline["frac_of_measured_peak"] = round(achieved / pr["tflops"], 4)
+        copy_gbs = measure_copy_gbs()
+        roofline["measured_hbm_copy"] = {"gbps": round(copy_gbs, 1),
+                                         "kernel": "device copy of 1 GiB, bytes read + written"}
+        if roofline["bound"] == "hbm":
+            roofline["frac_of_measured_copy"] = round(roofline["achieved"] / copy_gbs, 4)
+    else:
+        copy_gbs = None
     if roofline["traffic"] is not None:  # achieved HBM rate of the dominant kernel
         roofline["hbm_gbps"] = round(roofline["traffic"] / (r["kernel_avg_ms"][dominant] * 1e-3) / 1e9, 1)
     if "bwd_bias_grad" in r["kernel_avg_ms"]:
@@ -647,13 +677,13 @@ def main():
                 if wn == name:
                     continue
                 rx = time_workload(wn, prec, sub_steps, 2, dtype=a.dtype, settle_ms=sub_settle)
-                out["workloads"][wn] = workload_record(rx, prec)
+                out["workloads"][wn] = workload_record(rx, prec, copy_gbs)
                 del rx
                 torch.cuda.empty_cache()
             short = {}
             for wn in SHORT:
                 rx = time_workload(wn, "fast", sub_steps, 2, dtype=a.dtype, settle_ms=sub_settle)
-                rec = workload_record(rx, "fast")
+                rec = workload_record(rx, "fast", copy_gbs)
                 ws = rx["workload"]
                 rec.pop("seqlens")
                 rec["launches_per_pass"] = {p_: int(sa.plan_stats(ws.B, ws.H, ws.Lmax, ws.d, rx["seqlens"], p_)[2])

@@ -1019,14 +1019,17 @@ bwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const
 // (keys x queries).  Phase 2: dQ^T (d x 32 queries) += K^T dS^T over the 128
 // keys, with both operands read from LDS by transposing reads.
 // The dS^T buffer keeps each key row's 4-query (8-byte) groups in order up
-// to an XOR of the group index by Y(r) = (r % 4) * 8 + (r / 4) % 8: the phase-1
-// stores (32 keys, one group) and the phase-2 transposing reads (4 keys x 8
-// groups) each hit 32 distinct groups, all 64 banks.
+// to an XOR of the group index by Y(r) = (r % 4) * 8 + (r / 2) % 8.  An 8-byte
+// LDS store serves 16 lanes per cycle over 32 four-byte banks (128 bytes), a
+// transposing read 32 lanes over 64 banks (measured: SQ_LDS_BANK_CONFLICT).
+// The phase-1 stores (16 consecutive keys, one group) then hit 16 distinct
+// groups modulo 16, and the phase-2 reads (4 keys x 8 aligned groups) 32
+// distinct groups: no bank conflicts either way.
 // Rows of dQ, dK and dV from n_b to Lmax - 1 are written as 0 here.
 // ---------------------------------------------------------------------------
 constexpr int kSmallRows = 128;
 
-__device__ __forceinline__ int ds_group(int r, int g) { return g ^ (((r & 3) << 3) | ((r >> 2) & 7)); }
+__device__ __forceinline__ int ds_group(int r, int g) { return g ^ (((r & 3) << 3) | ((r >> 1) & 7)); }
 
 // Rows n .. Lmax-1 of a slice as 0 (16-byte stores, all threads).
 template <int D>
@@ -1147,17 +1150,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_small_kernel(
   // Phase 2: dQ^T += K^T dS^T, eight 16-key chunks.  The B fragment of chunk
   // cc is read as dS^T rows (keys) 16cc + 4hf + j/4 (+ 8), queries
   // 32w + 16gq + 4(j%4) .. +3 (lane j of each 16, gq = lane / 16 % 2): the
-  // key order of TrFrag's reads of K.  Y(16cc + x) = Y(x) ^ 4 (cc % 2).
+  // key order of TrFrag's reads of K.  Y(16cc + x) = Y(x).
   const int j16 = lane & 15, gq = (lane >> 4) & 1;
   const int rl = 4 * hf + (j16 >> 2), grp = 8 * w + 4 * gq + (j16 & 3);
-  int boff[2][2];  // [cc % 2][first / second read]
+  int boff[2];  // first / second read
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int r = rl + 8 * hh;
-      boff[par][hh] = r * R + 4 * (ds_group(r, grp) ^ (4 * par));
-    }
+  for (int hh = 0; hh < 2; ++hh) boff[hh] = (rl + 8 * hh) * R + 4 * ds_group(rl + 8 * hh, grp);
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
@@ -1165,8 +1163,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_small_kernel(
   for (int cc = 0; cc < R / 16; ++cc) {
     e16x8 a[D / 32];
     read_value_frags<D>(a, tr, kt, cc);
-    const bf16x4 lo = lds_tr4(dst + 16 * cc * R + boff[cc & 1][0]);
-    const bf16x4 hi = lds_tr4(dst + 16 * cc * R + boff[cc & 1][1]);
+    const bf16x4 lo = lds_tr4(dst + 16 * cc * R + boff[0]);
+    const bf16x4 hi = lds_tr4(dst + 16 * cc * R + boff[1]);
     const e16x8 b = __builtin_bit_cast(e16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = mfma(a[db], b, acc[db]);
