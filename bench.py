@@ -59,8 +59,8 @@ KERNEL_FLOP_UNITS = {"fwd": 4, "bwd": 10, "bwd_dq": 2, "bwd_dkdv": 8}
 # the backward recomputes S and dP on the dQ side, and split precision doubles
 # the products that take P or dX.
 EXECUTED_UNITS = {"fwd": (4, 6), "bwd": (14, 20), "bwd_dq": (6, 8), "bwd_dkdv": (8, 12)}
-# ... except where sigattn_bwd runs the one-tile backward (every sequence
-# within one 128-row tile, head dim 64, fast precision, no mask): S and dP
+# ... except where sigattn_bwd runs the short-sequence backward (every
+# sequence within 256 rows, head dim 64, fast precision, no mask): S and dP
 # once, so it issues exactly the algorithmic 10.
 ONE_TILE_EXECUTED = 10
 # Algorithmic HBM bytes per launch: each input's valid rows read once, each
@@ -79,8 +79,9 @@ def pair_flops(seqlens, H, d, causal=False):
 
 
 def one_tile_bwd(w, precision, causal=False) -> bool:
-    """Whether sigattn_bwd runs the one-tile backward for this workload."""
-    return w.d == 64 and precision == "fast" and not causal and w.Lmax <= 128
+    """Whether sigattn_bwd runs the short-sequence backward (one workgroup per
+    (sequence, head)) for this workload."""
+    return w.d == 64 and precision == "fast" and not causal and w.Lmax <= 256
 
 
 def executed_units(kname, w, precision, causal=False):

@@ -192,21 +192,21 @@ sigattn_status sigattn_bwd_dkdv(const sigattn_args *args, const void *q, const v
 /* The whole backward in one call: dQ (as sigattn_bwd_dq), dK and dV (as
  * sigattn_bwd_dkdv) and, if dbias is not NULL, the bias-gradient rows (as
  * sigattn_bwd_dkdv_dbias).  Results are bitwise those of the separate calls,
- * except in the one-tile case below.
+ * except in the short-sequence case below.
  * At d = 64 both sides normally run in ONE fused launch: the dK/dV
  * workgroups first, then the dQ workgroups, which fill the CUs the dK/dV work
  * leaves idle towards its end (§2C's two backward kernels, scheduled
  * together; still no atomics: every output row has one writer).  At d = 128
  * the two kernels run at different occupancies, and the dK/dV and dQ
  * launches run in turn on args->stream.
- * One-tile case: d = 64, fast precision, no mask, dbias NULL and Lmax <= 128
- * (every sequence within one 128-row tile).  Then one workgroup per
- * (sequence, head) writes all of its dQ, dK and dV rows (one launch per 4096
- * sequences), computing S, dP and dS once instead of once per side: dK and
- * dV are bitwise those of sigattn_bwd_dkdv, and dQ is taken from the same dS
- * (the scores from K scaled by -log2(e)/sqrt(d) and rounded to the element
- * type, where sigattn_bwd_dq scales Q), so it differs from sigattn_bwd_dq by
- * rounding only.
+ * Short-sequence case: d = 64, fast precision, no mask, dbias NULL and
+ * Lmax <= 256.  Then one workgroup per (sequence, head) writes all of its
+ * dQ, dK and dV rows (one launch per 4096 sequences), computing S, dP and dS
+ * once instead of once per side: dK and dV are bitwise those of
+ * sigattn_bwd_dkdv, and dQ is taken from the same dS (the scores from K
+ * scaled by -log2(e)/sqrt(d) and rounded to the element type, where
+ * sigattn_bwd_dq scales Q), so it differs from sigattn_bwd_dq by rounding
+ * only.
  * args->strides, if set, has 7 entries: q, k, v, dout, dq, dk, dv.  Same
  * checks and errors as the separate calls (dq, dk, dv are outputs; dbias is
  * checked like a row output). */
@@ -299,9 +299,9 @@ const char *sigattn_status_str(sigattn_status status);
  * tiles are not counted because they are never computed — and the number of
  * kernel launches.  For SIGATTN_PASS_BWD: the dK/dV and dQ sides summed,
  * and 1 launch when sigattn_bwd fuses them (d = 64, both sides fitting one
- * launch each), or the dK/dV side's launch count in sigattn_bwd's one-tile
- * case (one launch per length table; the items and pairs are still those of
- * the two sides).
+ * launch each), or the dK/dV side's launch count in sigattn_bwd's
+ * short-sequence case (one launch per length table; the items and pairs are
+ * still those of the two sides).
  * Any of the output pointers may be NULL.  Validates args (shape, seqlens,
  * bias, precision) as the compute calls do. */
 sigattn_status sigattn_plan_stats(const sigattn_args *args, int32_t pass, int64_t *work_items,

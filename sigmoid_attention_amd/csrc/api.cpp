@@ -267,13 +267,13 @@ bool fused_bwd(int32_t d, size_t dkdv_launches, size_t dq_launches) {
   return d == 64 && dkdv_launches == 1 && dq_launches == 1;
 }
 
-// Whether the sigmoid backward runs as the one-tile kernel (launch_bwd_small):
-// head dim 64, fast precision, no mask, no bias gradient, every sequence
-// within one 128-row tile.
+// Whether the sigmoid backward runs as the short-sequence kernel
+// (launch_bwd_small, one workgroup per (sequence, head)): head dim 64, fast
+// precision, no mask, no bias gradient, every sequence within 256 rows.
+constexpr int32_t kSmallBwdRows = 256;
 bool small_bwd(const sigattn_args* a, bool softmax, bool dbias) {
-  static_assert(kDkdvOuter == 128, "the one-tile kernel's rows are the dK/dV schedule's tiles");
   return a->d == 64 && a->precision == SIGATTN_PREC_FAST && a->mask != SIGATTN_MASK_CAUSAL && !softmax && !dbias &&
-         a->Lmax <= kDkdvOuter;
+         a->Lmax <= kSmallBwdRows;
 }
 
 // The backward of both sides: one fused launch (fused_bwd), the dK/dV

@@ -35,9 +35,8 @@
 //   launch (dispatched last, they fill the tail), so each call is one launch;
 // * at d = 64 the two backward kernels run as one launch (bwd_kernel): the
 //   dQ workgroups fill the CUs that the dK/dV workgroups leave idle at the
-//   end; when every sequence fits one 128-row tile, one workgroup per
-//   (sequence, head) computes S and dP once for dQ, dK and dV
-//   (bwd_small_kernel);
+//   end; when every sequence fits 256 rows, one workgroup per (sequence,
+//   head) computes S and dP once for dQ, dK and dV (bwd_small_kernel);
 // * variants: a causal mask (tiles above the diagonal skipped, the straddling
 //   tile masked in registers), a per-head bias read from device memory with
 //   its gradient (per-key sums of dS), and softmax attention on the same
@@ -1005,19 +1004,24 @@ bwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const
 }
 
 // ---------------------------------------------------------------------------
-// Backward of sequences that fit one 128-row tile (Lmax <= 128; sigmoid, fast
-// precision, no mask, head dim 64).  The two-kernel split of the pages (§2C)
-// recomputes S and dP on each side; for long sequences that costs 2/5 more
-// matrix work but keeps every workgroup's output private.  When a whole
-// (sequence, head) is one tile, one workgroup owns all of its dQ, dK and dV
-// rows, so the split buys nothing: this kernel computes S, dP and dS once.
-// Workgroup = (sequence, head); wave w owns keys 32w .. 32w+31 and, in the
-// second phase, queries 32w .. 32w+31.
-// Phase 1 (as the dK/dV kernel, two 64-query halves): S = Q K^T and
-// dP = dO V^T with the key as the lane's column, dS = dP sigma (1 - sigma),
-// dV^T += dO^T P, dK^T += Q^T dS; each dS chunk is also stored to LDS as dS^T
-// (keys x queries).  Phase 2: dQ^T (d x 32 queries) += K^T dS^T over the 128
-// keys, with both operands read from LDS by transposing reads.
+// Backward of short sequences, one workgroup per (sequence, head): Lmax <= R
+// with R = 128 (4 waves) or 256 (8 waves); sigmoid, fast precision, no mask,
+// head dim 64.  The two-kernel split of the pages (§2C) recomputes S and dP
+// on each side; for long sequences that costs 2/5 more matrix work but keeps
+// every workgroup's output private.  When one workgroup holds a whole
+// (sequence, head), it owns all of its dQ, dK and dV rows, so the split buys
+// nothing: this kernel computes S, dP and dS once.
+// Wave w owns keys 32w .. 32w+31.  Phase 1 (as the dK/dV kernel, 64-query
+// halves j): S = Q K^T and dP = dO V^T with the key as the lane's column,
+// dS = dP sigma (1 - sigma), dV^T += dO^T P, dK^T += Q^T dS; each dS chunk is
+// also stored to LDS as dS^T (keys x the 128 queries of the half's pair).
+// Phase 2, after each pair of halves: dQ^T += K^T dS^T over all R keys for
+// the pair's 128 queries, as eight 32-query x 32-column blocks spread over
+// the waves (wave w: query block w % 4, column blocks w / 4 .. in steps of
+// R / 128), both operands read from LDS by transposing reads.  At R = 256,
+// halves past the sequence's last row skip their work (the workgroup's n is
+// uniform), and so, with phase 2 over those keys, do the waves of the second
+// 128-key tile when the sequence ends in the first.
 // The dS^T buffer keeps each key row's 4-query (8-byte) groups in order up
 // to an XOR of the group index by Y(r) = (r % 4) * 8 + (r / 2) % 8.  An 8-byte
 // LDS store serves 16 lanes per cycle over 32 four-byte banks (128 bytes), a
@@ -1025,28 +1029,36 @@ bwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const
 // The phase-1 stores (16 consecutive keys, one group) then hit 16 distinct
 // groups modulo 16, and the phase-2 reads (4 keys x 8 aligned groups) 32
 // distinct groups: no bank conflicts either way.
+// LDS: Q, dO, K (R rows each) and the dS^T of one pair (R x 128): 80 KB at
+// R = 128 (two workgroups per CU), 160 KB at R = 256 (one of eight waves).
 // Rows of dQ, dK and dV from n_b to Lmax - 1 are written as 0 here.
 // ---------------------------------------------------------------------------
-constexpr int kSmallRows = 128;
-
 __device__ __forceinline__ int ds_group(int r, int g) { return g ^ (((r & 3) << 3) | ((r >> 1) & 7)); }
 
-// Rows n .. Lmax-1 of a slice as 0 (16-byte stores, all threads).
-template <int D>
+// Rows n .. Lmax-1 of a slice as 0 (16-byte stores, all NT threads).
+template <int D, int NT>
 __device__ __forceinline__ void zero_rows(uint16_t* p, int rs, int n, int lmax) {
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (int c = (int)threadIdx.x; c < (lmax - n) * (D / 8); c += kThreads)
+  for (int c = (int)threadIdx.x; c < (lmax - n) * (D / 8); c += NT)
     *(u32x4*)(p + (size_t)(n + c / (D / 8)) * rs + 8 * (c % (D / 8))) = z;
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_small_kernel(
+template <int R> struct SmallCfg {
+  static constexpr int NW = R / 32;    // waves
+  static constexpr int NT = 64 * NW;   // threads
+  static constexpr int OCC = R == 128 ? 2 : 1;  // workgroups per CU the LDS allows
+};
+
+template <int D, int R>
+__global__ __launch_bounds__(SmallCfg<R>::NT, SmallCfg<R>::OCC) void bwd_small_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     const SeqTable T, const Sched S, const int64_t dq_sb, const int64_t dq_sh, const int32_t dq_sl) {
   static_assert(D == 64, "head dim 64");
-  constexpr int R = kSmallRows;
-  __shared__ __align__(16) uint16_t qt[R * D], gt[R * D], kt[R * D], dst[R * R];
+  static_assert(R == 128 || R == 256, "one or two 128-row tiles");
+  constexpr int NW = SmallCfg<R>::NW, NT = SmallCfg<R>::NT, PQ = 128;  // queries per pair
+  constexpr int DBW = 8 / NW;  // phase-2 column blocks per wave
+  __shared__ __align__(16) uint16_t qt[R * D], gt[R * D], kt[R * D], dst[R * PQ];
 
   const int s = (int)blockIdx.x / S.H, h = (int)blockIdx.x - s * S.H;
   Item it;
@@ -1059,9 +1071,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_small_kernel(
   uint16_t* const dkp = slice_base(dK, S, it.bh, 4);
   uint16_t* const dvp = slice_base(dV, S, it.bh, 5);
   if (n == 0) {
-    zero_rows<D>(dqp, dq_sl, 0, S.Lmax);
-    zero_rows<D>(dkp, S.sl[4], 0, S.Lmax);
-    zero_rows<D>(dvp, S.sl[5], 0, S.Lmax);
+    zero_rows<D, NT>(dqp, dq_sl, 0, S.Lmax);
+    zero_rows<D, NT>(dkp, S.sl[4], 0, S.Lmax);
+    zero_rows<D, NT>(dvp, S.sl[5], 0, S.Lmax);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -1069,12 +1081,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_small_kernel(
   const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]), gs(slice_base(dO, S, it.bh, 3), n, S.sl[3]);
   {
-    const TileDma<R, D> dma_q(w, lane, S.sl[0]), dma_g(w, lane, S.sl[3]), dma_k(w, lane, S.sl[1]);
+    const TileDma<R, D, NW> dma_q(w, lane, S.sl[0]), dma_g(w, lane, S.sl[3]), dma_k(w, lane, S.sl[1]);
     dma_q.load(qs, 0, qt);
     dma_g.load(gs, 0, gt);
     dma_k.load(ks, 0, kt);
   }
   const int krow = 32 * w + l32;
+  // Waves of the second 128-key tile skip their work when the sequence ends
+  // in the first (their dS^T rows are then not read).
+  const bool keys = R == 128 || w < 4 || n > 128;
   e16x8 kf[D / 16], vf[D / 16];
   load_bfrag_scaled<D>(kf, ks, krow, hf, score_c1<D>());
   load_bfrag<D>(vf, vs, krow, hf);
@@ -1087,99 +1102,123 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_small_kernel(
     dk[i] = (f32x16){};
     dv[i] = (f32x16){};
   }
+  // phase 2: this wave's query block and the B-fragment offsets of its dS^T
+  // reads: rows (keys) 16cc + 4hf + j/4 (+ 8), queries 32qb + 16gq + 4(j%4)
+  // .. +3 (lane j of each 16, gq = lane / 16 % 2): the key order of TrFrag's
+  // reads of K.  Y(16cc + x) = Y(x).
+  const int qb = w & 3, db0 = DBW == 2 ? 0 : w >> 2;
+  const int j16 = lane & 15, gq = (lane >> 4) & 1;
+  const int rl = 4 * hf + (j16 >> 2), grp = 8 * qb + 4 * gq + (j16 & 3);
+  int boff[2];  // first / second read
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) boff[hh] = (rl + 8 * hh) * PQ + 4 * ds_group(rl + 8 * hh, grp);
+  // TrFrag offsets of this wave's K^T column blocks (selected, not indexed:
+  // db0 is a run-time value)
+  int koff[DBW][2];
+#pragma unroll
+  for (int i = 0; i < DBW; ++i)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      koff[i][hh] = DBW == 2 ? tr.off[i][hh] : (db0 ? tr.off[1][hh] : tr.off[0][hh]);
   vm_drain();
   __syncthreads();
 
-  // Phase 1: the two 64-query halves.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint16_t* Qj = qt + 64 * j * D;
-    const uint16_t* Gj = gt + 64 * j * D;
-    f32x16 sc[2], gc[2];
-    zero2(sc);
-    zero2(gc);
-    score_pipelined<D>(sc, Qj, kf, fa);
-    score_pipelined<D>(gc, Gj, vf, fa);
-    e16x8 dh[4], dl[4], ph[4], pl[4];
-    e16x8 ag[2][D / 32], aq[2][D / 32];
+  for (int j = 0; j < R / 64; ++j) {
+    if (keys && (R == 128 || 64 * j < n)) {
+      const uint16_t* Qj = qt + 64 * j * D;
+      const uint16_t* Gj = gt + 64 * j * D;
+      f32x16 sc[2], gc[2];
+      zero2(sc);
+      zero2(gc);
+      score_pipelined<D>(sc, Qj, kf, fa);
+      score_pipelined<D>(gc, Gj, vf, fa);
+      e16x8 dh[4], dl[4], ph[4], pl[4];
+      e16x8 ag[2][D / 32], aq[2][D / 32];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      read_value_frags<D>(ag[c & 1], tr, Gj, c);
-      read_value_frags<D>(aq[c & 1], tr, Qj, c);
-      sched_fence();
-      dsigmoid_chunk<D, false, true, true>(sc, gc, c, m, dh[c], dl[c], ph[c], pl[c]);
-      // dS^T rows: this lane's key; queries 64j + 16c + 4hf + {0..3} and + 8
-      const u32x4 pk = as_u32x4(dh[c]);
-      const int g0 = 16 * j + 4 * c + hf;
-      *(uint2*)(dst + krow * R + 4 * ds_group(krow, g0)) = (uint2){pk[0], pk[1]};
-      *(uint2*)(dst + krow * R + 4 * ds_group(krow, g0 + 2)) = (uint2){pk[2], pk[3]};
-      if (c > 0) {
-        value_chunk_pre<D, false>(dv, ag[(c - 1) & 1], ph[c - 1], pl[c - 1]);
-        value_chunk_pre<D, false>(dk, aq[(c - 1) & 1], dh[c - 1], dl[c - 1]);
-        interleave<2 * (D / 32), 64 / (2 * (D / 32))>();
-      }
-      sched_fence();
-    }
-    value_chunk_pre<D, false>(dv, ag[1], ph[3], pl[3]);
-    value_chunk_pre<D, false>(dk, aq[1], dh[3], dl[3]);
-  }
-  {
-    const float scale = S.out_scale;
-    if (krow < n) {
-      uint16_t* rk = dkp + (size_t)krow * S.sl[4];
-      uint16_t* rv = dvp + (size_t)krow * S.sl[5];
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          store4(rk + 32 * db + 8 * i + 4 * hf, dk[db], i, scale);
-          store4(rv + 32 * db + 8 * i + 4 * hf, dv[db], i, 1.0f);
+      for (int c = 0; c < 4; ++c) {
+        read_value_frags<D>(ag[c & 1], tr, Gj, c);
+        read_value_frags<D>(aq[c & 1], tr, Qj, c);
+        sched_fence();
+        dsigmoid_chunk<D, false, true, true>(sc, gc, c, m, dh[c], dl[c], ph[c], pl[c]);
+        // dS^T row: this lane's key; queries 64(j % 2) + 16c + 4hf + {0..3}
+        // and + 8 of the pair (groups 16(j % 2) + 4c + hf, + 2)
+        const u32x4 pk = as_u32x4(dh[c]);
+        const int g0 = 16 * (j & 1) + 4 * c + hf;
+        *(uint2*)(dst + krow * PQ + 4 * ds_group(krow, g0)) = (uint2){pk[0], pk[1]};
+        *(uint2*)(dst + krow * PQ + 4 * ds_group(krow, g0 + 2)) = (uint2){pk[2], pk[3]};
+        if (c > 0) {
+          value_chunk_pre<D, false>(dv, ag[(c - 1) & 1], ph[c - 1], pl[c - 1]);
+          value_chunk_pre<D, false>(dk, aq[(c - 1) & 1], dh[c - 1], dl[c - 1]);
+          interleave<2 * (D / 32), 64 / (2 * (D / 32))>();
         }
-    } else if (krow < S.Lmax) {
-      uint16_t* rk = dkp + (size_t)krow * S.sl[4];
-      uint16_t* rv = dvp + (size_t)krow * S.sl[5];
+        sched_fence();
+      }
+      value_chunk_pre<D, false>(dv, ag[1], ph[3], pl[3]);
+      value_chunk_pre<D, false>(dk, aq[1], dh[3], dl[3]);
+    }
+    if (j == R / 64 - 1) {  // dK, dV complete
+      const float scale = S.out_scale;
+      if (krow < n) {
+        uint16_t* rk = dkp + (size_t)krow * S.sl[4];
+        uint16_t* rv = dvp + (size_t)krow * S.sl[5];
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        *(uint2*)(rk + 8 * i + 4 * hf) = (uint2){0u, 0u};
-        *(uint2*)(rv + 8 * i + 4 * hf) = (uint2){0u, 0u};
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            store4(rk + 32 * db + 8 * i + 4 * hf, dk[db], i, scale);
+            store4(rv + 32 * db + 8 * i + 4 * hf, dv[db], i, 1.0f);
+          }
+      } else if (krow < S.Lmax) {
+        uint16_t* rk = dkp + (size_t)krow * S.sl[4];
+        uint16_t* rv = dvp + (size_t)krow * S.sl[5];
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+          *(uint2*)(rk + 8 * i + 4 * hf) = (uint2){0u, 0u};
+          *(uint2*)(rv + 8 * i + 4 * hf) = (uint2){0u, 0u};
+        }
       }
     }
-  }
-  __syncthreads();
-
-  // Phase 2: dQ^T += K^T dS^T, eight 16-key chunks.  The B fragment of chunk
-  // cc is read as dS^T rows (keys) 16cc + 4hf + j/4 (+ 8), queries
-  // 32w + 16gq + 4(j%4) .. +3 (lane j of each 16, gq = lane / 16 % 2): the
-  // key order of TrFrag's reads of K.  Y(16cc + x) = Y(x).
-  const int j16 = lane & 15, gq = (lane >> 4) & 1;
-  const int rl = 4 * hf + (j16 >> 2), grp = 8 * w + 4 * gq + (j16 & 3);
-  int boff[2];  // first / second read
+    if (j % 2 == 0) continue;
+    // Phase 2 for the pair p = j / 2: queries PQ p + 32 qb + l32.
+    const int p = j / 2;
+    __syncthreads();  // the pair's dS^T is complete
+    const int qrow = PQ * p + 32 * qb + l32;
+    if (PQ * p < n) {
+      f32x16 acc[DBW];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) boff[hh] = (rl + 8 * hh) * R + 4 * ds_group(rl + 8 * hh, grp);
-  f32x16 acc[D / 32];
+      for (int i = 0; i < DBW; ++i) acc[i] = (f32x16){};
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+      for (int cc = 0; cc < R / 16; ++cc) {
+        if (cc < 8 || n > 128) {
+          const bf16x4 lo = lds_tr4(dst + 16 * cc * PQ + boff[0]);
+          const bf16x4 hi = lds_tr4(dst + 16 * cc * PQ + boff[1]);
+          const e16x8 b = __builtin_bit_cast(e16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-  for (int cc = 0; cc < R / 16; ++cc) {
-    e16x8 a[D / 32];
-    read_value_frags<D>(a, tr, kt, cc);
-    const bf16x4 lo = lds_tr4(dst + 16 * cc * R + boff[0]);
-    const bf16x4 hi = lds_tr4(dst + 16 * cc * R + boff[1]);
-    const e16x8 b = __builtin_bit_cast(e16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          for (int i = 0; i < DBW; ++i) {
+            const bf16x4 alo = lds_tr4(kt + 16 * cc * D + koff[i][0]);
+            const bf16x4 ahi = lds_tr4(kt + 16 * cc * D + koff[i][1]);
+            const e16x8 a = __builtin_bit_cast(e16x8, __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[i] = mfma(a, b, acc[i]);
+          }
+        }
+      }
+      if (qrow < n) {
+        uint16_t* rq = dqp + (size_t)qrow * dq_sl;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] = mfma(a[db], b, acc[db]);
-  }
-  const int qrow = 32 * w + l32;
-  if (qrow < n) {
-    uint16_t* rq = dqp + (size_t)qrow * dq_sl;
+        for (int i = 0; i < DBW; ++i)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+          for (int r4 = 0; r4 < 4; ++r4) store4(rq + 32 * (db0 + i) + 8 * r4 + 4 * hf, acc[i], r4, S.out_scale);
+      }
+    }
+    if (qrow >= n && qrow < S.Lmax) {
+      uint16_t* rq = dqp + (size_t)qrow * dq_sl;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) store4(rq + 32 * db + 8 * i + 4 * hf, acc[db], i, S.out_scale);
-  } else if (qrow < S.Lmax) {
-    uint16_t* rq = dqp + (size_t)qrow * dq_sl;
+      for (int i = 0; i < DBW; ++i)
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) *(uint2*)(rq + 8 * i + 4 * hf) = (uint2){0u, 0u};
+        for (int r4 = 0; r4 < 4; ++r4) *(uint2*)(rq + 32 * (db0 + i) + 8 * r4 + 4 * hf) = (uint2){0u, 0u};
+    }
+    if (j + 1 < R / 64) __syncthreads();  // phase-2 reads done before the next pair's stores
   }
 }
 
@@ -1261,10 +1300,15 @@ hipError_t launch_bwd_fused_d(const BwdSched& P, int32_t blocks, const void* q, 
 hipError_t launch_bwd_small_t(const Launch& L, const void* q, const void* k, const void* v, const void* g, void* dq,
                               void* dk, void* dv, int64_t dq_sb, int64_t dq_sh, int32_t dq_sl, hipStream_t st) {
   const int64_t blocks = (int64_t)L.T.nseq * L.sched.H;
-  if (L.sched.Lmax > kSmallRows || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_small_kernel<64>), dim3((unsigned)blocks), dim3(kThreads), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq, (uint16_t*)dk,
-                     (uint16_t*)dv, L.T, L.sched, dq_sb, dq_sh, dq_sl);
+  if (L.sched.Lmax > 256 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (L.sched.Lmax <= 128)
+    hipLaunchKernelGGL((bwd_small_kernel<64, 128>), dim3((unsigned)blocks), dim3(SmallCfg<128>::NT), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq,
+                       (uint16_t*)dk, (uint16_t*)dv, L.T, L.sched, dq_sb, dq_sh, dq_sl);
+  else
+    hipLaunchKernelGGL((bwd_small_kernel<64, 256>), dim3((unsigned)blocks), dim3(SmallCfg<256>::NT), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq,
+                       (uint16_t*)dk, (uint16_t*)dv, L.T, L.sched, dq_sb, dq_sh, dq_sl);
   return hipGetLastError();
 }
 

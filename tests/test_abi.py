@@ -353,13 +353,15 @@ def test_fused_backward_pass_in_validate_and_plan_stats():
     # beyond one launch's length table (4096 sequences): each side runs two
     # launches and the backward runs them in turn instead of one fused launch
     many = [64] * 5000
-    for lmax, prec in ((160, "fast"), (96, "split")):
+    for lmax, prec in ((300, "fast"), (96, "split")):
         kv_l = sa.plan_stats(5000, 1, lmax, 64, many, "bwd_dkdv", precision=prec)[2]
         q_l = sa.plan_stats(5000, 1, lmax, 64, many, "bwd_dq", precision=prec)[2]
         assert kv_l == 2 and sa.plan_stats(5000, 1, lmax, 64, many, "bwd", precision=prec)[2] == kv_l + q_l
-    # every sequence within one 128-row tile (fast precision, d = 64): the
-    # one-tile backward, one launch per length table
+    # every sequence within 256 rows (fast precision, d = 64): the
+    # short-sequence backward, one launch per length table
     assert sa.plan_stats(5000, 1, 96, 64, many, "bwd")[2] == 2
+    assert sa.plan_stats(5000, 1, 256, 64, many, "bwd")[2] == 2
+    assert sa.plan_stats(5000, 1, 257, 64, many, "bwd")[2] == 4
     assert sa.plan_stats(2, 2, 128, 64, lens, "bwd", precision="split")[2] == 1  # fused
 
 

@@ -2,8 +2,8 @@
 work in one launch) gives bitwise the results of the separate dQ and dK/dV
 calls (the same arithmetic in the same order), across the variants, and
 matches the CPU fp64 oracle; batches beyond one launch's capacity take the
-multi-launch route with the same results.  (Batches within one 128-row tile
-take the one-tile backward instead: test_gpu_one_tile_bwd.py.)"""
+multi-launch route with the same results.  (Batches of sequences within 256
+rows take the short-sequence backward instead: test_gpu_one_tile_bwd.py.)"""
 import math
 
 import numpy as np
@@ -64,7 +64,7 @@ def test_fused_with_bias_rows_and_per_head_bias():
 
 def test_fused_strided_fused_qkv_layout():
     """[B, L, 3, H, d] projection slices in, [B, L, 3, H, d] gradient buffer out."""
-    B, H, d, L, lens = 2, 4, 64, 192, [192, 100]
+    B, H, d, L, lens = 2, 4, 64, 320, [320, 100]
     c = workloads.random_case(B, H, d, L, lens, seed=63)
     qkv = torch.stack([c[x].permute(0, 2, 1, 3) for x in ("q", "k", "v")], dim=2).contiguous().to(DEV)
     q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
@@ -95,18 +95,18 @@ def test_fused_softmax_equals_separate_and_oracle():
         assert worst_ratio(host(g), ref[name]) <= 1.0, name
 
 
-@pytest.mark.parametrize("L", [96, 160])
+@pytest.mark.parametrize("L", [96, 300])
 def test_multi_launch_route(L):
     """4500 sequences exceed one launch's length table (4096 sequences), so
     the schedule has two launches per side (and per forward) and sigattn_bwd
-    runs them in turn (at Lmax 96, two launches of the one-tile backward,
-    whose dQ is checked against the oracle only); results still equal the
-    separate calls and the oracle."""
+    runs them in turn (at Lmax 96, two launches of the short-sequence
+    backward, whose dQ is checked against the oracle only); results still
+    equal the separate calls and the oracle."""
     B, H, d = 4500, 1, 64
     lens = list(np.random.default_rng(5).integers(0, L + 1, size=B))
     assert sa.plan_stats(B, H, L, d, lens, "bwd_dq")[2] == 2
     assert sa.plan_stats(B, H, L, d, lens, "fwd")[2] == 2
-    assert sa.plan_stats(B, H, L, d, lens, "bwd")[2] == (2 if L <= 128 else 4)
+    assert sa.plan_stats(B, H, L, d, lens, "bwd")[2] == (2 if L <= 256 else 4)
     c = workloads.random_case(B, H, d, L, lens, seed=65)
     t = {x: c[x].to(DEV) for x in ("q", "k", "v", "do")}
     n = c["seqlens"]
@@ -114,7 +114,7 @@ def test_multi_launch_route(L):
     dq0 = sa.bwd_dq(t["q"], t["k"], t["v"], t["do"], n)
     dk0, dv0 = sa.bwd_dkdv(t["q"], t["k"], t["v"], t["do"], n)
     torch.cuda.synchronize()
-    assert (L <= 128 or torch.equal(dq, dq0)) and torch.equal(dk, dk0) and torch.equal(dv, dv0)
+    assert (L <= 256 or torch.equal(dq, dq0)) and torch.equal(dk, dk0) and torch.equal(dv, dv0)
     o = sa.fwd(t["q"], t["k"], t["v"], n)
     torch.cuda.synchronize()
     ref = oracle.attention(host(c["q"]), host(c["k"]), host(c["v"]), n, do=host(c["do"]))

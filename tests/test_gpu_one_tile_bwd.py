@@ -1,10 +1,11 @@
-"""The one-tile backward: when every sequence fits one 128-row tile (sigmoid,
+"""The short-sequence backward: when every sequence fits 256 rows (sigmoid,
 fast precision, head dim 64, no mask, no bias gradient), sigattn_bwd runs one
-workgroup per (sequence, head) that computes S, dP and dS once for dQ, dK
-and dV.  Its dK and dV take the dK/dV kernel's arithmetic in the same order
-(bitwise equal to sigattn_bwd_dkdv); its dQ uses that side's dS (scores
-from the prescaled K rather than the prescaled Q), so it is checked against
-the CPU fp64 oracle, element by element, with the padded rows zero."""
+workgroup per (sequence, head) (4 waves for Lmax <= 128, 8 waves up to 256)
+that computes S, dP and dS once for dQ, dK and dV.  Its dK and dV take the
+dK/dV kernel's arithmetic in the same order (bitwise equal to
+sigattn_bwd_dkdv); its dQ uses that side's dS (scores from the prescaled K
+rather than the prescaled Q), so it is checked against the CPU fp64 oracle,
+element by element, with the padded rows zero."""
 import numpy as np
 import pytest
 import torch
@@ -25,6 +26,11 @@ CASES = [
     (3, 4, 128, [128, 128, 100], "fixed_n", 200.0, torch.float16),
     (6, 1, 16, [16, 3, 0, 16, 9, 1], "const", -1.5, torch.bfloat16),
     (2, 2, 40, [0, 0], "seqlen", 0.0, torch.bfloat16),
+    # 8 waves: two 128-row tiles, dQ in two 128-query pairs
+    (5, 3, 256, [256, 129, 128, 1, 0], "seqlen", 0.0, torch.bfloat16),
+    (4, 2, 200, [200, 77, 150, 33], "per_head", [-4.0, -2.5], torch.bfloat16),
+    (3, 2, 256, [255, 256, 193], "fixed_n", 300.0, torch.float16),
+    (3, 1, 129, [129, 0, 65], "const", -2.0, torch.bfloat16),
 ]
 IDS = [f"B{c[0]}H{c[1]}L{c[2]}-{c[4]}-{str(c[6])[6:]}" for c in CASES]
 
@@ -62,7 +68,7 @@ def test_one_tile_backward(case):
 
 def test_one_tile_strided_fused_qkv_layout():
     """[B, L, 3, H, d] projection slices in, one [B, L, 3, H, d] gradient buffer out."""
-    B, H, L, lens = 3, 4, 112, [112, 60, 5]
+    B, H, L, lens = 3, 4, 240, [240, 60, 129]
     c = workloads.random_case(B, H, 64, L, lens, seed=81)
     qkv = torch.stack([c[x].permute(0, 2, 1, 3) for x in ("q", "k", "v")], dim=2).contiguous().to(DEV)
     q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
@@ -76,19 +82,21 @@ def test_one_tile_strided_fused_qkv_layout():
         assert torch.equal(g[:, :, i].permute(0, 2, 1, 3), ref), i
 
 
-def test_one_tile_matches_two_kernel_route_closely():
-    """The same batch at Lmax 128 (one-tile kernel) and 129 (the fused
-    two-kernel launch; the extra row is padding in every sequence): dK and
+@pytest.mark.parametrize("L,lens", [(128, [128, 100, 64, 1, 127, 90, 33, 128]),
+                                    (256, [256, 200, 129, 1, 255, 128, 64, 17])], ids=["L128", "L256"])
+def test_one_tile_matches_two_kernel_route_closely(L, lens):
+    """The same batch at Lmax L (short-sequence kernel) and 257 (the fused
+    two-kernel launch; the extra rows are padding in every sequence): dK and
     dV agree bitwise, dQ to the rounding of the prescaled operand."""
-    B, H, lens = 8, 2, [128, 100, 64, 1, 127, 90, 33, 128]
-    c = workloads.random_case(B, H, 64, 128, lens, seed=82)
+    B, H = len(lens), 2
+    c = workloads.random_case(B, H, 64, L, lens, seed=82 + L)
     t = {x: c[x].to(DEV) for x in ("q", "k", "v", "do")}
-    pad = {x: torch.nn.functional.pad(t[x], (0, 0, 0, 1)) for x in t}
+    pad = {x: torch.nn.functional.pad(t[x], (0, 0, 0, 257 - L)) for x in t}
     n = c["seqlens"]
-    assert sa.plan_stats(B, H, 129, 64, n, "bwd")[2] == 1
+    assert sa.plan_stats(B, H, 257, 64, n, "bwd")[2] == 1
     dq, dk, dv = sa.bwd(t["q"], t["k"], t["v"], t["do"], n)
     dq1, dk1, dv1 = sa.bwd(pad["q"], pad["k"], pad["v"], pad["do"], n)
     torch.cuda.synchronize()
-    assert torch.equal(dk, dk1[:, :, :128]) and torch.equal(dv, dv1[:, :, :128])
-    a, b = host(dq), host(dq1[:, :, :128])
+    assert torch.equal(dk, dk1[:, :, :L]) and torch.equal(dv, dv1[:, :, :L])
+    a, b = host(dq), host(dq1[:, :, :L])
     assert np.max(np.abs(a - b) / (1e-2 * (1.0 + np.abs(b)))) <= 1.0
