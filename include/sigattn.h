@@ -199,14 +199,14 @@ sigattn_status sigattn_bwd_dkdv(const sigattn_args *args, const void *q, const v
  * together; still no atomics: every output row has one writer).  At d = 128
  * the two kernels run at different occupancies, and the dK/dV and dQ
  * launches run in turn on args->stream.
- * Short-sequence case: d = 64, fast precision, no mask, dbias NULL and
- * Lmax <= 256.  Then one workgroup per (sequence, head) writes all of its
- * dQ, dK and dV rows (one launch per 4096 sequences), computing S, dP and dS
- * once instead of once per side: dK and dV are bitwise those of
- * sigattn_bwd_dkdv, and dQ is taken from the same dS (the scores from K
- * scaled by -log2(e)/sqrt(d) and rounded to the element type, where
- * sigattn_bwd_dq scales Q), so it differs from sigattn_bwd_dq by rounding
- * only.
+ * Short-sequence case: d = 64, fast precision, no mask and Lmax <= 256.
+ * Then one workgroup per (sequence, head) writes all of its dQ, dK and dV
+ * rows and its bias-gradient rows (one launch per 4096 sequences), computing
+ * S, dP and dS once instead of once per side: dK, dV and the bias rows are
+ * bitwise those of sigattn_bwd_dkdv(_dbias), and dQ is taken from the same
+ * dS (the scores from K scaled by -log2(e)/sqrt(d) and rounded to the
+ * element type, where sigattn_bwd_dq scales Q), so it differs from
+ * sigattn_bwd_dq by rounding only.
  * args->strides, if set, has 7 entries: q, k, v, dout, dq, dk, dv.  Same
  * checks and errors as the separate calls (dq, dk, dv are outputs; dbias is
  * checked like a row output). */

@@ -283,10 +283,10 @@ def bwd(q, k, v, dout, seqlens, dq=None, dk=None, dv=None, dbias=None, bias_rows
     """The whole backward in one call (one fused launch at d = 64): returns
     (dQ, dK, dV), plus the bias-gradient rows if `bias_rows` or `dbias` is
     given.  Bitwise the results of bwd_dq and bwd_dkdv(_dbias), except when
-    every sequence fits 256 rows (d = 64, fast precision, no mask, no bias
-    rows): then one kernel computes dS once for all three, dK and dV are
-    still bitwise those of bwd_dkdv, and dQ differs from bwd_dq by rounding
-    only."""
+    every sequence fits 256 rows (d = 64, fast precision, no mask): then one
+    kernel computes dS once for all of them, dK, dV and the bias rows are
+    still bitwise those of bwd_dkdv(_dbias), and dQ differs from bwd_dq by
+    rounding only."""
     import torch
 
     dq = _new_like(q) if dq is None else dq

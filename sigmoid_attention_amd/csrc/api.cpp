@@ -269,10 +269,10 @@ bool fused_bwd(int32_t d, size_t dkdv_launches, size_t dq_launches) {
 
 // Whether the sigmoid backward runs as the short-sequence kernel
 // (launch_bwd_small, one workgroup per (sequence, head)): head dim 64, fast
-// precision, no mask, no bias gradient, every sequence within 256 rows.
+// precision, no mask, every sequence within 256 rows.
 constexpr int32_t kSmallBwdRows = 256;
-bool small_bwd(const sigattn_args* a, bool softmax, bool dbias) {
-  return a->d == 64 && a->precision == SIGATTN_PREC_FAST && a->mask != SIGATTN_MASK_CAUSAL && !softmax && !dbias &&
+bool small_bwd(const sigattn_args* a, bool softmax) {
+  return a->d == 64 && a->precision == SIGATTN_PREC_FAST && a->mask != SIGATTN_MASK_CAUSAL && !softmax &&
          a->Lmax <= kSmallBwdRows;
 }
 
@@ -300,12 +300,12 @@ sigattn_status run_bwd(const sigattn_args* a, const void* const* t, const float*
   const hipStream_t st = (hipStream_t)a->stream;
   const auto impl_fused = f16(a) ? sigattn::f16::launch_bwd_fused : sigattn::bf16::launch_bwd_fused;
   (void)hipGetLastError();
-  if (small_bwd(a, lse2 != nullptr, dbias != nullptr)) {
+  if (small_bwd(a, lse2 != nullptr)) {
     const View vq = views(a, tq, 5, kDq)[4];
     for (const Launch& L : pk)
       if ((f16(a) ? sigattn::f16::launch_bwd_small : sigattn::bf16::launch_bwd_small)(
               L, t[0], t[1], t[2], t[3], const_cast<void*>(t[4]), const_cast<void*>(t[5]), const_cast<void*>(t[6]),
-              vq.sb, vq.sh, (int32_t)vq.sl, st) != hipSuccess)
+              dbias, vq.sb, vq.sh, (int32_t)vq.sl, st) != hipSuccess)
         return SIGATTN_ERR_HIP;
     return SIGATTN_OK;
   }
@@ -594,7 +594,7 @@ sigattn_status sigattn_plan_stats(const sigattn_args* a, int32_t pass, int64_t* 
     if (work_items) *work_items = sk.items + sq.items;
     if (tile_pairs) *tile_pairs = sk.pairs + sq.pairs;
     if (launches)
-      *launches = small_bwd(a, false, false) ? (int32_t)lk : fused_bwd(a->d, lk, lq) ? 1 : (int32_t)(lk + lq);
+      *launches = small_bwd(a, false) ? (int32_t)lk : fused_bwd(a->d, lk, lq) ? 1 : (int32_t)(lk + lq);
     return SIGATTN_OK;
   }
   sigattn::PlanStats st;

@@ -1006,7 +1006,7 @@ bwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const
 // ---------------------------------------------------------------------------
 // Backward of short sequences, one workgroup per (sequence, head): Lmax <= R
 // with R = 128 (4 waves) or 256 (8 waves); sigmoid, fast precision, no mask,
-// head dim 64.  The two-kernel split of the pages (§2C) recomputes S and dP
+// head dim 64; optionally with the bias-gradient rows.  The two-kernel split of the pages (§2C) recomputes S and dP
 // on each side; for long sequences that costs 2/5 more matrix work but keeps
 // every workgroup's output private.  When one workgroup holds a whole
 // (sequence, head), it owns all of its dQ, dK and dV rows, so the split buys
@@ -1049,11 +1049,14 @@ template <int R> struct SmallCfg {
   static constexpr int OCC = R == 128 ? 2 : 1;  // workgroups per CU the LDS allows
 };
 
-template <int D, int R>
+// DB: also the bias-gradient rows (per key, the sum of its dS column over the
+// valid queries), as the dK/dV kernel writes them.
+template <int D, int R, bool DB>
 __global__ __launch_bounds__(SmallCfg<R>::NT, SmallCfg<R>::OCC) void bwd_small_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    const SeqTable T, const Sched S, const int64_t dq_sb, const int64_t dq_sh, const int32_t dq_sl) {
+    float* __restrict__ DBIAS, const SeqTable T, const Sched S, const int64_t dq_sb, const int64_t dq_sh,
+    const int32_t dq_sl) {
   static_assert(D == 64, "head dim 64");
   static_assert(R == 128 || R == 256, "one or two 128-row tiles");
   constexpr int NW = SmallCfg<R>::NW, NT = SmallCfg<R>::NT, PQ = 128;  // queries per pair
@@ -1074,6 +1077,8 @@ __global__ __launch_bounds__(SmallCfg<R>::NT, SmallCfg<R>::OCC) void bwd_small_k
     zero_rows<D, NT>(dqp, dq_sl, 0, S.Lmax);
     zero_rows<D, NT>(dkp, S.sl[4], 0, S.Lmax);
     zero_rows<D, NT>(dvp, S.sl[5], 0, S.Lmax);
+    if (DB)
+      for (int r = (int)threadIdx.x; r < S.Lmax; r += NT) DBIAS[(size_t)it.bh * S.Lmax + r] = 0.0f;
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -1102,6 +1107,7 @@ __global__ __launch_bounds__(SmallCfg<R>::NT, SmallCfg<R>::OCC) void bwd_small_k
     dk[i] = (f32x16){};
     dv[i] = (f32x16){};
   }
+  float dsum = 0.0f;  // with DB: sum of this lane's dS values (its key column)
   // phase 2: this wave's query block and the B-fragment offsets of its dS^T
   // reads: rows (keys) 16cc + 4hf + j/4 (+ 8), queries 32qb + 16gq + 4(j%4)
   // .. +3 (lane j of each 16, gq = lane / 16 % 2): the key order of TrFrag's
@@ -1140,7 +1146,7 @@ __global__ __launch_bounds__(SmallCfg<R>::NT, SmallCfg<R>::OCC) void bwd_small_k
         read_value_frags<D>(ag[c & 1], tr, Gj, c);
         read_value_frags<D>(aq[c & 1], tr, Qj, c);
         sched_fence();
-        dsigmoid_chunk<D, false, true, true>(sc, gc, c, m, dh[c], dl[c], ph[c], pl[c]);
+        dsigmoid_chunk<D, false, true, true, DB>(sc, gc, c, m, dh[c], dl[c], ph[c], pl[c], &dsum);
         // dS^T row: this lane's key; queries 64(j % 2) + 16c + 4hf + {0..3}
         // and + 8 of the pair (groups 16(j % 2) + 4c + hf, + 2)
         const u32x4 pk = as_u32x4(dh[c]);
@@ -1158,6 +1164,10 @@ __global__ __launch_bounds__(SmallCfg<R>::NT, SmallCfg<R>::OCC) void bwd_small_k
       value_chunk_pre<D, false>(dk, aq[1], dh[3], dl[3]);
     }
     if (j == R / 64 - 1) {  // dK, dV complete
+      if constexpr (DB) {
+        dsum += __shfl_xor(dsum, 32);  // the other half of the column's query rows
+        if (hf == 0 && krow < S.Lmax) DBIAS[(size_t)it.bh * S.Lmax + krow] = krow < n ? dsum : 0.0f;
+      }
       const float scale = S.out_scale;
       if (krow < n) {
         uint16_t* rk = dkp + (size_t)krow * S.sl[4];
@@ -1297,18 +1307,27 @@ hipError_t launch_bwd_fused_d(const BwdSched& P, int32_t blocks, const void* q, 
   return launch_bwd_fused_t<D, SPLIT, false, false>(P, blocks, q, k, v, g, dq, dk, dv, lse, delta, dbias, st);
 }
 
+template <int R, bool DB>
+void launch_small_r(int64_t blocks, const Launch& L, const void* q, const void* k, const void* v, const void* g,
+                    void* dq, void* dk, void* dv, float* dbias, int64_t dq_sb, int64_t dq_sh, int32_t dq_sl,
+                    hipStream_t st) {
+  hipLaunchKernelGGL((bwd_small_kernel<64, R, DB>), dim3((unsigned)blocks), dim3(SmallCfg<R>::NT), 0, st,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq,
+                     (uint16_t*)dk, (uint16_t*)dv, dbias, L.T, L.sched, dq_sb, dq_sh, dq_sl);
+}
+
 hipError_t launch_bwd_small_t(const Launch& L, const void* q, const void* k, const void* v, const void* g, void* dq,
-                              void* dk, void* dv, int64_t dq_sb, int64_t dq_sh, int32_t dq_sl, hipStream_t st) {
+                              void* dk, void* dv, float* dbias, int64_t dq_sb, int64_t dq_sh, int32_t dq_sl,
+                              hipStream_t st) {
   const int64_t blocks = (int64_t)L.T.nseq * L.sched.H;
   if (L.sched.Lmax > 256 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
-  if (L.sched.Lmax <= 128)
-    hipLaunchKernelGGL((bwd_small_kernel<64, 128>), dim3((unsigned)blocks), dim3(SmallCfg<128>::NT), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq,
-                       (uint16_t*)dk, (uint16_t*)dv, L.T, L.sched, dq_sb, dq_sh, dq_sl);
-  else
-    hipLaunchKernelGGL((bwd_small_kernel<64, 256>), dim3((unsigned)blocks), dim3(SmallCfg<256>::NT), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)dq,
-                       (uint16_t*)dk, (uint16_t*)dv, L.T, L.sched, dq_sb, dq_sh, dq_sl);
+  if (L.sched.Lmax <= 128) {
+    if (dbias) launch_small_r<128, true>(blocks, L, q, k, v, g, dq, dk, dv, dbias, dq_sb, dq_sh, dq_sl, st);
+    else launch_small_r<128, false>(blocks, L, q, k, v, g, dq, dk, dv, dbias, dq_sb, dq_sh, dq_sl, st);
+  } else {
+    if (dbias) launch_small_r<256, true>(blocks, L, q, k, v, g, dq, dk, dv, dbias, dq_sb, dq_sh, dq_sl, st);
+    else launch_small_r<256, false>(blocks, L, q, k, v, g, dq, dk, dv, dbias, dq_sb, dq_sh, dq_sl, st);
+  }
   return hipGetLastError();
 }
 
@@ -1419,8 +1438,9 @@ hipError_t launch_bwd_fused(int d, bool split, const BwdSched& P, int32_t blocks
 }
 
 hipError_t launch_bwd_small(const Launch& L, const void* q, const void* k, const void* v, const void* g, void* dq,
-                            void* dk, void* dv, int64_t dq_sb, int64_t dq_sh, int32_t dq_sl, hipStream_t st) {
-  return kern::launch_bwd_small_t(L, q, k, v, g, dq, dk, dv, dq_sb, dq_sh, dq_sl, st);
+                            void* dk, void* dv, float* dbias, int64_t dq_sb, int64_t dq_sh, int32_t dq_sl,
+                            hipStream_t st) {
+  return kern::launch_bwd_small_t(L, q, k, v, g, dq, dk, dv, dbias, dq_sb, dq_sh, dq_sl, st);
 }
 
 hipError_t launch_bias_grad(int32_t B, int32_t H, int32_t Lmax, const float* dbias, float* db, hipStream_t st) {

@@ -100,3 +100,33 @@ def test_one_tile_matches_two_kernel_route_closely(L, lens):
     assert torch.equal(dk, dk1[:, :, :L]) and torch.equal(dv, dv1[:, :, :L])
     a, b = host(dq), host(dq1[:, :, :L])
     assert np.max(np.abs(a - b) / (1e-2 * (1.0 + np.abs(b)))) <= 1.0
+
+
+@pytest.mark.parametrize("L,lens", [(128, [128, 77, 0, 1]), (256, [256, 129, 100, 0])], ids=["L128", "L256"])
+def test_one_tile_bias_rows(L, lens):
+    """With the bias-gradient rows (a learnable per-head bias): the rows, dK
+    and dV bitwise those of sigattn_bwd_dkdv_dbias, every output against the
+    oracle, padded rows 0 (outputs pre-filled with NaN)."""
+    B, H = len(lens), 3
+    c = workloads.random_case(B, H, 64, L, lens, seed=90 + L)
+    t = {x: c[x].to(DEV) for x in ("q", "k", "v", "do")}
+    n = c["seqlens"]
+    vals = [-float(np.log(x)) for x in (60.0, 250.0, 700.0)]  # -ln n for lengths in the workloads' range
+    kw = dict(bias_mode="per_head", bias_arg=torch.tensor(vals, dtype=torch.float32, device=DEV))
+    dq, dk, dv = (torch.full_like(t["q"], float("nan")) for _ in range(3))
+    rows = torch.full((B, H, L), float("nan"), dtype=torch.float32, device=DEV)
+    sa.bwd(t["q"], t["k"], t["v"], t["do"], n, dq=dq, dk=dk, dv=dv, dbias=rows, **kw)
+    dk0, dv0, rows0 = sa.bwd_dkdv_dbias(t["q"], t["k"], t["v"], t["do"], n, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, dk0) and torch.equal(dv, dv0) and torch.equal(rows, rows0)
+    ref = oracle.attention(host(c["q"]), host(c["k"]), host(c["v"]), n, do=host(c["do"]), bias_mode="per_head",
+                           bias_arg=np.asarray(vals))
+    got = {"dq": dq, "dk": dk, "dv": dv, "dbias": rows}
+    ratios = {k_: worst_ratio(host(g), ref[k_]) for k_, g in got.items()}
+    print(f"[one-tile] bias rows L={L} ratios={ratios}", flush=True)
+    for k_, r in ratios.items():
+        assert r <= 1.0, (k_, ratios)
+    for b, nb in enumerate(n):
+        assert bool((rows[b, :, nb:] == 0).all())
+        for g in (dq, dk, dv):
+            assert bool((g[b, :, nb:] == 0).all())
