@@ -101,6 +101,17 @@ __device__ __forceinline__ e16x8 to_e16x8(f32x8 x) { return __builtin_convertvec
 // Widen back to float exactly.
 __device__ __forceinline__ f32x8 to_f32x8(e16x8 x) { return __builtin_convertvector(x, f32x8); }
 
+// The low part of split precision: the remainder x - hi, rounded, where hi is
+// x rounded (to_e16x8(x)).  hi is widened from its packed registers (one VALU
+// instruction per value); the empty asm keeps the compiler from seeing that
+// hi came from x, since it would then round every value of x a second time,
+// one at a time, to widen it (two instructions per value).
+__device__ __forceinline__ e16x8 split_lo(const f32x8& x, e16x8 hi) {
+  u32x4 w = as_u32x4(hi);
+  asm("" : "+v"(w));
+  return to_e16x8(x - to_f32x8(as_e16x8(w)));
+}
+
 // The eight values of C register block `blk` that form K-chunk `half` (0/1).
 __device__ __forceinline__ f32x8 chunk8(const f32x16& c, int half) {
   f32x8 r;

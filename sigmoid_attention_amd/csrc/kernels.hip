@@ -81,11 +81,12 @@ constexpr int kInner = 64;  // rows per inner tile
 // for the forward and dK/dV; dQ keeps the lookahead of its scores.  At
 // d = 128 the forward fits lookahead and two waves per SIMD (1.43x faster
 // than one wave per SIMD on the dense 8K batch).
-// Forward waves per SIMD: 4 at d = 64 (3 in split precision, whose hi + lo
-// packs do not fit 128 registers without spilling), 2 at d = 128.
+// Forward waves per SIMD: 4 at d = 64 (split precision included: with the
+// low part taken from the packed high part, see split_lo, it needs 117
+// registers), 2 at d = 128.
 template <int D, bool SPLIT = false> struct FwdCfg {
   static constexpr bool LA = D != 64;
-  static constexpr int OCC = D == 64 ? (SPLIT ? 3 : 4) : 2;
+  static constexpr int OCC = D == 64 ? 4 : 2;
 };
 // The dQ kernel runs two waves per SIMD at either head dim (at d = 128 one
 // 16-byte value is spilled and reloaded once per step).  The dK/dV kernel
@@ -121,7 +122,7 @@ __device__ __forceinline__ void sigmoid_chunk(const f32x16 (&sc)[2], int c, floa
 #pragma unroll
   for (int t = 0; t < 8; ++t) p[t] = sigma_of<D, PRE>(p[t], arg);
   hi = to_e16x8(p);
-  if (SPLIT) lo = to_e16x8(p - to_f32x8(hi));
+  if (SPLIT) lo = split_lo(p, hi);
 }
 
 // dS = dP * sigma * (1 - sigma) for K-chunk c (and optionally sigma itself;
@@ -143,10 +144,10 @@ __device__ __forceinline__ void dsigmoid_chunk(const f32x16 (&sc)[NB], const f32
     ds[t] = gv[t] * __builtin_fmaf(-p, p, p);  // dP * p (1 - p)
   }
   dh = to_e16x8(ds);
-  if (SPLIT) dl = to_e16x8(ds - to_f32x8(dh));
+  if (SPLIT) dl = split_lo(ds, dh);
   if (WANT_P) {
     ph = to_e16x8(p8);
-    if (SPLIT) pl = to_e16x8(p8 - to_f32x8(ph));
+    if (SPLIT) pl = split_lo(p8, ph);
   }
   if constexpr (DSUM)  // pairwise: keeps the eight values' live ranges short
     *dsum += ((ds[0] + ds[1]) + (ds[2] + ds[3])) + ((ds[4] + ds[5]) + (ds[6] + ds[7]));
@@ -218,7 +219,7 @@ __device__ __forceinline__ void dsoftmax_chunk_col(const f32x16 (&sc)[NB], const
     ds[t] = p * (gv[t] - dlt);
   }
   dh = to_e16x8(ds);
-  if (SPLIT) dl = to_e16x8(ds - to_f32x8(dh));
+  if (SPLIT) dl = split_lo(ds, dh);
 }
 
 // P and dS for K-chunk c when queries are rows (dK/dV kernel): lse2 and delta
@@ -237,9 +238,9 @@ __device__ __forceinline__ void dsoftmax_chunk_row(const f32x16 (&sc)[NB], const
     ds[t] = p * (gv[t] - dlt8[t]);
   }
   dh = to_e16x8(ds);
-  if (SPLIT) dl = to_e16x8(ds - to_f32x8(dh));
+  if (SPLIT) dl = split_lo(ds, dh);
   ph = to_e16x8(p8);
-  if (SPLIT) pl = to_e16x8(p8 - to_f32x8(ph));
+  if (SPLIT) pl = split_lo(p8, ph);
 }
 
 // Store 4 consecutive fp32 values of an output row in the element type (8 bytes).
@@ -422,6 +423,10 @@ __global__ __launch_bounds__(kThreads, (FwdCfg<D, SPLIT>::OCC)) void fwd_kernel(
   auto Vb = [&](int i) { return lds.p[3 + i]; };
   const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]);
+  // the first tiles load while the fragments below are read
+  dma_k.load(ks, 0, Kb(0));
+  dma_k.load(ks, BK, Kb(1));
+  dma_v.load(vs, 0, Vb(0));
 
   const int qrow = it.tile * BQ + 32 * w + l32;
   e16x8 qf[D / 16];
@@ -433,9 +438,6 @@ __global__ __launch_bounds__(kThreads, (FwdCfg<D, SPLIT>::OCC)) void fwd_kernel(
 
   const int nk = S.causal ? min((n + BK - 1) / BK, causal_inner_end(it.tile, BQ, BK)) : (n + BK - 1) / BK;
   const int q0w = it.tile * BQ + 32 * w;  // this wave's first query
-  dma_k.load(ks, 0, Kb(0));
-  dma_k.load(ks, BK, Kb(1));
-  dma_v.load(vs, 0, Vb(0));
   vm_drain();
   __syncthreads();
   f32x16 sA[2], sB[2];
@@ -504,7 +506,7 @@ __device__ __forceinline__ void softmax_chunk(const f32x16 (&sc)[2], int c, floa
     l += p[t];
   }
   hi = to_e16x8(p);
-  if (SPLIT) lo = to_e16x8(p - to_f32x8(hi));
+  if (SPLIT) lo = split_lo(p, hi);
 }
 
 // Scores of keys >= nv (tile-relative) to -inf; lane half hf holds keys
@@ -541,6 +543,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_softmax_kernel(
   auto Vb = [&](int i) { return lds.p[3 + i]; };
   const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]);
+  // the first tiles load while the fragments below are read
+  dma_k.load(ks, 0, Kb(0));
+  dma_k.load(ks, BK, Kb(1));
+  dma_v.load(vs, 0, Vb(0));
 
   const int qrow = it.tile * BQ + 32 * w + l32;
   e16x8 qf[D / 16];
@@ -552,9 +558,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_softmax_kernel(
 
   const int nk = S.causal ? min((n + BK - 1) / BK, causal_inner_end(it.tile, BQ, BK)) : (n + BK - 1) / BK;
   const int q0w = it.tile * BQ + 32 * w;  // this wave's first query
-  dma_k.load(ks, 0, Kb(0));
-  dma_k.load(ks, BK, Kb(1));
-  dma_v.load(vs, 0, Vb(0));
   vm_drain();
   __syncthreads();
   f32x16 sA[2], sB[2];
@@ -647,6 +650,10 @@ __device__ __forceinline__ void dq_body(const Ring& lds, int vb, const uint16_t*
   auto Vb = [&](int i) { return lds.p[3 + i]; };
   const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]), gs(slice_base(dO, S, it.bh, 3), n, S.sl[3]);
+  // the first tiles load while the fragments below are read
+  dma_k.load(ks, 0, Kb(0));
+  dma_k.load(ks, BK, Kb(1));
+  dma_v.load(vs, 0, Vb(0));
 
   const int qrow = it.tile * BQ + 32 * w + l32;
   e16x8 qf[D / 16], gf[D / 16];
@@ -666,9 +673,6 @@ __device__ __forceinline__ void dq_body(const Ring& lds, int vb, const uint16_t*
 
   const int nk = S.causal ? min((n + BK - 1) / BK, causal_inner_end(it.tile, BQ, BK)) : (n + BK - 1) / BK;
   const int q0w = it.tile * BQ + 32 * w;  // this wave's first query
-  dma_k.load(ks, 0, Kb(0));
-  dma_k.load(ks, BK, Kb(1));
-  dma_v.load(vs, 0, Vb(0));
   vm_drain();
   __syncthreads();
   f32x16 sA[2], sB[2];
@@ -772,6 +776,24 @@ __device__ __forceinline__ void dkdv_body(const Ring& lds, float* __restrict__ r
   auto Gb = [&](int i) { return lds.p[3 + i]; };
   const Slice qs(slice_base(Q, S, it.bh, 0), n, S.sl[0]), ks(slice_base(K, S, it.bh, 1), n, S.sl[1]),
       vs(slice_base(V, S, it.bh, 2), n, S.sl[2]), gs(slice_base(dO, S, it.bh, 3), n, S.sl[3]);
+  const int nq = (n + BQ - 1) / BQ;
+  // causal: query tiles before this key tile's first key see none of it
+  const int j0 = S.causal ? causal_first_inner(it.tile, BKV, BQ) : 0;
+  const int k0w = it.tile * BKV + 32 * w;  // this wave's first key
+  // softmax: wave 0 streams lse2, wave 1 delta (one value per lane and row)
+  const RowDma<BQ> rdma(SOFTMAX && w < 2 ? (w == 0 ? LSE : DELTA) + (size_t)it.bh * S.Lmax : nullptr, n, lane);
+  auto Rb = [&](int i) { return rowv + (2 * i + (w & 1)) * BQ; };
+  auto row_load = [&](int row0, int i) {
+    if constexpr (SOFTMAX)
+      if (w < 2) rdma.load(row0, Rb(i));
+  };
+  // the first tiles load while the fragments below are read
+  dma_q.load(qs, j0 * BQ, Qb(0));
+  dma_g.load(gs, j0 * BQ, Gb(0));
+  dma_q.load(qs, (j0 + 1) * BQ, Qb(1));
+  dma_g.load(gs, (j0 + 1) * BQ, Gb(1));
+  row_load(j0 * BQ, 0);
+  row_load((j0 + 1) * BQ, 1);
 
   const int krow = it.tile * BKV + 32 * w + l32;
   e16x8 kf[D / 16], vf[D / 16];
@@ -785,23 +807,6 @@ __device__ __forceinline__ void dkdv_body(const Ring& lds, float* __restrict__ r
     dv[i] = (f32x16){};
   }
 
-  const int nq = (n + BQ - 1) / BQ;
-  // causal: query tiles before this key tile's first key see none of it
-  const int j0 = S.causal ? causal_first_inner(it.tile, BKV, BQ) : 0;
-  const int k0w = it.tile * BKV + 32 * w;  // this wave's first key
-  // softmax: wave 0 streams lse2, wave 1 delta (one value per lane and row)
-  const RowDma<BQ> rdma(SOFTMAX && w < 2 ? (w == 0 ? LSE : DELTA) + (size_t)it.bh * S.Lmax : nullptr, n, lane);
-  auto Rb = [&](int i) { return rowv + (2 * i + (w & 1)) * BQ; };
-  auto row_load = [&](int row0, int i) {
-    if constexpr (SOFTMAX)
-      if (w < 2) rdma.load(row0, Rb(i));
-  };
-  dma_q.load(qs, j0 * BQ, Qb(0));
-  dma_g.load(gs, j0 * BQ, Gb(0));
-  dma_q.load(qs, (j0 + 1) * BQ, Qb(1));
-  dma_g.load(gs, (j0 + 1) * BQ, Gb(1));
-  row_load(j0 * BQ, 0);
-  row_load((j0 + 1) * BQ, 1);
   vm_drain();
   __syncthreads();
   float dsum = 0.0f;  // with DB: sum of this lane's dS values (its key column)
