@@ -41,7 +41,11 @@ def rocm_include() -> str:
 
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The AMDGPU register-pressure trackers in the machine scheduler: the head-dim
+# 128 backward kernels, at the register limit, spill 8 bytes instead of 24
+# and run 2 % faster (same-session A/B on MI355X); the others are unchanged.
+DEVICE = [f"--offload-arch={ARCH}", "-mllvm", "--amdgpu-use-amdgpu-trackers",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def _run(cmd, verbose):
